@@ -1,0 +1,410 @@
+"""Plain fp64 CPU oracle for GPTQ's per-layer solver.
+
+TEST INFRASTRUCTURE ONLY.  Only the test-suite, the smoke check and the
+benchmark's CPU-baseline leg may import this module.  The GPU library never
+calls it and shares no code with it.
+
+Sources (the pages this follows; cited by page, section and equation):
+
+* itwiki "GPTQ" page, section "문제 설정" (problem setting): the layer objective
+  argmin over the grid of ||W X - What X||^2.
+* same page, section "OBQ에서 GPTQ로" (from OBQ to GPTQ): the OBQ compensation
+  delta_F and the Gaussian-elimination downdate of H_F^-1 (the two displayed
+  equations), and the three-changes table (fixed column order, lazy batch
+  B = 128, Cholesky form of H^-1 with 1% damping).
+* same page, section "알고리즘" (Algorithm 1): Q, E; the upper Cholesky factor of
+  H^-1; block loop, column loop, in-block update, out-of-block update.
+* same page, section "최소 구현" (minimal implementation): the asymmetric per-row
+  min/max grid, H = 2 X^T X, damping by percdamp * mean(diag H), the factor
+  chain cholesky -> cholesky_inverse -> cholesky(upper).
+* same page, section "실무 변형" (practical variants): group quantization with
+  group parameters taken from the latest updated weights.
+* molayo1419.me blog "GPTQ를 밑바닥부터 구현하며 배운 것들", section 3
+  (implementation): H = 2 X^T X and the per-column update rule.
+
+Readings of points the pages leave open are listed in the repository's design
+notes; the ones that change arithmetic are restated next to the code below.
+
+Parity pins: every function here is checked in tests against closed forms,
+brute force on tiny inputs, the OBQ explicit-inverse form, or invariants.
+"""
+from __future__ import annotations
+
+import dataclasses
+from typing import Iterable, Optional
+
+import numpy as np
+import scipy.linalg as sla
+
+
+# ---------------------------------------------------------------------------
+# Hessian and damping
+# ---------------------------------------------------------------------------
+
+def hessian(x_chunks: Iterable[np.ndarray], d_col: Optional[int] = None) -> np.ndarray:
+    """H = sum over chunks of 2 * X_c^T X_c, in fp64.
+
+    Blog section 3 and the wiki sketch write H = 2 X^T X with X [n x d_in]; the
+    sum (not a mean) over calibration rows is taken.  Chunks are read exactly
+    as stored (fp16/fp32 values are exact in fp64).
+    """
+    H = None
+    for xc in x_chunks:
+        x = np.asarray(xc, dtype=np.float64)
+        if H is None:
+            H = np.zeros((x.shape[1], x.shape[1]))
+        H += 2.0 * (x.T @ x)
+    if H is None:
+        if d_col is None:
+            raise ValueError("no chunks")
+        H = np.zeros((d_col, d_col))
+    return H
+
+
+def damp(H: np.ndarray, percdamp: float = 0.01):
+    """H_lambda = H + lambda I with lambda = percdamp * mean(diag H).
+
+    Wiki sketch (damping line) and the three-changes table (1% of the mean
+    diagonal).  lambda is taken from the undamped diagonal.
+    """
+    lam = float(percdamp) * float(np.mean(np.diag(H)))
+    return H + lam * np.eye(H.shape[0]), lam
+
+
+# ---------------------------------------------------------------------------
+# inverse-Hessian factor
+# ---------------------------------------------------------------------------
+
+class NotPositiveDefinite(ArithmeticError):
+    pass
+
+
+def inv_hessian_factor(H_lam: np.ndarray) -> np.ndarray:
+    """U upper triangular with U^T U = H_lam^-1, by the sketch's route.
+
+    Wiki "최소 구현": L = cholesky(H); Hinv = cholesky_inverse(L) = L^-T L^-1;
+    U = cholesky(Hinv, upper).  Algorithm 1 writes the same object as
+    Cholesky(H^-1)^T (the transpose of the lower factor).
+    """
+    try:
+        L = np.linalg.cholesky(H_lam)
+    except np.linalg.LinAlgError as exc:
+        raise NotPositiveDefinite(str(exc)) from exc
+    Linv = sla.solve_triangular(L, np.eye(L.shape[0]), lower=True)
+    Hinv = Linv.T @ Linv
+    Hinv = 0.5 * (Hinv + Hinv.T)
+    try:
+        Lh = np.linalg.cholesky(Hinv)
+    except np.linalg.LinAlgError as exc:
+        raise NotPositiveDefinite(str(exc)) from exc
+    return Lh.T.copy()
+
+
+def inv_hessian_factor_reverse(H_lam: np.ndarray) -> np.ndarray:
+    """Same U by the reverse-order route: H_lam = Ut Ut^T with Ut upper, U = Ut^-1.
+
+    By uniqueness of the Cholesky factor of H_lam^-1 (positive diagonal) this
+    equals :func:`inv_hessian_factor`.  Ut is the lower Cholesky factor of the
+    row/column-reversed matrix, reversed back.
+    """
+    J = H_lam[::-1, ::-1]
+    Lr = np.linalg.cholesky(J)
+    Ut = Lr[::-1, ::-1]
+    return sla.solve_triangular(Ut, np.eye(Ut.shape[0]), lower=False)
+
+
+# ---------------------------------------------------------------------------
+# grid and quantizer (wiki "최소 구현": quantize(), per-row min/max grid)
+# ---------------------------------------------------------------------------
+
+def grid_params(w: np.ndarray, bits: int):
+    """Asymmetric min/max grid over the last axis of w.
+
+    scale = max(max - min, 1e-8) / maxq; zero = round(-min / scale), with the
+    range floor 1e-8 as written; zero is an integer and is not clamped.
+    Rounding is round-half-to-even, as torch.round.
+    """
+    maxq = (1 << bits) - 1
+    wmin = np.min(w, axis=-1)
+    wmax = np.max(w, axis=-1)
+    scale = np.maximum(wmax - wmin, 1e-8) / maxq
+    zero = np.rint(-wmin / scale)
+    return scale, zero
+
+
+def quant_codes(w, scale, zero, maxq):
+    """c = clamp(round(w / scale) + zero, 0, maxq) -- the sketch's quantize()."""
+    return np.clip(np.rint(w / scale) + zero, 0, maxq)
+
+
+def dequant(c, scale, zero):
+    """What = scale * (c - zero)."""
+    return scale * (c - zero)
+
+
+# ---------------------------------------------------------------------------
+# GPTQ lazy-batch loop (Algorithm 1 + the sketch's loop + grouping)
+# ---------------------------------------------------------------------------
+
+@dataclasses.dataclass
+class GPTQResult:
+    codes: np.ndarray        # uint8 [d_row x d_col]
+    scales: np.ndarray       # fp64 [d_row x n_groups]
+    zeros: np.ndarray        # int64 [d_row x n_groups]
+    w_hat: np.ndarray        # fp64 [d_row x d_col]
+    err_sq_sum: float        # sum of squared scaled errors E over all columns
+    adopted_codes: int = 0   # forced-replay statistics
+    adopted_zeros: int = 0
+    max_boundary_dist: float = 0.0
+
+
+class ReplayMismatch(AssertionError):
+    pass
+
+
+def check_alignment(block_size: int, group_size: int):
+    if block_size <= 0:
+        raise ValueError("block_size must be positive")
+    if group_size < 0:
+        raise ValueError("group_size must be >= 0")
+    if group_size and not (group_size % block_size == 0 or block_size % group_size == 0):
+        raise ValueError("group_size and block_size must divide one another")
+
+
+def gptq_quantize(W0: np.ndarray, U: np.ndarray, bits: int, group_size: int = 0,
+                  block_size: int = 128, replay_codes: Optional[np.ndarray] = None,
+                  replay_zeros: Optional[np.ndarray] = None,
+                  replay_tol: float = 1e-3) -> GPTQResult:
+    """Quantize W0 [d_row x d_col] given U (upper, U^T U = H_lambda^-1).
+
+    Steps (wiki Algorithm 1 / sketch), natural column order:
+      per-row grid from W0 (or per-group grid at each group start from the
+      then-current weights);
+      for each block [i1, i2): copy W1 = W[:, i1:i2]; for each column j:
+        c = quant(W1[:, j]); q = dequant(c); e = (W1[:, j] - q) / U[j, j];
+        W1[:, j:] -= e * U[j, j:]; E[:, j] = e;
+      then W[:, i2:] -= E @ U[i1:i2, i2:].
+
+    Forced replay (``replay_codes`` given): wherever the supplied code differs
+    from this oracle's, the difference is accepted only if it is 1 and
+    w / scale lies within ``replay_tol`` of the half-integer between the two
+    candidates; the supplied code is then adopted and the loop continues.  The
+    same applies to group zero-points with -min / scale.  Any other difference
+    raises ReplayMismatch.
+    """
+    check_alignment(block_size, group_size)
+    W = np.array(W0, dtype=np.float64, copy=True)
+    U = np.asarray(U, dtype=np.float64)
+    d_row, d_col = W.shape
+    maxq = (1 << bits) - 1
+    g = group_size if group_size else d_col
+    n_groups = (d_col + g - 1) // g
+    codes = np.zeros((d_row, d_col), dtype=np.float64)
+    scales = np.zeros((d_row, n_groups))
+    zeros = np.zeros((d_row, n_groups))
+    err_sq = 0.0
+    adopted_c = adopted_z = 0
+    max_dist = 0.0
+
+    if not group_size:
+        s, z = grid_params(W, bits)
+        z = _replay_zero(z, -np.min(W, axis=1) / s, replay_zeros, 0, replay_tol)
+        adopted_z += int(np.sum(z[1]))
+        scales[:, 0], zeros[:, 0] = s, z[0]
+
+    for i1 in range(0, d_col, block_size):
+        i2 = min(i1 + block_size, d_col)
+        W1 = W[:, i1:i2].copy()
+        Ub = U[i1:i2, i1:i2]
+        E = np.zeros((d_row, i2 - i1))
+        for j in range(i2 - i1):
+            col = i1 + j
+            gi = col // g
+            if group_size and col % g == 0:
+                # group parameters from the latest weights: columns inside the
+                # block come from W1, the rest (only when g > B, where they are
+                # fully updated at a block start) from W
+                end = min(col + g, d_col)
+                cur = np.concatenate([W1[:, j:], W[:, i2:end]], axis=1)[:, :end - col]
+                s, z = grid_params(cur, bits)
+                z = _replay_zero(z, -np.min(cur, axis=1) / s, replay_zeros, gi, replay_tol)
+                adopted_z += int(np.sum(z[1]))
+                scales[:, gi], zeros[:, gi] = s, z[0]
+            s = scales[:, gi]
+            z = zeros[:, gi]
+            w = W1[:, j]
+            c = quant_codes(w, s, z, maxq)
+            if replay_codes is not None:
+                rc = np.asarray(replay_codes[:, col], dtype=np.float64)
+                diff = rc != c
+                if np.any(diff):
+                    v = w[diff] / s[diff]
+                    lo = np.minimum(rc[diff], c[diff]) - z[diff]
+                    dist = np.abs(v - (lo + 0.5))
+                    bad = (np.abs(rc[diff] - c[diff]) != 1) | (dist > replay_tol)
+                    if np.any(bad):
+                        rows = np.nonzero(diff)[0][bad]
+                        raise ReplayMismatch(
+                            f"code mismatch at column {col}, rows {rows[:8].tolist()}: "
+                            f"given {rc[rows[:8]].tolist()} oracle {c[rows[:8]].tolist()} "
+                            f"w/scale {(w[rows[:8]] / s[rows[:8]]).tolist()}")
+                    max_dist = max(max_dist, float(np.max(dist)))
+                    adopted_c += int(np.sum(diff))
+                    c = rc
+            q = dequant(c, s, z)
+            e = (w - q) / Ub[j, j]
+            W1[:, j:] -= np.outer(e, Ub[j, j:])
+            E[:, j] = e
+            codes[:, col] = c
+        err_sq += float(np.sum(E * E))
+        W[:, i2:] -= E @ U[i1:i2, i2:]
+
+    w_hat = np.empty_like(codes)
+    for gi in range(n_groups):
+        sl = slice(gi * g, min((gi + 1) * g, d_col))
+        w_hat[:, sl] = dequant(codes[:, sl], scales[:, gi:gi + 1], zeros[:, gi:gi + 1])
+    return GPTQResult(codes.astype(np.uint8), scales, zeros.astype(np.int64), w_hat, err_sq,
+                      adopted_c, adopted_z, max_dist)
+
+
+def _replay_zero(z, v, replay_zeros, gi, tol):
+    """Return (zeros, adopted-mask); adopt a supplied zero-point within tol of a tie."""
+    if replay_zeros is None:
+        return z, np.zeros(z.shape, dtype=bool)
+    rz = np.asarray(replay_zeros[:, gi], dtype=np.float64)
+    diff = rz != z
+    if np.any(diff):
+        lo = np.minimum(rz[diff], z[diff])
+        bad = (np.abs(rz[diff] - z[diff]) != 1) | (np.abs(v[diff] - (lo + 0.5)) > tol)
+        if np.any(bad):
+            rows = np.nonzero(diff)[0][bad]
+            raise ReplayMismatch(f"zero-point mismatch in group {gi}, rows {rows[:8].tolist()}")
+        z = np.where(diff, rz, z)
+    return z, diff
+
+
+# ---------------------------------------------------------------------------
+# output error (wiki "문제 설정": ||W X - What X||^2)
+# ---------------------------------------------------------------------------
+
+def output_error(W0: np.ndarray, W_hat: np.ndarray, H: np.ndarray) -> float:
+    """||X dW^T||_F^2 = 1/2 sum_r dW_r H dW_r^T with H = 2 X^T X undamped."""
+    D = np.asarray(W0, dtype=np.float64) - np.asarray(W_hat, dtype=np.float64)
+    return 0.5 * float(np.sum((D @ H) * D))
+
+
+def output_error_direct(W0: np.ndarray, W_hat: np.ndarray, X: np.ndarray) -> float:
+    """||W X - What X||^2 evaluated from the calibration rows themselves."""
+    D = np.asarray(W0, dtype=np.float64) - np.asarray(W_hat, dtype=np.float64)
+    Y = np.asarray(X, dtype=np.float64) @ D.T
+    return float(np.sum(Y * Y))
+
+
+# ---------------------------------------------------------------------------
+# RTN baseline (wiki "문제 설정": nearest grid point, no error feedback)
+# ---------------------------------------------------------------------------
+
+def rtn(W0: np.ndarray, bits: int, group_size: int = 0):
+    """Round-to-nearest on the same grid structure, parameters from W0."""
+    W = np.asarray(W0, dtype=np.float64)
+    d_row, d_col = W.shape
+    maxq = (1 << bits) - 1
+    g = group_size if group_size else d_col
+    codes = np.zeros_like(W)
+    w_hat = np.zeros_like(W)
+    for g0 in range(0, d_col, g):
+        blk = W[:, g0:g0 + g]
+        s, z = grid_params(blk, bits)
+        c = quant_codes(blk, s[:, None], z[:, None], maxq)
+        codes[:, g0:g0 + g] = c
+        w_hat[:, g0:g0 + g] = dequant(c, s[:, None], z[:, None])
+    return codes.astype(np.uint8), w_hat
+
+
+# ---------------------------------------------------------------------------
+# OBQ form in the same fixed order (wiki "OBQ에서 GPTQ로", both equations)
+# ---------------------------------------------------------------------------
+
+def obq_fixed_order(W0: np.ndarray, H_lam: np.ndarray, bits: int, group_size: int = 0,
+                    downdate: str = "inverse"):
+    """Per row: quantize weights in natural order with the OBQ compensation.
+
+    For weight q with remaining set F: delta_F = -(w_q - quant(w_q)) /
+    [H_F^-1]_qq * (H_F^-1)[:, q]; then q leaves F.  ``downdate="inverse"``
+    recomputes H_F^-1 by direct inversion of H_lam[F, F] at every step (brute
+    force); ``downdate="gauss"`` removes q's row and column from H^-1 by the
+    Gaussian-elimination step H^-1 - H^-1[:, q] H^-1[q, :] / H^-1[q, q].
+    Group parameters (if any) come from the current weights at group starts.
+    Returns (codes, w_hat).
+    """
+    W = np.array(W0, dtype=np.float64, copy=True)
+    d_row, d_col = W.shape
+    maxq = (1 << bits) - 1
+    g = group_size if group_size else d_col
+    codes = np.zeros((d_row, d_col))
+    w_hat = np.zeros((d_row, d_col))
+    for r in range(d_row):
+        w = W[r].copy()
+        if not group_size:
+            s, z = grid_params(w, bits)
+        Hinv = np.linalg.inv(H_lam)
+        for q in range(d_col):
+            F = np.arange(q, d_col)
+            if downdate == "inverse":
+                HF = np.linalg.inv(H_lam[np.ix_(F, F)])
+            else:
+                HF = Hinv[np.ix_(F, F)]
+            if group_size and q % g == 0:
+                s, z = grid_params(w[q:q + g], bits)
+            c = quant_codes(w[q], s, z, maxq)
+            qv = dequant(c, s, z)
+            delta = -(w[q] - qv) / HF[0, 0] * HF[:, 0]
+            w[F] += delta
+            w[q] = qv
+            codes[r, q] = c
+            w_hat[r, q] = qv
+            if downdate == "gauss":
+                Hinv = Hinv - np.outer(Hinv[:, q], Hinv[q, :]) / Hinv[q, q]
+    return codes.astype(np.uint8), w_hat
+
+
+def exhaustive_optimum(W0: np.ndarray, H: np.ndarray, bits: int) -> float:
+    """Exact minimum of 1/2 sum_r dW_r H dW_r^T over the per-row grid (tiny only)."""
+    W = np.asarray(W0, dtype=np.float64)
+    d_row, d_col = W.shape
+    maxq = (1 << bits) - 1
+    if (maxq + 1) ** d_col > 1 << 16:
+        raise ValueError("too large for enumeration")
+    grid = np.array(np.meshgrid(*[np.arange(maxq + 1)] * d_col, indexing="ij"))
+    grid = grid.reshape(d_col, -1).T.astype(np.float64)
+    total = 0.0
+    for r in range(d_row):
+        s, z = grid_params(W[r], bits)
+        cand = dequant(grid, s, z)
+        D = W[r][None, :] - cand
+        total += float(np.min(0.5 * np.sum((D @ H) * D, axis=1)))
+    return total
+
+
+# ---------------------------------------------------------------------------
+# whole layer
+# ---------------------------------------------------------------------------
+
+@dataclasses.dataclass
+class LayerSolution:
+    H: np.ndarray
+    lam: float
+    U: np.ndarray
+    result: GPTQResult
+    err: float
+
+
+def solve_layer(W0: np.ndarray, x_chunks: Iterable[np.ndarray], bits: int,
+                group_size: int = 0, block_size: int = 128,
+                percdamp: float = 0.01) -> LayerSolution:
+    """H -> damping -> U -> lazy-batch loop -> output error (undamped H)."""
+    H = hessian(x_chunks, W0.shape[1])
+    H_lam, lam = damp(H, percdamp)
+    U = inv_hessian_factor(H_lam)
+    res = gptq_quantize(W0, U, bits, group_size, block_size)
+    return LayerSolution(H, lam, U, res, output_error(W0, res.w_hat, H))
