@@ -1,0 +1,167 @@
+/*
+ * gptq.h -- C ABI of the GPTQ per-layer quantization solver for AMD gfx950.
+ *
+ * The solver finds, for one linear layer with weights W [d_row x d_col] and
+ * calibration inputs X [n x d_col], integer codes on an asymmetric k-bit
+ * min/max grid (one grid per row, or one per group of g consecutive columns)
+ * that approximately minimise ||W X^T - What X^T||^2 (the layer objective of
+ * the itwiki "GPTQ" page, section "문제 설정").  It runs in three calls:
+ *
+ *   gptq_hessian_accumulate   H += 2 X_c^T X_c for each calibration chunk
+ *   gptq_prepare_hinv         damping, then U = upper Cholesky factor of H^-1
+ *   gptq_quantize_layer       the lazy-batch column loop; codes, grid, error
+ *
+ * Conventions shared by every call:
+ *   - All matrices are row-major.  A "leading dimension" (ld_*) is the
+ *     distance in elements between consecutive rows and must be >= the row
+ *     width.
+ *   - Pointers marked [device] are device (HBM) addresses on the current HIP
+ *     device; [host] pointers are host addresses.  The caller owns every
+ *     buffer; the library allocates nothing and keeps no state between calls.
+ *   - `stream` is a hipStream_t (NULL = the null stream).  Every call only
+ *     enqueues work on that stream and returns; results are valid once the
+ *     stream has been synchronised.  Calls on different streams are
+ *     independent; the caller orders calls that share buffers.
+ *   - `ws` is a caller-provided device workspace of at least the size that the
+ *     matching *_workspace_size() query returns for the same shape.  Its
+ *     contents are scratch on entry and exit.
+ *   - The return value reports argument validation (done on the host, before
+ *     anything is enqueued) and launch errors.  Numerical failures are
+ *     reported through device words (`info`, NaN error) documented per call.
+ */
+#ifndef GPTQ_H_
+#define GPTQ_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  GPTQ_OK = 0,
+  GPTQ_ERR_NULL_POINTER = 1,    /* a required pointer is NULL            */
+  GPTQ_ERR_BAD_SIZE = 2,        /* a size is negative or zero             */
+  GPTQ_ERR_BAD_LEADING_DIM = 3, /* ld_* smaller than the row width        */
+  GPTQ_ERR_BAD_DTYPE = 4,       /* element type not GPTQ_F32 / GPTQ_F16   */
+  GPTQ_ERR_BAD_BITS = 5,        /* bits outside [2, 8]                    */
+  GPTQ_ERR_BAD_BLOCK = 6,       /* block_size not one of 16, 32, 64, 128  */
+  GPTQ_ERR_BAD_GROUP = 7,       /* group_size and block_size misaligned   */
+  GPTQ_ERR_WORKSPACE = 8,       /* ws NULL or smaller than the query      */
+  GPTQ_ERR_BAD_DAMP = 9,        /* percdamp negative or not finite        */
+  GPTQ_ERR_LAUNCH = 10,         /* a HIP launch or runtime call failed    */
+  GPTQ_ERR_TOO_LARGE = 11       /* a size exceeds the library's limits    */
+} gptq_status;
+
+typedef enum {
+  GPTQ_F32 = 0, /* IEEE binary32 */
+  GPTQ_F16 = 1  /* IEEE binary16 */
+} gptq_dtype;
+
+/*
+ * Hessian accumulation: H += 2 * X^T X   (blog "GPTQ를 밑바닥부터 구현하며 배운
+ * 것들", section 3, formula H = 2 X^T X; itwiki "GPTQ", minimal implementation).
+ *
+ *   H      [device] float [d_col x d_col], row-major, leading dimension d_col.
+ *          Accumulated in place, both triangles written (H stays exactly
+ *          symmetric).  The caller zeroes H before the first chunk; the call
+ *          may be repeated for any number of chunks (the sum is over all rows
+ *          of all chunks -- a sum, not a mean).
+ *   d_col  number of input features (columns of X, rows/cols of H); >= 1.
+ *   X      [device] n_rows x d_col chunk, row-major, element type x_dtype,
+ *          leading dimension ld_x >= d_col.  Read only.
+ *   n_rows rows in this chunk; 0 is a no-op that returns GPTQ_OK.
+ *   ws     [device] workspace, >= gptq_hessian_accumulate_workspace_size().
+ *
+ * Products of fp16 values are exact in fp32; accumulation is fp32 on the
+ * matrix cores, split over row ranges whose partial sums are added in a fixed
+ * order, so results are bitwise reproducible for a given shape.
+ */
+gptq_status gptq_hessian_accumulate(float* H, int64_t d_col, const void* X, int32_t x_dtype,
+                                    int64_t n_rows, int64_t ld_x, void* ws, size_t ws_bytes,
+                                    void* stream);
+size_t gptq_hessian_accumulate_workspace_size(int64_t d_col, int64_t n_rows, int32_t x_dtype);
+
+/*
+ * Inverse-Hessian factor (itwiki "GPTQ": three-changes table, change 3;
+ * Algorithm 1, first line; minimal implementation, damping and factor lines):
+ *
+ *   lambda = percdamp * mean(diag H);   H_l = H + lambda * I
+ *   U      = upper-triangular factor with U^T U = H_l^-1 and diag(U) > 0
+ *
+ * computed as U = Ut^-1 where H_l = Ut Ut^T, Ut upper (the reverse-order
+ * Cholesky factor): the Cholesky runs in fp64, the triangular inverse in fp32.
+ *
+ *   H          [device] float [d_col x d_col] row-major; read only (the
+ *              undamped H is preserved for the error of gptq_quantize_layer).
+ *   percdamp   damping fraction (0.01 in the pages); finite and >= 0.
+ *   U          [device] float [d_col x d_col] row-major output; the strictly
+ *              lower triangle is written as zeros.
+ *   lambda_out [device] one float: the lambda used.
+ *   info       [device] one int32: 0 on success; k + 1 if H_l is not
+ *              positive definite, with k the first failing pivot in the
+ *              natural column order.  U is unspecified when info != 0.
+ *   ws         [device] workspace, >= gptq_prepare_hinv_workspace_size().
+ */
+gptq_status gptq_prepare_hinv(const float* H, int64_t d_col, float percdamp, float* U,
+                              float* lambda_out, int32_t* info, void* ws, size_t ws_bytes,
+                              void* stream);
+size_t gptq_prepare_hinv_workspace_size(int64_t d_col);
+
+/*
+ * Lazy-batch quantization loop (itwiki "GPTQ", Algorithm 1 and the minimal
+ * implementation; group quantization from the "practical variants" section),
+ * natural column order:
+ *
+ *   grid: scale = max(max - min, 1e-8) / (2^bits - 1), zero = round(-min/scale)
+ *         per row from W0 (group_size == 0), or per group of group_size
+ *         columns from the then-current weights when the group's first column
+ *         is reached;
+ *   for each block [i, i + block_size):
+ *     for each column j: c = clamp(round(w_j / scale) + zero, 0, 2^bits - 1)
+ *                        e = (w_j - scale * (c - zero)) / U[j, j]
+ *                        W[:, j:i+B] -= e * U[j, j:i+B]
+ *     W[:, i+B:] -= E * U[i:i+B, i+B:]
+ *   round() is round-half-to-even.
+ *
+ *   W0         [device] d_row x d_col weights, element type w_dtype, leading
+ *              dimension ld_w >= d_col; read only (the fp32 working copy
+ *              lives in ws).
+ *   U          [device] float [d_col x d_col], the factor from
+ *              gptq_prepare_hinv (only the upper triangle is read).
+ *   lambda     [device] one float from gptq_prepare_hinv, or NULL.
+ *   bits       2..8.
+ *   group_size 0 (one grid per row) or a positive size with
+ *              group_size % block_size == 0 or block_size % group_size == 0.
+ *   block_size 16, 32, 64 or 128 (the pages use 128); the last block may be
+ *              partial.
+ *   codes      [device] uint8 [d_row x d_col] row-major output codes.
+ *   scales     [device] float [d_row x n_groups] output, n_groups =
+ *              ceil(d_col / group_size) or 1.
+ *   zeros      [device] int32 [d_row x n_groups] output zero-points.
+ *   out_err    [device] one double: ||X (W0 - What)^T||^2 with What =
+ *              scale * (codes - zero), evaluated as 1/2 ||E||^2 -
+ *              lambda/2 ||W0 - What||^2 from the scaled errors E of the loop
+ *              (exact for the undamped H given U of the damped one); when
+ *              lambda is NULL it is 1/2 ||E||^2 (the damped objective).  NaN
+ *              or Inf if an input was not finite.
+ *   ws         [device] workspace, >= gptq_quantize_layer_workspace_size().
+ */
+gptq_status gptq_quantize_layer(const void* W0, int32_t w_dtype, int64_t d_row, int64_t d_col,
+                                int64_t ld_w, const float* U, const float* lambda, int32_t bits,
+                                int64_t group_size, int64_t block_size, uint8_t* codes,
+                                float* scales, int32_t* zeros, double* out_err, void* ws,
+                                size_t ws_bytes, void* stream);
+size_t gptq_quantize_layer_workspace_size(int64_t d_row, int64_t d_col, int64_t block_size);
+
+/* [host] static description of a status code; never NULL. */
+const char* gptq_status_string(int32_t status);
+/* [host] library version string, e.g. "gptq-gfx950 0.1.0". */
+const char* gptq_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GPTQ_H_ */

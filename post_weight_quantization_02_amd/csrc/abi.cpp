@@ -1,0 +1,117 @@
+// C ABI of the GPTQ layer solver: argument validation (host, before anything is
+// enqueued), workspace queries and stream-ordered launches.  Declarations and
+// the contract of every entry point are in include/gptq.h.
+#include "gptq.h"
+
+#include <cmath>
+
+#include "gptq_internal.h"
+
+namespace {
+
+constexpr int64_t kMaxDim = int64_t(1) << 20;        // d_col and d_row limits
+constexpr int64_t kMaxElems = int64_t(1) << 40;
+
+bool block_ok(int64_t b) { return b == 16 || b == 32 || b == 64 || b == 128; }
+
+gptq_status ws_check(const void* ws, size_t have, size_t need) {
+  if (need == 0) return GPTQ_OK;
+  if (ws == nullptr || have < need) return GPTQ_ERR_WORKSPACE;
+  return GPTQ_OK;
+}
+
+gptq_status from_hip(hipError_t e) { return e == hipSuccess ? GPTQ_OK : GPTQ_ERR_LAUNCH; }
+
+}  // namespace
+
+extern "C" {
+
+size_t gptq_hessian_accumulate_workspace_size(int64_t d_col, int64_t n_rows, int32_t x_dtype) {
+  if (d_col <= 0 || d_col > kMaxDim || n_rows <= 0 || (x_dtype != GPTQ_F32 && x_dtype != GPTQ_F16))
+    return 0;
+  return gptq::hessian_plan(d_col, n_rows, x_dtype).ws_bytes;
+}
+
+gptq_status gptq_hessian_accumulate(float* H, int64_t d_col, const void* X, int32_t x_dtype,
+                                    int64_t n_rows, int64_t ld_x, void* ws, size_t ws_bytes,
+                                    void* stream) {
+  if (d_col <= 0 || n_rows < 0) return GPTQ_ERR_BAD_SIZE;
+  if (d_col > kMaxDim || n_rows > kMaxElems / d_col) return GPTQ_ERR_TOO_LARGE;
+  if (x_dtype != GPTQ_F32 && x_dtype != GPTQ_F16) return GPTQ_ERR_BAD_DTYPE;
+  if (H == nullptr) return GPTQ_ERR_NULL_POINTER;
+  if (n_rows == 0) return GPTQ_OK;
+  if (X == nullptr) return GPTQ_ERR_NULL_POINTER;
+  if (ld_x < d_col) return GPTQ_ERR_BAD_LEADING_DIM;
+  const gptq::HessianPlan plan = gptq::hessian_plan(d_col, n_rows, x_dtype);
+  if (gptq_status st = ws_check(ws, ws_bytes, plan.ws_bytes)) return st;
+  return from_hip(gptq::hessian_launch(plan, H, d_col, X, n_rows, ld_x, ws, (hipStream_t)stream));
+}
+
+size_t gptq_prepare_hinv_workspace_size(int64_t d_col) {
+  if (d_col <= 0 || d_col > kMaxDim) return 0;
+  return gptq::factor_plan(d_col).ws_bytes;
+}
+
+gptq_status gptq_prepare_hinv(const float* H, int64_t d_col, float percdamp, float* U,
+                              float* lambda_out, int32_t* info, void* ws, size_t ws_bytes,
+                              void* stream) {
+  if (d_col <= 0) return GPTQ_ERR_BAD_SIZE;
+  if (d_col > kMaxDim) return GPTQ_ERR_TOO_LARGE;
+  if (H == nullptr || U == nullptr || lambda_out == nullptr || info == nullptr)
+    return GPTQ_ERR_NULL_POINTER;
+  if (!std::isfinite(percdamp) || percdamp < 0.f) return GPTQ_ERR_BAD_DAMP;
+  const gptq::FactorPlan plan = gptq::factor_plan(d_col);
+  if (gptq_status st = ws_check(ws, ws_bytes, plan.ws_bytes)) return st;
+  return from_hip(gptq::factor_launch(plan, H, percdamp, U, lambda_out, info, ws, (hipStream_t)stream));
+}
+
+size_t gptq_quantize_layer_workspace_size(int64_t d_row, int64_t d_col, int64_t block_size) {
+  if (d_row <= 0 || d_col <= 0 || d_row > kMaxDim || d_col > kMaxDim || !block_ok(block_size))
+    return 0;
+  return gptq::quant_plan(d_row, d_col, block_size).ws_bytes;
+}
+
+gptq_status gptq_quantize_layer(const void* W0, int32_t w_dtype, int64_t d_row, int64_t d_col,
+                                int64_t ld_w, const float* U, const float* lambda, int32_t bits,
+                                int64_t group_size, int64_t block_size, uint8_t* codes,
+                                float* scales, int32_t* zeros, double* out_err, void* ws,
+                                size_t ws_bytes, void* stream) {
+  if (d_row <= 0 || d_col <= 0) return GPTQ_ERR_BAD_SIZE;
+  if (d_row > kMaxDim || d_col > kMaxDim) return GPTQ_ERR_TOO_LARGE;
+  if (w_dtype != GPTQ_F32 && w_dtype != GPTQ_F16) return GPTQ_ERR_BAD_DTYPE;
+  if (W0 == nullptr || U == nullptr || codes == nullptr || scales == nullptr || zeros == nullptr ||
+      out_err == nullptr)
+    return GPTQ_ERR_NULL_POINTER;
+  if (ld_w < d_col) return GPTQ_ERR_BAD_LEADING_DIM;
+  if (bits < 2 || bits > 8) return GPTQ_ERR_BAD_BITS;
+  if (!block_ok(block_size)) return GPTQ_ERR_BAD_BLOCK;
+  if (group_size < 0 || (group_size > 0 && group_size % block_size != 0 &&
+                         block_size % group_size != 0))
+    return GPTQ_ERR_BAD_GROUP;
+  const gptq::QuantPlan plan = gptq::quant_plan(d_row, d_col, block_size);
+  if (gptq_status st = ws_check(ws, ws_bytes, plan.ws_bytes)) return st;
+  return from_hip(gptq::quant_launch(plan, W0, w_dtype, ld_w, U, lambda, bits, group_size, codes,
+                                     scales, zeros, out_err, ws, (hipStream_t)stream));
+}
+
+const char* gptq_status_string(int32_t status) {
+  switch (status) {
+    case GPTQ_OK: return "ok";
+    case GPTQ_ERR_NULL_POINTER: return "a required pointer is NULL";
+    case GPTQ_ERR_BAD_SIZE: return "a size is zero or negative";
+    case GPTQ_ERR_BAD_LEADING_DIM: return "leading dimension smaller than the row width";
+    case GPTQ_ERR_BAD_DTYPE: return "unsupported element type";
+    case GPTQ_ERR_BAD_BITS: return "bits must be in [2, 8]";
+    case GPTQ_ERR_BAD_BLOCK: return "block_size must be 16, 32, 64 or 128";
+    case GPTQ_ERR_BAD_GROUP: return "group_size must be 0 or divide / be divided by block_size";
+    case GPTQ_ERR_WORKSPACE: return "workspace missing or smaller than the query";
+    case GPTQ_ERR_BAD_DAMP: return "percdamp must be finite and >= 0";
+    case GPTQ_ERR_LAUNCH: return "a HIP launch or runtime call failed";
+    case GPTQ_ERR_TOO_LARGE: return "a size exceeds the library limits";
+    default: return "unknown status";
+  }
+}
+
+const char* gptq_version(void) { return "gptq-gfx950 0.1.0"; }
+
+}  // extern "C"

@@ -1,0 +1,72 @@
+// Internal declarations shared by the gfx950 kernels and the C ABI layer.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include <algorithm>
+#include <type_traits>
+
+namespace gptq {
+
+typedef _Float16 half8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef double f64x4 __attribute__((ext_vector_type(4)));
+
+inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// ---------------------------------------------------------------- Hessian
+struct HessianPlan {
+  int dtype;              // 0 = f32, 1 = f16
+  int bt;                 // square tile edge
+  int64_t tiles_side;     // ceil(d / bt)
+  int64_t ntiles;         // upper-triangle tiles
+  int64_t nsplit;         // row ranges reduced in a fixed order
+  int64_t rows_per_split;
+  size_t ws_bytes;        // partial tiles
+};
+HessianPlan hessian_plan(int64_t d, int64_t n, int dtype);
+hipError_t hessian_launch(const HessianPlan& p, float* H, int64_t d, const void* X, int64_t n,
+                          int64_t ldx, void* ws, hipStream_t s);
+
+// ---------------------------------------------------------------- factor
+struct FactorPlan {
+  int64_t d;
+  int nb;                 // Cholesky block
+  int64_t nblk;
+  size_t off_a64, off_dinv, off_tmp, off_lam, ws_bytes;
+};
+FactorPlan factor_plan(int64_t d);
+hipError_t factor_launch(const FactorPlan& p, const float* H, float percdamp, float* U,
+                         float* lambda_out, int32_t* info, void* ws, hipStream_t s);
+
+// ---------------------------------------------------------------- quantize
+struct QuantPlan {
+  int64_t d_row, d_col, B, nblk;
+  int64_t panel_wgs;      // work-groups of the panel kernel
+  size_t off_w, off_e, off_part, off_err, ws_bytes;
+};
+QuantPlan quant_plan(int64_t d_row, int64_t d_col, int64_t B);
+hipError_t quant_launch(const QuantPlan& p, const void* W0, int w_dtype, int64_t ldw,
+                        const float* U, const float* lambda, int bits, int64_t group,
+                        uint8_t* codes, float* scales, int32_t* zeros, double* out_err,
+                        void* ws, hipStream_t s);
+
+// fp32 C[m, n] += alpha * sum_k A[m, k] B[k, n] over a batch; every matrix
+// row-major.  kmode restricts k to exploit triangular operands:
+//   0: all k;  1: B lower triangular in (k, n) (k >= n);  2: A lower in (m, k) (k <= m)
+struct GemmBatch {
+  const float* A; const float* B; float* C;
+  int64_t lda, ldb, ldc;
+  int64_t sA, sB, sC;     // batch strides (elements)
+  int M, N, K, batch;
+  float alpha;
+  int beta_zero;          // 1: C = alpha*A*B (C not read)
+  int kmode;
+};
+hipError_t gemm_f32_launch(const GemmBatch& g, hipStream_t s);
+
+}  // namespace gptq

@@ -1,0 +1,356 @@
+// Hessian accumulation H += 2 X^T X on gfx950 matrix cores.
+//
+// Blog "GPTQ를 밑바닥부터 구현하며 배운 것들", section 3: H = 2 X^T X over the
+// calibration inputs; itwiki "GPTQ", minimal implementation: the same line.
+//
+// Design (MI355X): only the upper triangle of square tiles is computed.  The
+// calibration rows are split into row ranges ("splits"); every (tile, split)
+// pair is one work-group that accumulates in fp32 on MFMA and writes a partial
+// tile.  A reduce kernel adds the partials in split order (bitwise
+// reproducible, no float atomics), scales by 2, adds to H and mirrors the
+// tile into the lower triangle through LDS so both triangles are written with
+// coalesced stores.
+//
+// fp16 X: v_mfma_f32_32x32x16_f16, 256x256 tiles, 64 rows per stage.  X is
+// stored row-major (features contiguous), the MFMA wants 8 consecutive rows
+// per lane, so each thread loads an 8x8 block (8 rows x 16 bytes), transposes
+// it in registers and writes 8 features' 16-byte row chunks to LDS.  LDS rows
+// are 128 bytes; the 16-byte chunk c of feature m is stored at chunk
+// c ^ ((m ^ (m >> 3)) & 7), which keeps both these staging writes (lanes 8
+// features apart) and the fragment reads (consecutive features) free of bank
+// conflicts.
+// fp32 X: v_mfma_f32_32x32x2f32 reads one row value per lane, so the natural
+// [row][feature] LDS layout needs no transpose; 128x128 tiles.
+#include "gptq_internal.h"
+
+namespace gptq {
+namespace {
+
+constexpr int kThreads = 256;
+
+// upper-triangle tile enumeration t = tj (tj + 1) / 2 + ti with ti <= tj
+__device__ __forceinline__ void tile_of(int64_t t, int& ti, int& tj) {
+  int j = (int)((sqrt(8.0 * (double)t + 1.0) - 1.0) * 0.5);
+  while ((int64_t)(j + 1) * (j + 2) / 2 <= t) ++j;
+  while ((int64_t)j * (j + 1) / 2 > t) --j;
+  tj = j;
+  ti = (int)(t - (int64_t)j * (j + 1) / 2);
+}
+
+// work-group -> (tile, split).  With a multiple of 8 splits, XCD x (work-groups
+// are dispatched round-robin over the 8 XCDs) owns splits x, x + 8, ...: each
+// calibration row is read from HBM by one XCD and shared in its L2 by all the
+// tiles that XCD runs.
+__device__ __forceinline__ void wg_map(int64_t ntiles, int64_t nsplit, int64_t& tile,
+                                       int64_t& split) {
+  const int64_t bid = blockIdx.x;
+  if ((nsplit & 7) == 0) {
+    const int64_t loc = bid >> 3;
+    split = (bid & 7) + 8 * (loc / ntiles);
+    tile = loc % ntiles;
+  } else {
+    split = bid / ntiles;
+    tile = bid % ntiles;
+  }
+}
+
+// ------------------------------------------------------------------ fp16
+constexpr int kBT16 = 256, kKS16 = 64;
+
+__device__ __forceinline__ int sw16(int m, int c) {
+  return m * kKS16 + ((c ^ ((m ^ (m >> 3)) & 7)) << 3);
+}
+
+template <bool VEC>
+__global__ __launch_bounds__(kThreads) void syrk_f16_kernel(
+    const _Float16* __restrict__ X, int64_t ldx, int64_t n, int d, int64_t ntiles,
+    int64_t nsplit, int64_t rps, float* __restrict__ part) {
+  __shared__ __attribute__((aligned(16))) _Float16 lds[2][kBT16 * kKS16];
+  int64_t tile, split;
+  wg_map(ntiles, nsplit, tile, split);
+  int ti, tj;
+  tile_of(tile, ti, tj);
+  const bool diag = (ti == tj);
+  const int I0 = ti * kBT16, J0 = tj * kBT16;
+  const int64_t r0 = split * rps;
+  const int64_t r1 = min(n, r0 + rps);
+  const int t = threadIdx.x, lane = t & 63, w = t >> 6;
+  const int wm = w & 1, wn = w >> 1;
+  const int mg = t & 31, kg = t >> 5;
+
+  f32x16 acc[4][4];
+#pragma unroll
+  for (int a = 0; a < 4; ++a)
+#pragma unroll
+    for (int b = 0; b < 4; ++b)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[a][b][r] = 0.f;
+
+  half8 ra[8], rb[8];
+  auto gload = [&](int64_t k0, int col0, half8* r) {
+    const int col = col0 + mg * 8;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int64_t row = k0 + kg * 8 + i;
+      if (VEC) {
+        if (row < r1 && col < d) {
+          r[i] = *(const half8*)(X + row * ldx + col);
+        } else {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) r[i][e] = (_Float16)0.f;
+        }
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          r[i][e] = (row < r1 && col + e < d) ? X[row * ldx + col + e] : (_Float16)0.f;
+      }
+    }
+  };
+  auto lstore = [&](_Float16* L, const half8* r) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      half8 v;
+#pragma unroll
+      for (int k = 0; k < 8; ++k) v[k] = r[k][i];
+      *(half8*)(L + sw16(mg * 8 + i, kg)) = v;
+    }
+  };
+
+  const int64_t nst = (r1 > r0) ? (r1 - r0 + kKS16 - 1) / kKS16 : 0;
+  if (nst > 0) {
+    gload(r0, I0, ra);
+    if (!diag) gload(r0, J0, rb);
+  }
+  for (int64_t s = 0; s < nst; ++s) {
+    lstore(lds[0], ra);
+    if (!diag) lstore(lds[1], rb);
+    __syncthreads();
+    if (s + 1 < nst) {
+      gload(r0 + (s + 1) * kKS16, I0, ra);
+      if (!diag) gload(r0 + (s + 1) * kKS16, J0, rb);
+    }
+    const _Float16* LA = lds[0];
+    const _Float16* LB = diag ? lds[0] : lds[1];
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+      half8 a[4], b[4];
+      const int c = 2 * kk + (lane >> 5);
+#pragma unroll
+      for (int f = 0; f < 4; ++f) {
+        a[f] = *(const half8*)(LA + sw16(wm * 128 + f * 32 + (lane & 31), c));
+        b[f] = *(const half8*)(LB + sw16(wn * 128 + f * 32 + (lane & 31), c));
+      }
+#pragma unroll
+      for (int fm = 0; fm < 4; ++fm)
+#pragma unroll
+        for (int fn = 0; fn < 4; ++fn)
+          acc[fm][fn] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[fm], b[fn], acc[fm][fn], 0, 0, 0);
+    }
+    __syncthreads();
+  }
+  float* P = part + (split * ntiles + tile) * (int64_t)(kBT16 * kBT16);
+#pragma unroll
+  for (int fm = 0; fm < 4; ++fm)
+#pragma unroll
+    for (int fn = 0; fn < 4; ++fn)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int row = wm * 128 + fm * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+        const int col = wn * 128 + fn * 32 + (lane & 31);
+        P[row * kBT16 + col] = acc[fm][fn][r];
+      }
+}
+
+// ------------------------------------------------------------------ fp32
+constexpr int kBT32 = 128, kKS32 = 16, kP32 = kBT32 + 4;
+
+template <bool VEC>
+__global__ __launch_bounds__(kThreads) void syrk_f32_kernel(
+    const float* __restrict__ X, int64_t ldx, int64_t n, int d, int64_t ntiles, int64_t nsplit,
+    int64_t rps, float* __restrict__ part) {
+  __shared__ __attribute__((aligned(16))) float lds[2][kKS32 * kP32];
+  int64_t tile, split;
+  wg_map(ntiles, nsplit, tile, split);
+  int ti, tj;
+  tile_of(tile, ti, tj);
+  const bool diag = (ti == tj);
+  const int I0 = ti * kBT32, J0 = tj * kBT32;
+  const int64_t r0 = split * rps;
+  const int64_t r1 = min(n, r0 + rps);
+  const int t = threadIdx.x, lane = t & 63, w = t >> 6;
+  const int wm = w & 1, wn = w >> 1;
+  const int c4 = t & 31, rr = t >> 5;
+
+  f32x16 acc[2][2];
+#pragma unroll
+  for (int a = 0; a < 2; ++a)
+#pragma unroll
+    for (int b = 0; b < 2; ++b)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[a][b][r] = 0.f;
+
+  f32x4 ra[2], rb[2];
+  auto gload = [&](int64_t k0, int col0, f32x4* r) {
+    const int col = col0 + c4 * 4;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int64_t row = k0 + rr + 8 * i;
+      if (VEC) {
+        if (row < r1 && col < d) r[i] = *(const f32x4*)(X + row * ldx + col);
+        else r[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) r[i][e] = (row < r1 && col + e < d) ? X[row * ldx + col + e] : 0.f;
+      }
+    }
+  };
+  auto lstore = [&](float* L, const f32x4* r) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) *(f32x4*)(L + (rr + 8 * i) * kP32 + c4 * 4) = r[i];
+  };
+
+  const int64_t nst = (r1 > r0) ? (r1 - r0 + kKS32 - 1) / kKS32 : 0;
+  if (nst > 0) {
+    gload(r0, I0, ra);
+    if (!diag) gload(r0, J0, rb);
+  }
+  for (int64_t s = 0; s < nst; ++s) {
+    lstore(lds[0], ra);
+    if (!diag) lstore(lds[1], rb);
+    __syncthreads();
+    if (s + 1 < nst) {
+      gload(r0 + (s + 1) * kKS32, I0, ra);
+      if (!diag) gload(r0 + (s + 1) * kKS32, J0, rb);
+    }
+    const float* LA = lds[0];
+    const float* LB = diag ? lds[0] : lds[1];
+#pragma unroll
+    for (int kk = 0; kk < kKS32 / 2; ++kk) {
+      const int k = 2 * kk + (lane >> 5);
+      float a[2], b[2];
+#pragma unroll
+      for (int f = 0; f < 2; ++f) {
+        a[f] = LA[k * kP32 + wm * 64 + f * 32 + (lane & 31)];
+        b[f] = LB[k * kP32 + wn * 64 + f * 32 + (lane & 31)];
+      }
+#pragma unroll
+      for (int fm = 0; fm < 2; ++fm)
+#pragma unroll
+        for (int fn = 0; fn < 2; ++fn)
+          acc[fm][fn] = __builtin_amdgcn_mfma_f32_32x32x2f32(a[fm], b[fn], acc[fm][fn], 0, 0, 0);
+    }
+    __syncthreads();
+  }
+  float* P = part + (split * ntiles + tile) * (int64_t)(kBT32 * kBT32);
+#pragma unroll
+  for (int fm = 0; fm < 2; ++fm)
+#pragma unroll
+    for (int fn = 0; fn < 2; ++fn)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int row = wm * 64 + fm * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+        const int col = wn * 64 + fn * 32 + (lane & 31);
+        P[row * kBT32 + col] = acc[fm][fn][r];
+      }
+}
+
+// ------------------------------------------------------------------ reduce
+// One work-group per 64x64 sub-block of an upper tile: H_sub += 2 * sum over
+// splits (fixed order), and the mirror H_sub^T into the lower triangle.  On a
+// diagonal tile only its upper triangle is used, so H stays exactly symmetric.
+__global__ __launch_bounds__(kThreads) void syrk_reduce_kernel(
+    const float* __restrict__ part, int64_t ntiles, int64_t nsplit, int bt, int d,
+    float* __restrict__ H) {
+  __shared__ float tr[64][65];
+  const int nsub = bt / 64;
+  const int64_t b = blockIdx.x;
+  const int64_t tile = b / (nsub * nsub);
+  const int sb = (int)(b % (nsub * nsub));
+  const int sa = sb / nsub, sc = sb % nsub;
+  int ti, tj;
+  tile_of(tile, ti, tj);
+  const bool diag = (ti == tj);
+  if (diag && sa > sc) return;
+  const bool subdiag = diag && sa == sc;
+  const int64_t R0 = (int64_t)ti * bt + sa * 64, C0 = (int64_t)tj * bt + sc * 64;
+  const int t = threadIdx.x;
+  const int col = t & 63;
+  const int64_t tsz = (int64_t)bt * bt;
+  for (int i = 0; i < 16; ++i) {
+    const int row = (t >> 6) + 4 * i;
+    const float* p = part + tile * tsz + (int64_t)(sa * 64 + row) * bt + sc * 64 + col;
+    float s = 0.f;
+    for (int64_t sp = 0; sp < nsplit; ++sp) s += p[sp * ntiles * tsz];
+    s *= 2.f;
+    if (R0 + row < d && C0 + col < d && (!subdiag || row <= col)) H[(R0 + row) * d + C0 + col] += s;
+    tr[row][col] = s;
+  }
+  __syncthreads();
+  for (int i = 0; i < 16; ++i) {
+    const int orow = t & 63;            // row of the upper element
+    const int ocol = (t >> 6) + 4 * i;  // its column
+    if (subdiag && !(orow < ocol)) continue;
+    if (C0 + ocol < d && R0 + orow < d) H[(C0 + ocol) * d + R0 + orow] += tr[orow][ocol];
+  }
+}
+
+}  // namespace
+
+HessianPlan hessian_plan(int64_t d, int64_t n, int dtype) {
+  HessianPlan p{};
+  p.dtype = dtype;
+  p.bt = (dtype == 1) ? kBT16 : kBT32;
+  const int ks = (dtype == 1) ? kKS16 : kKS32;
+  p.tiles_side = cdiv(d, p.bt);
+  p.ntiles = p.tiles_side * (p.tiles_side + 1) / 2;
+  if (n <= 0) {
+    p.nsplit = 0;
+    p.rows_per_split = 0;
+    p.ws_bytes = 0;
+    return p;
+  }
+  // enough work-groups to fill 256 CUs several times, and at most 32768 rows
+  // per fp32 accumulation chain
+  int64_t ns = std::max<int64_t>(cdiv(1024, p.ntiles), cdiv(n, 32768));
+  const int64_t cap = std::max<int64_t>(1, cdiv(n, 1024));
+  if (ns > 8) ns = cdiv(ns, 8) * 8;
+  ns = std::min(ns, cap);
+  int64_t rps = cdiv(n, ns);
+  rps = cdiv(rps, ks) * ks;
+  p.rows_per_split = rps;
+  p.nsplit = cdiv(n, rps);
+  p.ws_bytes = (size_t)p.nsplit * (size_t)p.ntiles * (size_t)p.bt * (size_t)p.bt * sizeof(float);
+  return p;
+}
+
+hipError_t hessian_launch(const HessianPlan& p, float* H, int64_t d, const void* X, int64_t n,
+                          int64_t ldx, void* ws, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  float* part = (float*)ws;
+  const int64_t grid = p.ntiles * p.nsplit;
+  if (p.dtype == 1) {
+    const bool vec = (d % 8 == 0) && (ldx % 8 == 0) && (((uintptr_t)X & 15) == 0);
+    if (vec)
+      hipLaunchKernelGGL(syrk_f16_kernel<true>, dim3((unsigned)grid), dim3(kThreads), 0, s,
+                         (const _Float16*)X, ldx, n, (int)d, p.ntiles, p.nsplit, p.rows_per_split, part);
+    else
+      hipLaunchKernelGGL(syrk_f16_kernel<false>, dim3((unsigned)grid), dim3(kThreads), 0, s,
+                         (const _Float16*)X, ldx, n, (int)d, p.ntiles, p.nsplit, p.rows_per_split, part);
+  } else {
+    const bool vec = (d % 4 == 0) && (ldx % 4 == 0) && (((uintptr_t)X & 15) == 0);
+    if (vec)
+      hipLaunchKernelGGL(syrk_f32_kernel<true>, dim3((unsigned)grid), dim3(kThreads), 0, s,
+                         (const float*)X, ldx, n, (int)d, p.ntiles, p.nsplit, p.rows_per_split, part);
+    else
+      hipLaunchKernelGGL(syrk_f32_kernel<false>, dim3((unsigned)grid), dim3(kThreads), 0, s,
+                         (const float*)X, ldx, n, (int)d, p.ntiles, p.nsplit, p.rows_per_split, part);
+  }
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int nsub = p.bt / 64;
+  hipLaunchKernelGGL(syrk_reduce_kernel, dim3((unsigned)(p.ntiles * nsub * nsub)), dim3(kThreads),
+                     0, s, part, p.ntiles, p.nsplit, p.bt, (int)d, H);
+  return hipGetLastError();
+}
+
+}  // namespace gptq

@@ -1,0 +1,371 @@
+// The lazy-batch quantization loop (itwiki "GPTQ": Algorithm 1, minimal
+// implementation, practical variants / group quantization).
+//
+//   grid  per row from W0 (scale = max(max - min, 1e-8) / maxq, zero =
+//         round(-min / scale)), or per group from the current weights when
+//         the group's first column is reached;
+//   panel for each column j of a block: c = clamp(round(w/scale) + zero, 0,
+//         maxq); e = (w - scale (c - zero)) / U[j,j]; W[:, j:] -= e U[j, j:]
+//         inside the block; E[:, j] = e;
+//   GEMM  W[:, i+B:] -= E U[i:i+B, i+B:]  (gemm.hip);
+//   error ||X dW^T||^2 = 1/2 ||E||^2 - lambda/2 ||dW||^2 (the damped objective
+//         is 1/2 ||E||^2 by the OBS increment of the wiki's OBQ equation).
+//
+// Panel layout (gfx950): rows are independent (all rows share U, the wiki's
+// change 1), so a wave holds 4 rows and each row is spread over a 16-lane DPP
+// row, 8 consecutive block columns per lane (B = 128).  Per column the owner
+// lane's scaled error reaches the other 15 lanes of its row with one DPP
+// row_newbcast, and every lane applies the rank-1 update to its own columns
+// with U[j, :] read from LDS (the block's diagonal part of U lives there).
+// Per-group min/max is a 16-lane butterfly.  No block-wide barrier is needed
+// after U is staged.
+#include "gptq_internal.h"
+
+namespace gptq {
+namespace {
+
+constexpr int kThreads = 256;
+
+template <int I, int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (I < N) {
+    f(std::integral_constant<int, I>{});
+    static_for<I + 1, N>(f);
+  }
+}
+
+// lane (16 * (lane / 16) + K) of the caller's DPP row, broadcast to the row
+template <int K>
+__device__ __forceinline__ float row_bcast(float v) {
+  return __builtin_bit_cast(
+      float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x150 + K, 0xF, 0xF, false));
+}
+
+__device__ __forceinline__ void grid_from_minmax(float mn, float mx, int maxq, float& s, float& z) {
+  s = fmaxf(mx - mn, 1e-8f) / (float)maxq;
+  z = rintf(-mn / s);
+}
+
+__global__ void zero_f64_kernel(double* p, int64_t n) {
+  for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n;
+       i += (int64_t)gridDim.x * blockDim.x)
+    p[i] = 0.0;
+}
+
+// fp32 working copy of W0; with a per-row grid also that row's scale / zero
+template <typename T>
+__global__ __launch_bounds__(kThreads) void prep_kernel(const T* __restrict__ W0, int64_t ldw,
+                                                        int64_t d_col, float* __restrict__ W,
+                                                        int per_row, int maxq,
+                                                        float* __restrict__ scales,
+                                                        int32_t* __restrict__ zeros) {
+  __shared__ float smn[kThreads], smx[kThreads];
+  const int64_t row = blockIdx.x;
+  const int t = threadIdx.x;
+  float mn = INFINITY, mx = -INFINITY;
+  for (int64_t c = t; c < d_col; c += kThreads) {
+    const float v = (float)W0[row * ldw + c];
+    W[row * d_col + c] = v;
+    mn = fminf(mn, v);
+    mx = fmaxf(mx, v);
+  }
+  if (!per_row) return;
+  smn[t] = mn;
+  smx[t] = mx;
+  __syncthreads();
+  for (int o = kThreads / 2; o > 0; o >>= 1) {
+    if (t < o) {
+      smn[t] = fminf(smn[t], smn[t + o]);
+      smx[t] = fmaxf(smx[t], smx[t + o]);
+    }
+    __syncthreads();
+  }
+  if (t == 0) {
+    float s, z;
+    grid_from_minmax(smn[0], smx[0], maxq, s, z);
+    scales[row] = s;
+    zeros[row] = (int32_t)z;
+  }
+}
+
+// group grid for groups wider than the block, at a block start: one wave per row
+__global__ __launch_bounds__(kThreads) void group_grid_kernel(const float* __restrict__ W,
+                                                              int64_t d_row, int64_t d_col,
+                                                              int64_t g0, int64_t gw, int64_t gi,
+                                                              int64_t ngroups, int maxq,
+                                                              float* __restrict__ scales,
+                                                              int32_t* __restrict__ zeros) {
+  const int lane = threadIdx.x & 63;
+  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= d_row) return;
+  float mn = INFINITY, mx = -INFINITY;
+  for (int64_t c = g0 + lane; c < g0 + gw; c += 64) {
+    const float v = W[row * d_col + c];
+    mn = fminf(mn, v);
+    mx = fmaxf(mx, v);
+  }
+  for (int o = 32; o > 0; o >>= 1) {
+    mn = fminf(mn, __shfl_xor(mn, o, 64));
+    mx = fmaxf(mx, __shfl_xor(mx, o, 64));
+  }
+  if (lane == 0) {
+    float s, z;
+    grid_from_minmax(mn, mx, maxq, s, z);
+    scales[row * ngroups + gi] = s;
+    zeros[row * ngroups + gi] = (int32_t)z;
+  }
+}
+
+// One block of columns [i1, i1 + width) for 16 rows per work-group.
+// group: 0 = per-row grid (read from scales/zeros), <= B = computed here at
+// group starts, > B = read (computed by group_grid_kernel at the block start).
+template <int CPL>
+__global__ __launch_bounds__(kThreads) void panel_kernel(
+    float* __restrict__ W, int64_t d_row, int64_t d_col, int64_t i1, int width,
+    const float* __restrict__ U, int maxq, int64_t group, int64_t ngroups,
+    uint8_t* __restrict__ codes, float* __restrict__ scales, int32_t* __restrict__ zeros,
+    float* __restrict__ E, double* __restrict__ part_e) {
+  constexpr int B = 16 * CPL;
+  __shared__ __attribute__((aligned(16))) float Us[B * B];
+  __shared__ float rd[B];
+  __shared__ double red[kThreads / 64];
+  const int t = threadIdx.x;
+  for (int idx = t; idx < B * B; idx += kThreads) {
+    const int r = idx / B, c = idx % B;
+    Us[idx] = (r < width && c < width && c >= r) ? U[(i1 + r) * d_col + i1 + c] : 0.f;
+  }
+  for (int r = t; r < B; r += kThreads) rd[r] = (r < width) ? 1.0f / U[(i1 + r) * d_col + i1 + r] : 0.f;
+  __syncthreads();
+
+  const int lane = t & 63, p = lane & 15;
+  const int64_t row = (int64_t)blockIdx.x * 16 + (t >> 6) * 4 + (lane >> 4);
+  const bool valid = row < d_row;
+  const int64_t rowc = valid ? row : d_row - 1;
+  float w[CPL], cr[CPL], er[CPL];
+#pragma unroll
+  for (int r = 0; r < CPL; ++r) {
+    const int col = p * CPL + r;
+    w[r] = (col < width) ? W[rowc * d_col + i1 + col] : 0.f;
+    cr[r] = 0.f;
+    er[r] = 0.f;
+  }
+  float s = 1.f, z = 0.f;
+  if (group == 0) {
+    s = scales[rowc];
+    z = (float)zeros[rowc];
+  } else if (group > B) {
+    const int64_t gi = i1 / group;
+    s = scales[rowc * ngroups + gi];
+    z = (float)zeros[rowc * ngroups + gi];
+  }
+  float rs = 1.f / s;
+  const float fmaxq = (float)maxq;
+
+  static_for<0, 16>([&](auto kc) {
+    constexpr int kk = decltype(kc)::value;
+#pragma unroll
+    for (int jj = 0; jj < CPL; ++jj) {
+      const int j = kk * CPL + jj;
+      if (j < width) {
+        if (group > 0 && group <= B && (j % group) == 0) {
+          float mn = INFINITY, mx = -INFINITY;
+#pragma unroll
+          for (int r = 0; r < CPL; ++r) {
+            const int col = p * CPL + r;
+            if (col >= j && col < j + group && col < width) {
+              mn = fminf(mn, w[r]);
+              mx = fmaxf(mx, w[r]);
+            }
+          }
+#pragma unroll
+          for (int o = 8; o > 0; o >>= 1) {
+            mn = fminf(mn, __shfl_xor(mn, o, 16));
+            mx = fmaxf(mx, __shfl_xor(mx, o, 16));
+          }
+          grid_from_minmax(mn, mx, maxq, s, z);
+          rs = 1.f / s;
+          if (p == 0 && valid) {
+            const int64_t gi = (i1 + j) / group;
+            scales[row * ngroups + gi] = s;
+            zeros[row * ngroups + gi] = (int32_t)z;
+          }
+        }
+        const float x = w[jj];
+        const float c = fminf(fmaxf(rintf(x * rs) + z, 0.f), fmaxq);
+        const float e = (x - s * (c - z)) * rd[j];
+        if (p == kk) {
+          cr[jj] = c;
+          er[jj] = e;
+        }
+        const float eb = row_bcast<kk>(e);
+        const float* ur = &Us[j * B + p * CPL];
+#pragma unroll
+        for (int r = 0; r < CPL; ++r) w[r] = fmaf(-eb, ur[r], w[r]);
+      }
+    }
+  });
+
+  double se = 0.0;
+#pragma unroll
+  for (int r = 0; r < CPL; ++r) {
+    const int col = p * CPL + r;
+    if (valid && col < width) {
+      codes[row * d_col + i1 + col] = (uint8_t)cr[r];
+      E[row * B + col] = er[r];
+      se += (double)er[r] * (double)er[r];
+    }
+  }
+  for (int o = 32; o > 0; o >>= 1) se += __shfl_xor(se, o, 64);
+  if (lane == 0) red[t >> 6] = se;
+  __syncthreads();
+  if (t == 0) part_e[blockIdx.x] += (red[0] + red[1]) + (red[2] + red[3]);
+}
+
+// sum over rows of (W0 - scale (c - zero))^2, per work-group partials
+template <typename T>
+__global__ __launch_bounds__(kThreads) void err_delta_kernel(
+    const T* __restrict__ W0, int64_t ldw, int64_t d_row, int64_t d_col,
+    const uint8_t* __restrict__ codes, const float* __restrict__ scales,
+    const int32_t* __restrict__ zeros, int64_t g, int64_t ngroups, double* __restrict__ part_d) {
+  __shared__ double red[kThreads];
+  const int t = threadIdx.x;
+  double acc = 0.0;
+  for (int64_t row = blockIdx.x; row < d_row; row += gridDim.x) {
+    for (int64_t c = t; c < d_col; c += kThreads) {
+      const int64_t gi = c / g;
+      const float s = scales[row * ngroups + gi];
+      const float z = (float)zeros[row * ngroups + gi];
+      const float wh = s * ((float)codes[row * d_col + c] - z);
+      const double dlt = (double)(float)W0[row * ldw + c] - (double)wh;
+      acc += dlt * dlt;
+    }
+  }
+  red[t] = acc;
+  __syncthreads();
+  for (int o = kThreads / 2; o > 0; o >>= 1) {
+    if (t < o) red[t] += red[t + o];
+    __syncthreads();
+  }
+  if (t == 0) part_d[blockIdx.x] = red[0];
+}
+
+__global__ __launch_bounds__(kThreads) void err_final_kernel(const double* __restrict__ part_e,
+                                                             int64_t ne,
+                                                             const double* __restrict__ part_d,
+                                                             int64_t nd, const float* lambda,
+                                                             double* out) {
+  __shared__ double re[kThreads], rdd[kThreads];
+  const int t = threadIdx.x;
+  double a = 0.0, b = 0.0;
+  for (int64_t i = t; i < ne; i += kThreads) a += part_e[i];
+  for (int64_t i = t; i < nd; i += kThreads) b += part_d[i];
+  re[t] = a;
+  rdd[t] = b;
+  __syncthreads();
+  for (int o = kThreads / 2; o > 0; o >>= 1) {
+    if (t < o) {
+      re[t] += re[t + o];
+      rdd[t] += rdd[t + o];
+    }
+    __syncthreads();
+  }
+  if (t == 0) *out = 0.5 * re[0] - (lambda ? 0.5 * (double)*lambda * rdd[0] : 0.0);
+}
+
+constexpr int64_t kErrWGs = 1024;
+
+}  // namespace
+
+QuantPlan quant_plan(int64_t d_row, int64_t d_col, int64_t B) {
+  QuantPlan p{};
+  p.d_row = d_row;
+  p.d_col = d_col;
+  p.B = B;
+  p.nblk = cdiv(d_col, B);
+  p.panel_wgs = cdiv(d_row, 16);
+  size_t off = 0;
+  p.off_w = off;
+  off = align_up(off + (size_t)d_row * d_col * sizeof(float), 256);
+  p.off_e = off;
+  off = align_up(off + (size_t)d_row * B * sizeof(float), 256);
+  p.off_part = off;
+  off = align_up(off + (size_t)p.panel_wgs * sizeof(double), 256);
+  p.off_err = off;
+  off = align_up(off + (size_t)kErrWGs * sizeof(double), 256);
+  p.ws_bytes = off;
+  return p;
+}
+
+hipError_t quant_launch(const QuantPlan& p, const void* W0, int w_dtype, int64_t ldw,
+                        const float* U, const float* lambda, int bits, int64_t group,
+                        uint8_t* codes, float* scales, int32_t* zeros, double* out_err, void* ws,
+                        hipStream_t s) {
+  const int64_t d_row = p.d_row, d_col = p.d_col, B = p.B;
+  char* base = (char*)ws;
+  float* W = (float*)(base + p.off_w);
+  float* E = (float*)(base + p.off_e);
+  double* part_e = (double*)(base + p.off_part);
+  double* part_d = (double*)(base + p.off_err);
+  const int maxq = (1 << bits) - 1;
+  const int64_t ngroups = group ? cdiv(d_col, group) : 1;
+  hipError_t e;
+  hipLaunchKernelGGL(zero_f64_kernel, dim3(64), dim3(kThreads), 0, s, part_e, p.panel_wgs);
+  if (w_dtype == 1)
+    hipLaunchKernelGGL(prep_kernel<_Float16>, dim3((unsigned)d_row), dim3(kThreads), 0, s,
+                       (const _Float16*)W0, ldw, d_col, W, group == 0, maxq, scales, zeros);
+  else
+    hipLaunchKernelGGL(prep_kernel<float>, dim3((unsigned)d_row), dim3(kThreads), 0, s,
+                       (const float*)W0, ldw, d_col, W, group == 0, maxq, scales, zeros);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  for (int64_t i1 = 0; i1 < d_col; i1 += B) {
+    const int width = (int)std::min<int64_t>(B, d_col - i1);
+    if (group > B && i1 % group == 0) {
+      const int64_t gw = std::min<int64_t>(group, d_col - i1);
+      hipLaunchKernelGGL(group_grid_kernel, dim3((unsigned)cdiv(d_row, 4)), dim3(kThreads), 0, s, W,
+                         d_row, d_col, i1, gw, i1 / group, ngroups, maxq, scales, zeros);
+    }
+    const dim3 pg((unsigned)p.panel_wgs), pb(kThreads);
+    switch (B) {
+      case 16:
+        hipLaunchKernelGGL(panel_kernel<1>, pg, pb, 0, s, W, d_row, d_col, i1, width, U, maxq, group,
+                           ngroups, codes, scales, zeros, E, part_e);
+        break;
+      case 32:
+        hipLaunchKernelGGL(panel_kernel<2>, pg, pb, 0, s, W, d_row, d_col, i1, width, U, maxq, group,
+                           ngroups, codes, scales, zeros, E, part_e);
+        break;
+      case 64:
+        hipLaunchKernelGGL(panel_kernel<4>, pg, pb, 0, s, W, d_row, d_col, i1, width, U, maxq, group,
+                           ngroups, codes, scales, zeros, E, part_e);
+        break;
+      default:
+        hipLaunchKernelGGL(panel_kernel<8>, pg, pb, 0, s, W, d_row, d_col, i1, width, U, maxq, group,
+                           ngroups, codes, scales, zeros, E, part_e);
+        break;
+    }
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    const int64_t i2 = i1 + width;
+    if (i2 < d_col) {
+      GemmBatch g{};
+      g.A = E; g.lda = B;
+      g.B = U + i1 * d_col + i2; g.ldb = d_col;
+      g.C = W + i2; g.ldc = d_col;
+      g.M = (int)d_row; g.N = (int)(d_col - i2); g.K = width; g.batch = 1;
+      g.alpha = -1.f; g.beta_zero = 0; g.kmode = 0;
+      if ((e = gemm_f32_launch(g, s)) != hipSuccess) return e;
+    }
+  }
+  const unsigned nerr = (unsigned)std::min<int64_t>(kErrWGs, d_row);
+  const int64_t gsz = group ? group : d_col;
+  if (w_dtype == 1)
+    hipLaunchKernelGGL(err_delta_kernel<_Float16>, dim3(nerr), dim3(kThreads), 0, s,
+                       (const _Float16*)W0, ldw, d_row, d_col, codes, scales, zeros, gsz, ngroups, part_d);
+  else
+    hipLaunchKernelGGL(err_delta_kernel<float>, dim3(nerr), dim3(kThreads), 0, s, (const float*)W0, ldw,
+                       d_row, d_col, codes, scales, zeros, gsz, ngroups, part_d);
+  hipLaunchKernelGGL(err_final_kernel, dim3(1), dim3(kThreads), 0, s, part_e, p.panel_wgs, part_d,
+                     (int64_t)nerr, lambda, out_err);
+  return hipGetLastError();
+}
+
+}  // namespace gptq
