@@ -1,0 +1,208 @@
+#!/usr/bin/env python3
+"""Benchmark of the GPTQ layer solver on one MI355X.
+
+One step = one whole layer through the three C-ABI calls with the inputs
+already resident in HBM: H := 0; H += 2 X^T X over all calibration rows;
+damping + U; the lazy-batch loop with the output error.  Workload: a
+4096 x 4096 fp16 attention projection, X = 262144 x 4096 fp16 (rank-64
+covariance, 1% outlier channels at 20x), 4-bit asymmetric grid, group 128,
+block 128, 1% damping.
+
+Prints one JSON line.  The metric is seconds per layer (lower is better), with
+per-stage TFLOP/s and the dominant kernel's roofline fraction.  The CPU
+baseline is the fp64 oracle timed on a bounded sample of the same layer and
+scaled to one layer.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_F16_MFMA_TFLOPS = 2516.6     # MI355X dense fp16 matrix peak
+PEAK_F32_MFMA_TFLOPS = 157.3
+PEAK_F64_TFLOPS = 78.6
+PEAK_HBM_GBS = 8000.0
+METRIC = "GPTQ s/layer + Hessian/trailing-GEMM TFLOPS (4096×4096, 4-bit g128) at 1 GPU"
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--traffic", default=os.path.join(ROOT, "profiles", "syrk_f16_attn4096_traffic.json"),
+                    help="rocprofv3 --pmc derived HBM bytes of the dominant kernel (JSON), if any")
+    return ap.parse_args()
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def cpu_baseline(spec, W, X_chunk0):
+    """The fp64 oracle on a bounded sample of the same layer, scaled to one layer."""
+    import numpy as np
+    import oracle as O
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = len(os.sched_getaffinity(0))
+    n_chunks = spec.n_rows // X_chunk0.shape[0]
+    t0 = time.perf_counter()
+    H = O.hessian([X_chunk0])
+    t_h = (time.perf_counter() - t0) * n_chunks
+    t0 = time.perf_counter()
+    Hl, lam = O.damp(H * n_chunks, spec.percdamp)
+    U = O.inv_hessian_factor(Hl)
+    t_f = time.perf_counter() - t0
+    rows = 256
+    t0 = time.perf_counter()
+    O.gptq_quantize(W[:rows].astype(np.float64), U, spec.bits, spec.group_size, spec.block_size)
+    t_q = (time.perf_counter() - t0) * (spec.d_row / rows)
+    total = t_h + t_f + t_q
+    return {"value": total, "unit": "s/layer", "cores": int(threads), "kind": "oracle",
+            "sample": (f"H over {X_chunk0.shape[0]} of {spec.n_rows} calibration rows (x{n_chunks}), "
+                       f"full {spec.d_col}x{spec.d_col} fp64 factor, loop on {rows} of {spec.d_row} "
+                       f"weight rows (x{spec.d_row // rows}); scaled to one layer"),
+            "stages_s": {"hessian": t_h, "factor": t_f, "loop": t_q}}
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus > 1 or world > 1:
+        print("bench.py: this solver runs on one GPU; multi-GPU runs are not supported "
+              "(use --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+    import numpy as np
+    import torch
+
+    import post_weight_quantization_02_amd as G
+    import workloads as wl
+
+    spec = wl.workload_layers(3)[0]
+    dev = torch.device("cuda:0")
+    log(f"bench: generating {spec.name} W {spec.d_row}x{spec.d_col}, X {spec.n_rows}x{spec.d_col} fp16")
+    t0 = time.perf_counter()
+    W = wl.make_weight(spec)
+    Xd = torch.empty(spec.n_rows, spec.d_col, dtype=torch.float16, device=dev)
+    x0 = None
+    for c in range(wl.n_chunks(spec)):
+        xc = wl.make_x_chunk(spec, c)
+        if c == 0:
+            x0 = xc
+        Xd[c * wl.CHUNK_ROWS:(c + 1) * wl.CHUNK_ROWS].copy_(torch.from_numpy(xc))
+    Wd = torch.from_numpy(W).to(dev)
+    torch.cuda.synchronize()
+    log(f"bench: inputs resident in {time.perf_counter() - t0:.1f}s")
+
+    d, n, dr = spec.d_col, spec.n_rows, spec.d_row
+    ng = d // spec.group_size
+    H = torch.zeros(d, d, dtype=torch.float32, device=dev)
+    U = torch.empty(d, d, dtype=torch.float32, device=dev)
+    lam = torch.empty(1, dtype=torch.float32, device=dev)
+    info = torch.empty(1, dtype=torch.int32, device=dev)
+    codes = torch.empty(dr, d, dtype=torch.uint8, device=dev)
+    scales = torch.empty(dr, ng, dtype=torch.float32, device=dev)
+    zeros = torch.empty(dr, ng, dtype=torch.int32, device=dev)
+    err = torch.empty(1, dtype=torch.float64, device=dev)
+    ws_h = torch.empty(G.gptq_hessian_accumulate_workspace_size(d, n, G.GPTQ_F16), dtype=torch.uint8, device=dev)
+    ws_f = torch.empty(G.gptq_prepare_hinv_workspace_size(d), dtype=torch.uint8, device=dev)
+    ws_q = torch.empty(G.gptq_quantize_layer_workspace_size(dr, d, spec.block_size), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def step(ev=None):
+        if ev:
+            ev[0].record(stream)
+        H.zero_()
+        G.gptq_hessian_accumulate(H, Xd, ws=ws_h, stream=stream)
+        if ev:
+            ev[1].record(stream)
+        G.gptq_prepare_hinv(H, spec.percdamp, U, lam, info, ws=ws_f, stream=stream)
+        if ev:
+            ev[2].record(stream)
+        G.gptq_quantize_layer(Wd, U, lam, spec.bits, spec.group_size, spec.block_size, codes, scales,
+                              zeros, err, ws=ws_q, stream=stream)
+        if ev:
+            ev[3].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    if int(info.item()) != 0:
+        raise SystemExit(f"factor failed: info={int(info.item())}")
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(args.steps):
+        step(evs[k])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    st = np.array([[e[0].elapsed_time(e[1]), e[1].elapsed_time(e[2]), e[2].elapsed_time(e[3])]
+                   for e in evs]) / 1e3   # seconds: hessian, factor, quantize
+    per_step = wall / args.steps
+    t_h, t_f, t_q = (float(np.mean(st[:, i])) for i in range(3))
+    flops_h = n * d * (d + 1)                       # upper triangle of X^T X, 2 flop per MAC
+    flops_f = 2.0 * d ** 3 / 3.0                    # Cholesky d^3/3 + triangular inverse d^3/3
+    flops_gemm = dr * d * (d - spec.block_size)     # sum over blocks of 2 * d_row * B * (d - i2)
+    log(f"bench: stages ms hessian {t_h * 1e3:.3f} factor {t_f * 1e3:.3f} quantize {t_q * 1e3:.3f}; "
+        f"wall/step {per_step * 1e3:.3f} ms; err {float(err.item()):.6g}")
+
+    traffic = None
+    if args.traffic and os.path.exists(args.traffic):
+        try:
+            with open(args.traffic) as f:
+                tr = json.load(f)
+            traffic = tr.get("hbm_bytes_per_launch")
+        except Exception:
+            traffic = None
+    ach = flops_h / t_h / 1e12
+    roof = {"bound": "mfma", "kernel": "gptq_hessian_accumulate: syrk_f16_kernel + fixed-order split reduce",
+            "achieved": round(ach, 2), "peak": PEAK_F16_MFMA_TFLOPS, "unit": "TFLOP/s",
+            "frac": round(ach / PEAK_F16_MFMA_TFLOPS, 4), "traffic": traffic}
+
+    out = {
+        "metric": METRIC,
+        "value": round(per_step, 6),
+        "unit": "s/layer",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(per_step * 1e3, 4),
+        "higher_is_better": False,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16-mfma(f32 acc) syrk / f64 Cholesky / f32 loop",
+        "data": "synthetic",
+        "config": {"workload": "attn_4096: W 4096x4096 fp16, X 262144x4096 fp16 rank-64 + 1% 20x outliers, "
+                               "4-bit asymmetric, group 128, block 128, 1% damping",
+                   "d_row": dr, "d_col": d, "n_rows": n, "bits": spec.bits,
+                   "group_size": spec.group_size, "block_size": spec.block_size,
+                   "parallelism": "single-gpu"},
+        "stages": {
+            "hessian_ms": round(t_h * 1e3, 4), "hessian_tflops": round(flops_h / t_h / 1e12, 2),
+            "factor_ms": round(t_f * 1e3, 4), "factor_tflops": round(flops_f / t_f / 1e12, 3),
+            "quantize_ms": round(t_q * 1e3, 4),
+            "quantize_trailing_gemm_tflops_if_whole_stage": round(flops_gemm / t_q / 1e12, 2),
+            "err": float(err.item()),
+        },
+        "roofline": roof,
+    }
+    if not args.no_cpu_baseline:
+        log("bench: timing the fp64 oracle on a bounded sample (CPU)")
+        cb = cpu_baseline(spec, W, x0)
+        out["cpu_baseline"] = cb
+        out["gpu_speedup_vs_cpu_oracle"] = round(cb["value"] / per_step, 1)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()
