@@ -47,7 +47,7 @@ typedef enum {
   GPTQ_ERR_BAD_DTYPE = 4,       /* element type not GPTQ_F32 / GPTQ_F16   */
   GPTQ_ERR_BAD_BITS = 5,        /* bits outside [2, 8]                    */
   GPTQ_ERR_BAD_BLOCK = 6,       /* block_size not one of 16, 32, 64, 128  */
-  GPTQ_ERR_BAD_GROUP = 7,       /* group_size and block_size misaligned   */
+  GPTQ_ERR_BAD_GROUP = 7,       /* group_size not 0 / 16k aligned with B  */
   GPTQ_ERR_WORKSPACE = 8,       /* ws NULL or smaller than the query      */
   GPTQ_ERR_BAD_DAMP = 9,        /* percdamp negative or not finite        */
   GPTQ_ERR_LAUNCH = 10,         /* a HIP launch or runtime call failed    */
@@ -132,8 +132,11 @@ size_t gptq_prepare_hinv_workspace_size(int64_t d_col);
  *              gptq_prepare_hinv (only the upper triangle is read).
  *   lambda     [device] one float from gptq_prepare_hinv, or NULL.
  *   bits       2..8.
- *   group_size 0 (one grid per row) or a positive size with
- *              group_size % block_size == 0 or block_size % group_size == 0.
+ *   group_size 0 (one grid per row) or a positive multiple of 16 with
+ *              group_size % block_size == 0 or block_size % group_size == 0
+ *              (so a group never starts inside a block except at a
+ *              multiple of its size, and its parameters come from fully
+ *              updated weights).
  *   block_size 16, 32, 64 or 128 (the pages use 128); the last block may be
  *              partial.
  *   codes      [device] uint8 [d_row x d_col] row-major output codes.

@@ -85,8 +85,9 @@ gptq_status gptq_quantize_layer(const void* W0, int32_t w_dtype, int64_t d_row, 
   if (ld_w < d_col) return GPTQ_ERR_BAD_LEADING_DIM;
   if (bits < 2 || bits > 8) return GPTQ_ERR_BAD_BITS;
   if (!block_ok(block_size)) return GPTQ_ERR_BAD_BLOCK;
-  if (group_size < 0 || (group_size > 0 && group_size % block_size != 0 &&
-                         block_size % group_size != 0))
+  if (group_size < 0 || (group_size > 0 && (group_size % 16 != 0 ||
+                                            (group_size % block_size != 0 &&
+                                             block_size % group_size != 0))))
     return GPTQ_ERR_BAD_GROUP;
   const gptq::QuantPlan plan = gptq::quant_plan(d_row, d_col, block_size);
   if (gptq_status st = ws_check(ws, ws_bytes, plan.ws_bytes)) return st;
@@ -103,7 +104,7 @@ const char* gptq_status_string(int32_t status) {
     case GPTQ_ERR_BAD_DTYPE: return "unsupported element type";
     case GPTQ_ERR_BAD_BITS: return "bits must be in [2, 8]";
     case GPTQ_ERR_BAD_BLOCK: return "block_size must be 16, 32, 64 or 128";
-    case GPTQ_ERR_BAD_GROUP: return "group_size must be 0 or divide / be divided by block_size";
+    case GPTQ_ERR_BAD_GROUP: return "group_size must be 0, or a multiple of 16 that divides or is divided by block_size";
     case GPTQ_ERR_WORKSPACE: return "workspace missing or smaller than the query";
     case GPTQ_ERR_BAD_DAMP: return "percdamp must be finite and >= 0";
     case GPTQ_ERR_LAUNCH: return "a HIP launch or runtime call failed";

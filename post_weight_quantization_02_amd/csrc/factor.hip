@@ -16,10 +16,9 @@
 // fp32 (MFMA), whose error stays ~1e-6.
 //
 // Kernels: damp (lambda, info = 0) -> reversed fp64 copy with lambda on the
-// diagonal -> per 64-column block: diagonal factor + its inverse in LDS (one
-// work-group), panel solve and trailing update (fp64 MFMA 16x16x4) -> fp32
-// conversion -> triangular inverse by recursive doubling on the fp32 MFMA GEMM
-// -> reversed write of U.
+// diagonal -> one launch per 64-column block (blocked right-looking Cholesky
+// with look-ahead, the triangular inverse fused into the same sweep) ->
+// reversed write of U.
 #include "gptq_internal.h"
 
 namespace gptq {
@@ -27,6 +26,7 @@ namespace {
 
 constexpr int kNB = 64;
 constexpr int kThreads = 256;
+constexpr int kP = kNB + 1;  // LDS pitch (elements) of 64x64 tiles
 
 // Output layout of v_mfma_f64_16x16x4f64: lane l, register r holds
 // D[l / 16 + 4 r][l % 16] (checked on gfx950 against a host product).
@@ -72,111 +72,41 @@ __global__ __launch_bounds__(kThreads) void rev_copy_kernel(const float* __restr
   }
 }
 
-// Factor the diagonal block A[k0:k0+nbe, k0:k0+nbe] = L L^T in LDS, write L back
-// and L^-1 (lower, zeros above) to Dinv.  The first non-positive pivot sets
-// info to (its natural column index) + 1 if info is still 0.
-__global__ __launch_bounds__(kThreads) void potrf_diag_kernel(double* __restrict__ A, int64_t d,
-                                                              int64_t k0, int nbe,
-                                                              double* __restrict__ Dinv,
-                                                              int32_t* info) {
-  __shared__ double L[kNB][kNB + 1];
-  __shared__ double X[kNB][kNB + 1];
-  __shared__ int fail;
-  const int t = threadIdx.x;
-  for (int idx = t; idx < kNB * kNB; idx += kThreads) {
-    const int r = idx / kNB, c = idx % kNB;
-    double v;
-    if (r < nbe && c < nbe) v = (c <= r) ? A[(k0 + r) * d + k0 + c] : 0.0;
-    else v = (r == c) ? 1.0 : 0.0;  // identity padding of a ragged last block
-    L[r][c] = v;
-    X[r][c] = (r == c) ? 1.0 : 0.0;
-  }
-  if (t == 0) fail = -1;
-  __syncthreads();
-  for (int j = 0; j < kNB; ++j) {
-    if (t == 0) {
-      const double p = L[j][j];
-      if (!(p > 0.0) && fail < 0) fail = j;
-      L[j][j] = sqrt(p);
-    }
-    __syncthreads();
-    const double ljj = L[j][j];
-    for (int i = j + 1 + t; i < kNB; i += kThreads) L[i][j] /= ljj;
-    __syncthreads();
-    for (int i = j + 1 + (t >> 4); i < kNB; i += 16) {
-      const double lij = L[i][j];
-      for (int c = j + 1 + (t & 15); c <= i; c += 16) L[i][c] -= lij * L[c][j];
-    }
-    __syncthreads();
-  }
-  // X = L^-1 by row elimination: X[j] /= L[j][j]; X[i] -= L[i][j] X[j] for i > j
-  for (int j = 0; j < kNB; ++j) {
-    const double rl = 1.0 / L[j][j];
-    for (int c = t; c <= j; c += kThreads) X[j][c] *= rl;
-    __syncthreads();
-    for (int i = j + 1 + (t >> 4); i < kNB; i += 16) {
-      const double lij = L[i][j];
-      for (int c = (t & 15); c <= j; c += 16) X[i][c] -= lij * X[j][c];
-    }
-    __syncthreads();
-  }
-  for (int idx = t; idx < kNB * kNB; idx += kThreads) {
-    const int r = idx / kNB, c = idx % kNB;
-    if (r < nbe && c <= r) A[(k0 + r) * d + k0 + c] = L[r][c];
-    Dinv[idx] = (c <= r) ? X[r][c] : 0.0;
-  }
-  if (t == 0 && fail >= 0 && *info == 0) *info = (int32_t)(d - (k0 + fail));
-}
+// ---------------------------------------------------------------------------
+// One step of the blocked Cholesky (64-column blocks), with look-ahead and the
+// triangular inverse fused in.  Launch k (k = -1 .. nblk-1) runs four kinds of
+// independent work-groups; every input a work-group reads was finished by an
+// earlier launch, so no work-group ever waits on another:
+//   P  (rows r = k+1 .. nblk-1): apply step k to column block c = k+1 (tile
+//      (r, c) and the diagonal tile (c, c)), factor the diagonal tile in LDS
+//      (each P work-group redundantly), and solve its own tile:
+//      L[r][c] = T Lcc^-T.  The r == c work-group writes Lcc and Lcc^-1.
+//   F  (row k, tiles j = 0 .. k): finish block row k of Linv = L^-1:
+//      Linv[k][k] = Lkk^-1, Linv[k][j] = -Lkk^-1 (S[k][j] + L[k][k-1] Linv[k-1][j]).
+//   UC (tiles (i, j), i >= j >= k+2): A[i][j] -= L[i][k] L[j][k]^T      (fp64 MFMA)
+//   UI (tiles (i, j), i >= k+1, j <= k-1): S[i][j] += L[i][k-1] Linv[k-1][j]
+//      (fp32 MFMA; S accumulates in the Linv buffer, first touch writes).
+// ---------------------------------------------------------------------------
+struct StepArgs {
+  double* A;
+  double* Dinv;
+  float* Linv;
+  int32_t* info;
+  int d, nblk, k;
+  int np, nf, nuc, nui;
+};
 
-// fp64 64x64 tile product on MFMA: C = beta C + alpha * sum_k Am[m][k] Bn[n][k]
-// with K = 64.  mode 0: panel solve, tile row tr of rows below the diagonal
-// block: C = A21 (in place) * Dinv^T.  mode 1: trailing update of lower tile
-// (ti >= tj) of the trailing matrix: C -= L21[ti] L21[tj]^T.
-__global__ __launch_bounds__(kThreads) void chol_tile_kernel(double* __restrict__ A, int64_t d,
-                                                             int64_t k0, int mode,
-                                                             const double* __restrict__ Dinv) {
-  __shared__ double SA[kNB][kNB + 1];
-  __shared__ double SB[kNB][kNB + 1];
-  const int t = threadIdx.x, lane = t & 63, w = t >> 6;
-  const int wm = w & 1, wn = w >> 1;
-  const int64_t base = k0 + kNB;  // first row/col of the trailing matrix
-  int64_t R0, C0;
-  if (mode == 0) {
-    R0 = base + (int64_t)blockIdx.x * kNB;
-    C0 = k0;
-  } else {
-    const int64_t tt = blockIdx.x;
-    int i = (int)((sqrt(8.0 * (double)tt + 1.0) - 1.0) * 0.5);
-    while ((int64_t)(i + 1) * (i + 2) / 2 <= tt) ++i;
-    while ((int64_t)i * (i + 1) / 2 > tt) --i;
-    const int j = (int)(tt - (int64_t)i * (i + 1) / 2);
-    R0 = base + (int64_t)i * kNB;
-    C0 = base + (int64_t)j * kNB;
-  }
-  for (int idx = t; idx < kNB * kNB; idx += kThreads) {
-    const int r = idx / kNB, c = idx % kNB;
-    if (mode == 0) {
-      SA[r][c] = (R0 + r < d) ? A[(R0 + r) * d + k0 + c] : 0.0;
-      SB[r][c] = Dinv[idx];
-    } else {
-      SA[r][c] = (R0 + r < d) ? A[(R0 + r) * d + k0 + c] : 0.0;
-      SB[r][c] = (C0 + r < d) ? A[(C0 + r) * d + k0 + c] : 0.0;
-    }
-  }
-  __syncthreads();
-  f64x4 acc[2][2];
-#pragma unroll
-  for (int a = 0; a < 2; ++a)
-#pragma unroll
-    for (int b = 0; b < 2; ++b) acc[a][b] = f64x4{0.0, 0.0, 0.0, 0.0};
+// C[m][n] (this wave's 32x32 quadrant) += sum_k SA[m][k] SB[n][k], fp64 MFMA
+__device__ __forceinline__ void mma_nt_f64(const double* SA, const double* SB, f64x4 (&acc)[2][2],
+                                           int lane, int wm, int wn) {
 #pragma unroll 4
   for (int k4 = 0; k4 < kNB / 4; ++k4) {
     const int k = 4 * k4 + (lane >> 4);
     double a[2], b[2];
 #pragma unroll
     for (int f = 0; f < 2; ++f) {
-      a[f] = SA[wm * 32 + f * 16 + (lane & 15)][k];
-      b[f] = SB[wn * 32 + f * 16 + (lane & 15)][k];
+      a[f] = SA[(wm * 32 + f * 16 + (lane & 15)) * kP + k];
+      b[f] = SB[(wn * 32 + f * 16 + (lane & 15)) * kP + k];
     }
 #pragma unroll
     for (int fm = 0; fm < 2; ++fm)
@@ -184,39 +114,432 @@ __global__ __launch_bounds__(kThreads) void chol_tile_kernel(double* __restrict_
       for (int fn = 0; fn < 2; ++fn)
         acc[fm][fn] = __builtin_amdgcn_mfma_f64_16x16x4f64(a[fm], b[fn], acc[fm][fn], 0, 0, 0);
   }
+}
+
+// C[m][n] (this wave's 32x32 quadrant) += sum_k SA[m][k] SB[k][n], fp32 MFMA
+__device__ __forceinline__ void mma_nn_f32(const float* SA, const float* SB, f32x16& acc, int lane,
+                                           int wm, int wn) {
+#pragma unroll 8
+  for (int kk = 0; kk < kNB / 2; ++kk) {
+    const int k = 2 * kk + (lane >> 5);
+    const float a = SA[(wm * 32 + (lane & 31)) * kP + k];
+    const float b = SB[k * kP + wn * 32 + (lane & 31)];
+    acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, acc, 0, 0, 0);
+  }
+}
+
+// tile coordinates held by acc[fm][fn][r] of mma_nt_f64 / acc[r] of mma_nn_f32
+__device__ __forceinline__ int nt_row(int lane, int wm, int fm, int r) {
+  return wm * 32 + fm * 16 + f64_row(lane, r);
+}
+__device__ __forceinline__ int nt_col(int lane, int wn, int fn) { return wn * 32 + fn * 16 + (lane & 15); }
+__device__ __forceinline__ int nn_row(int lane, int wm, int r) {
+  return wm * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+}
+__device__ __forceinline__ int nn_col(int lane, int wn) { return wn * 32 + (lane & 31); }
+
+__device__ __forceinline__ void zero_acc(f64x4 (&acc)[2][2]) {
+#pragma unroll
+  for (int x = 0; x < 2; ++x)
+#pragma unroll
+    for (int y = 0; y < 2; ++y) acc[x][y] = f64x4{0.0, 0.0, 0.0, 0.0};
+}
+
+// load a 64x64 fp64 tile (rows R0.., cols C0..) into LDS [row][col], zeros outside d.
+// All global loads are issued before any LDS store (one memory round trip).
+__device__ __forceinline__ void load_tile_f64(double* S, const double* __restrict__ A, int64_t d,
+                                              int64_t R0, int64_t C0, int t) {
+  double v[16];
+#pragma unroll
+  for (int u = 0; u < 16; ++u) {
+    const int idx = t + u * kThreads;
+    const int r = idx >> 6, c = idx & 63;
+    v[u] = (R0 + r < d && C0 + c < d) ? A[(R0 + r) * d + C0 + c] : 0.0;
+  }
+#pragma unroll
+  for (int u = 0; u < 16; ++u) {
+    const int idx = t + u * kThreads;
+    S[(idx >> 6) * kP + (idx & 63)] = v[u];
+  }
+}
+
+// same for an fp32 tile of Linv and an fp64 tile of L converted to fp32
+__device__ __forceinline__ void load_tile_f32(float* S, const float* __restrict__ A, int64_t d,
+                                              int64_t R0, int64_t C0, int t) {
+  float v[16];
+#pragma unroll
+  for (int u = 0; u < 16; ++u) {
+    const int idx = t + u * kThreads;
+    const int r = idx >> 6, c = idx & 63;
+    v[u] = (R0 + r < d && C0 + c < d) ? A[(R0 + r) * d + C0 + c] : 0.f;
+  }
+#pragma unroll
+  for (int u = 0; u < 16; ++u) {
+    const int idx = t + u * kThreads;
+    S[(idx >> 6) * kP + (idx & 63)] = v[u];
+  }
+}
+__device__ __forceinline__ void load_tile_f64_as_f32(float* S, const double* __restrict__ A,
+                                                     int64_t d, int64_t R0, int64_t C0, int t) {
+  double v[16];
+#pragma unroll
+  for (int u = 0; u < 16; ++u) {
+    const int idx = t + u * kThreads;
+    const int r = idx >> 6, c = idx & 63;
+    v[u] = (R0 + r < d && C0 + c < d) ? A[(R0 + r) * d + C0 + c] : 0.0;
+  }
+#pragma unroll
+  for (int u = 0; u < 16; ++u) {
+    const int idx = t + u * kThreads;
+    S[(idx >> 6) * kP + (idx & 63)] = (float)v[u];
+  }
+}
+
+__device__ __forceinline__ double readlane_f64(double v, int lane) {
+  const uint64_t u = __builtin_bit_cast(uint64_t, v);
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)u, lane);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(u >> 32), lane);
+  return __builtin_bit_cast(double, ((uint64_t)hi << 32) | lo);
+}
+
+constexpr int kMP = 9;  // pitch of the panel-multiplier buffer
+
+// rank-8 update of a 16x16 tile of C (LDS, pitch kP): C[R+m][Cc+n] -= sum_k Ak(m, k) Bk(k, n)
+// with Ak(m, k) = Mp[(R+m)*kMP + k] and Bk(k, n) = B[(k)*ldb0 + ...] supplied by the caller as
+// values; lower-only restricts the store to col <= row.
+template <bool LOWER_ONLY, typename BV>
+__device__ __forceinline__ void rank8_tile(double* Cm, const double* Mp, int R, int Cc, int rows,
+                                           int cols, int lane, BV bval) {
+  f64x4 acc;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int row = R + f64_row(lane, r), col = Cc + (lane & 15);
+    acc[r] = (row < rows && col < cols) ? Cm[row * kP + col] : 0.0;
+  }
+#pragma unroll
+  for (int k4 = 0; k4 < 2; ++k4) {
+    const int k = 4 * k4 + (lane >> 4);
+    const int ar = R + (lane & 15);
+    const double av = (ar < rows) ? -Mp[ar * kMP + k] : 0.0;
+    const double bv = bval(k, Cc + (lane & 15));
+    acc = __builtin_amdgcn_mfma_f64_16x16x4f64(av, bv, acc, 0, 0, 0);
+  }
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int row = R + f64_row(lane, r), col = Cc + (lane & 15);
+    if (row < rows && col < cols && (!LOWER_ONLY || col <= row)) Cm[row * kP + col] = acc[r];
+  }
+}
+
+// Blocked LDL^T of the symmetric 64x64 matrix Dm (lower part used) with the
+// inverse X = M^-1 of its unit-lower factor M (M[i][j] = a_ij / d_j) built
+// alongside: X starts as the identity and receives the same row eliminations.
+// Per 8-column panel: wave 0 factors the panel with one row per lane in
+// registers (pivot values reach all lanes by readlane, no barrier) and
+// finishes X's 8 panel rows (one column per lane); then all four waves apply
+// the rank-8 updates to the trailing lower part of Dm and to X's rows below
+// the panel on fp64 MFMA.
+// On exit Dm[i][j] (i > j) holds the pivot-time column values a_ij, dv[j] =
+// d_j, and X[i][c] (c <= i) = M^-1[i][c].
+__device__ void blocked_ldl_inverse(double* Dm, double* X, double* Mp, double* dv, int t) {
+  const int lane = t & 63, w = t >> 6;
+  for (int idx = t; idx < kNB * kNB; idx += kThreads)
+    X[(idx >> 6) * kP + (idx & 63)] = ((idx >> 6) == (idx & 63)) ? 1.0 : 0.0;
+  __syncthreads();
+  for (int P = 0; P < kNB / 8; ++P) {
+    const int j0 = 8 * P;
+    if (w == 0) {
+      const int i = lane;
+      double v[8], mrow[8];
+#pragma unroll
+      for (int jj = 0; jj < 8; ++jj) v[jj] = (i >= j0) ? Dm[i * kP + j0 + jj] : 0.0;
+#pragma unroll
+      for (int jj = 0; jj < 8; ++jj) {
+        const double dj = readlane_f64(v[jj], j0 + jj);
+        const double rd = 1.0 / dj;
+        const double mi = (i > j0 + jj) ? v[jj] * rd : 0.0;
+        mrow[jj] = mi;
+#pragma unroll
+        for (int j2 = jj + 1; j2 < 8; ++j2) v[j2] -= mi * readlane_f64(v[jj], j0 + j2);
+        if (lane == 0) dv[j0 + jj] = dj;
+      }
+      if (i >= j0) {
+#pragma unroll
+        for (int jj = 0; jj < 8; ++jj) Dm[i * kP + j0 + jj] = v[jj];
+      }
+#pragma unroll
+      for (int jj = 0; jj < 8; ++jj) Mp[i * kMP + jj] = mrow[jj];
+      // X rows j0..j0+7 (column c = lane): x_jj -= sum_{jj' < jj} m[j0+jj][j0+jj'] x_jj'
+      double x[8];
+#pragma unroll
+      for (int jj = 0; jj < 8; ++jj) x[jj] = X[(j0 + jj) * kP + lane];
+#pragma unroll
+      for (int jj = 1; jj < 8; ++jj) {
+#pragma unroll
+        for (int q = 0; q < jj; ++q) x[jj] -= readlane_f64(mrow[q], j0 + jj) * x[q];
+      }
+#pragma unroll
+      for (int jj = 0; jj < 8; ++jj) X[(j0 + jj) * kP + lane] = x[jj];
+    }
+    __syncthreads();
+    const int T0 = j0 + 8;
+    if (T0 < kNB) {
+      // Dm[i][c] -= sum_k Mp[i][k] Dm[c][j0 + k] for T0 <= c <= i (lower 16x16 tiles)
+      const int nT = (kNB - T0 + 15) / 16;
+      const int ntl = nT * (nT + 1) / 2;
+      // X[i][c] -= sum_k Mp[i][k] X[j0 + k][c] for i >= T0, c < T0 (16x16 tiles)
+      const int nXc = (T0 + 15) / 16;
+      const int total = ntl + nT * nXc;
+      for (int tt = w; tt < total; tt += 4) {
+        if (tt < ntl) {
+          int a = 0;
+          while ((a + 1) * (a + 2) / 2 <= tt) ++a;
+          const int b = tt - a * (a + 1) / 2;
+          rank8_tile<true>(Dm, Mp, T0 + 16 * a, T0 + 16 * b, kNB, kNB, lane,
+                           [&](int k, int n) { return n < kNB ? Dm[n * kP + j0 + k] : 0.0; });
+        } else {
+          const int u = tt - ntl;
+          const int a = u / nXc, b = u % nXc;
+          rank8_tile<false>(X, Mp, T0 + 16 * a, 16 * b, kNB, T0, lane,
+                            [&](int k, int n) { return n < T0 ? X[(j0 + k) * kP + n] : 0.0; });
+        }
+      }
+    }
+    __syncthreads();
+  }
+}
+
+struct PanelSmem {
+  double S0[kNB * kP], S1[kNB * kP];
+  double Mp[kNB * kMP], dv[kNB], sq[kNB], rsq[kNB];  // Mp: 64x9 panel multipliers
+  int fail;
+};
+
+// S0: L[c1][k], then Dm (the diagonal tile; its factor), then T.
+// S1: L[r][k], then X = M^-1, then Lcc^-1.
+__device__ void task_panel(const StepArgs& a, int b, PanelSmem& sm) {
+  const int t = threadIdx.x, lane = t & 63, w = t >> 6, wm = w & 1, wn = w >> 1;
+  const int64_t d = a.d;
+  const int c1 = a.k + 1;
+  const int r = c1 + b;
+  const bool own = (r == c1);
+  const int64_t R0 = (int64_t)r * kNB, C0 = (int64_t)c1 * kNB, K0 = (int64_t)a.k * kNB;
+  f64x4 accD[2][2], accT[2][2];
+  zero_acc(accD);
+  zero_acc(accT);
+  if (a.k >= 0) {
+    load_tile_f64(sm.S0, a.A, d, C0, K0, t);            // L[c1][k]
+    if (!own) load_tile_f64(sm.S1, a.A, d, R0, K0, t);  // L[r][k]
+    __syncthreads();
+    mma_nt_f64(sm.S0, sm.S0, accD, lane, wm, wn);
+    if (!own) mma_nt_f64(sm.S1, sm.S0, accT, lane, wm, wn);
+    __syncthreads();
+  }
+  const int nbe = (int)std::min<int64_t>(kNB, d - C0);
+  // Dm := A[c1][c1] - L[c1][k] L[c1][k]^T (identity padding past d); T := A[r][c1] - ...
+  // (all global reads issued first)
+  double gD[16], gT[16];
 #pragma unroll
   for (int fm = 0; fm < 2; ++fm)
 #pragma unroll
     for (int fn = 0; fn < 2; ++fn)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int64_t row = R0 + wm * 32 + fm * 16 + f64_row(lane, r);
-        const int64_t col = C0 + wn * 32 + fn * 16 + (lane & 15);
-        if (row >= d || col >= d) continue;
-        if (mode == 0) {
-          A[row * d + col] = acc[fm][fn][r];
-        } else if (col <= row) {
-          A[row * d + col] -= acc[fm][fn][r];
-        }
+      for (int q = 0; q < 4; ++q) {
+        const int u = (fm * 2 + fn) * 4 + q;
+        const int rr = nt_row(lane, wm, fm, q), cc = nt_col(lane, wn, fn);
+        const int hi = rr > cc ? rr : cc, lo = rr > cc ? cc : rr;
+        gD[u] = (rr < nbe && cc < nbe) ? a.A[(C0 + hi) * d + C0 + lo] : 0.0;
+        gT[u] = (!own && R0 + rr < d && cc < nbe) ? a.A[(R0 + rr) * d + C0 + cc] : 0.0;
+      }
+#pragma unroll
+  for (int fm = 0; fm < 2; ++fm)
+#pragma unroll
+    for (int fn = 0; fn < 2; ++fn)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int u = (fm * 2 + fn) * 4 + q;
+        const int rr = nt_row(lane, wm, fm, q), cc = nt_col(lane, wn, fn);
+        sm.S0[rr * kP + cc] = (rr < nbe && cc < nbe) ? gD[u] - accD[fm][fn][q] : (rr == cc ? 1.0 : 0.0);
+        accT[fm][fn][q] = (!own && R0 + rr < d && cc < nbe) ? gT[u] - accT[fm][fn][q] : 0.0;
+      }
+  if (t == 0) sm.fail = kNB;
+  __syncthreads();
+  blocked_ldl_inverse(sm.S0, sm.S1, sm.Mp, sm.dv, t);
+  if (t < kNB) {
+    const double dj = sm.dv[t];
+    if (!(dj > 0.0)) atomicMin(&sm.fail, t);
+    sm.sq[t] = sqrt(dj);
+    sm.rsq[t] = 1.0 / sm.sq[t];
+  }
+  __syncthreads();
+  // S1 := Lcc^-1 = diag(rsq) X (unit diagonal implied), zeros above
+  for (int idx = t; idx < kNB * kNB; idx += kThreads) {
+    const int i = idx >> 6, c = idx & 63;
+    sm.S1[i * kP + c] = (c < i) ? sm.S1[i * kP + c] * sm.rsq[i] : (c == i ? sm.rsq[i] : 0.0);
+  }
+  __syncthreads();
+  if (own) {
+    for (int idx = t; idx < kNB * kNB; idx += kThreads) {
+      const int i = idx >> 6, c = idx & 63;
+      a.Dinv[(int64_t)c1 * kNB * kNB + idx] = sm.S1[i * kP + c];
+      if (i < nbe && c <= i)
+        a.A[(C0 + i) * d + C0 + c] = (c < i) ? sm.S0[i * kP + c] * sm.rsq[c] : sm.sq[i];
+    }
+    if (t == 0 && sm.fail < nbe && *a.info == 0) *a.info = (int32_t)(d - (C0 + sm.fail));
+    return;
+  }
+  // L[r][c1] = T Lcc^-T
+#pragma unroll
+  for (int fm = 0; fm < 2; ++fm)
+#pragma unroll
+    for (int fn = 0; fn < 2; ++fn)
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        sm.S0[nt_row(lane, wm, fm, q) * kP + nt_col(lane, wn, fn)] = accT[fm][fn][q];
+  __syncthreads();
+  f64x4 acc[2][2];
+  zero_acc(acc);
+  mma_nt_f64(sm.S0, sm.S1, acc, lane, wm, wn);
+#pragma unroll
+  for (int fm = 0; fm < 2; ++fm)
+#pragma unroll
+    for (int fn = 0; fn < 2; ++fn)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int rr = nt_row(lane, wm, fm, q), cc = nt_col(lane, wn, fn);
+        if (R0 + rr < d && cc < nbe) a.A[(R0 + rr) * d + C0 + cc] = acc[fm][fn][q];
       }
 }
 
-// L32 := fp32(L) (lower; zeros above) and Linv := blockdiag(fp32(Dinv_k)), zeros elsewhere
-__global__ __launch_bounds__(kThreads) void cvt_kernel(const double* __restrict__ A, int64_t d,
-                                                       const double* __restrict__ Dinv,
-                                                       float* __restrict__ L32,
-                                                       float* __restrict__ Linv) {
-  const int bj = blockIdx.x, bi = blockIdx.y;
-  const int t = threadIdx.x;
-  const int c = t & 63;
-  const int64_t j = (int64_t)bj * 64 + c;
-  for (int k = 0; k < 16; ++k) {
-    const int r = (t >> 6) + 4 * k;
-    const int64_t i = (int64_t)bi * 64 + r;
-    if (i >= d || j >= d) continue;
-    L32[i * d + j] = (j <= i) ? (float)A[i * d + j] : 0.f;
-    Linv[i * d + j] = (bi == bj) ? (float)Dinv[(int64_t)bi * kNB * kNB + r * kNB + c] : 0.f;
+struct TileSmem32 {
+  float F0[kNB * kP], F1[kNB * kP];
+};
+
+__device__ void task_finish_inverse_row(const StepArgs& a, int j, TileSmem32& sm) {
+  const int t = threadIdx.x, lane = t & 63, w = t >> 6, wm = w & 1, wn = w >> 1;
+  const int64_t d = a.d;
+  const int k = a.k;
+  const int64_t R0 = (int64_t)k * kNB, J0 = (int64_t)j * kNB;
+  const double* Dk = a.Dinv + (int64_t)k * kNB * kNB;
+  if (j == k) {
+    for (int idx = t; idx < kNB * kNB; idx += kThreads) {
+      const int i = idx >> 6, c = idx & 63;
+      if (R0 + i < d && R0 + c < d) a.Linv[(R0 + i) * d + R0 + c] = (float)Dk[idx];
+    }
+    return;
   }
+  // T = S[k][j] + L[k][k-1] Linv[k-1][j]
+  const int64_t P0 = (int64_t)(k - 1) * kNB;
+  f32x16 acc;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    const int64_t rr = R0 + nn_row(lane, wm, r);
+    acc[r] = (j <= k - 2 && rr < d) ? a.Linv[rr * d + J0 + nn_col(lane, wn)] : 0.f;
+  }
+  load_tile_f64_as_f32(sm.F0, a.A, d, R0, P0, t);  // L[k][k-1]
+  load_tile_f32(sm.F1, a.Linv, d, P0, J0, t);      // Linv[k-1][j]
+  __syncthreads();
+  mma_nn_f32(sm.F0, sm.F1, acc, lane, wm, wn);
+  __syncthreads();
+#pragma unroll
+  for (int r = 0; r < 16; ++r) sm.F1[nn_row(lane, wm, r) * kP + nn_col(lane, wn)] = acc[r];
+  for (int idx = t; idx < kNB * kNB; idx += kThreads)
+    sm.F0[(idx >> 6) * kP + (idx & 63)] = (float)Dk[idx];
+  __syncthreads();
+  f32x16 out;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) out[r] = 0.f;
+  mma_nn_f32(sm.F0, sm.F1, out, lane, wm, wn);
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    const int64_t rr = R0 + nn_row(lane, wm, r);
+    if (rr < d) a.Linv[rr * d + J0 + nn_col(lane, wn)] = -out[r];
+  }
+}
+
+__device__ void task_update_chol(const StepArgs& a, int b, PanelSmem& sm) {
+  const int t = threadIdx.x, lane = t & 63, w = t >> 6, wm = w & 1, wn = w >> 1;
+  const int64_t d = a.d;
+  int i = (int)((sqrt(8.0 * (double)b + 1.0) - 1.0) * 0.5);
+  while ((i + 1) * (i + 2) / 2 <= b) ++i;
+  while (i * (i + 1) / 2 > b) --i;
+  const int j = b - i * (i + 1) / 2;
+  const int base = a.k + 2;
+  const int64_t R0 = (int64_t)(base + i) * kNB, C0 = (int64_t)(base + j) * kNB,
+                K0 = (int64_t)a.k * kNB;
+  load_tile_f64(sm.S0, a.A, d, R0, K0, t);
+  load_tile_f64(sm.S1, a.A, d, C0, K0, t);
+  __syncthreads();
+  f64x4 acc[2][2];
+  zero_acc(acc);
+  double c[16];
+#pragma unroll
+  for (int fm = 0; fm < 2; ++fm)
+#pragma unroll
+    for (int fn = 0; fn < 2; ++fn)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int64_t row = R0 + nt_row(lane, wm, fm, q), col = C0 + nt_col(lane, wn, fn);
+        c[(fm * 2 + fn) * 4 + q] = (row < d && col <= row) ? a.A[row * d + col] : 0.0;
+      }
+  mma_nt_f64(sm.S0, sm.S1, acc, lane, wm, wn);
+#pragma unroll
+  for (int fm = 0; fm < 2; ++fm)
+#pragma unroll
+    for (int fn = 0; fn < 2; ++fn)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int64_t row = R0 + nt_row(lane, wm, fm, q), col = C0 + nt_col(lane, wn, fn);
+        if (row < d && col <= row) a.A[row * d + col] = c[(fm * 2 + fn) * 4 + q] - acc[fm][fn][q];
+      }
+}
+
+__device__ void task_update_inverse(const StepArgs& a, int b, TileSmem32& sm) {
+  const int t = threadIdx.x, lane = t & 63, w = t >> 6, wm = w & 1, wn = w >> 1;
+  const int64_t d = a.d;
+  const int k = a.k;
+  const int i = k + 1 + b / k, j = b % k;
+  const int64_t R0 = (int64_t)i * kNB, J0 = (int64_t)j * kNB, P0 = (int64_t)(k - 1) * kNB;
+  f32x16 acc;
+  const bool first = (j == k - 1);
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    const int64_t rr = R0 + nn_row(lane, wm, r);
+    acc[r] = (!first && rr < d) ? a.Linv[rr * d + J0 + nn_col(lane, wn)] : 0.f;
+  }
+  load_tile_f64_as_f32(sm.F0, a.A, d, R0, P0, t);  // L[i][k-1]
+  load_tile_f32(sm.F1, a.Linv, d, P0, J0, t);      // Linv[k-1][j]
+  __syncthreads();
+  mma_nn_f32(sm.F0, sm.F1, acc, lane, wm, wn);
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    const int64_t rr = R0 + nn_row(lane, wm, r);
+    if (rr < d) a.Linv[rr * d + J0 + nn_col(lane, wn)] = acc[r];
+  }
+}
+
+__global__ __launch_bounds__(kThreads) void chol_step_kernel(StepArgs a) {
+  __shared__ union Smem {
+    PanelSmem p;
+    TileSmem32 f;
+  } sm;
+  int b = blockIdx.x;
+  if (b < a.np) {
+    task_panel(a, b, sm.p);
+    return;
+  }
+  b -= a.np;
+  if (b < a.nf) {
+    task_finish_inverse_row(a, b, sm.f);
+    return;
+  }
+  b -= a.nf;
+  if (b < a.nuc) {
+    task_update_chol(a, b, sm.p);
+    return;
+  }
+  b -= a.nuc;
+  if (b < a.nui) task_update_inverse(a, b, sm.f);
 }
 
 // U[i][j] = Linv[d-1-i][d-1-j] for j >= i, else 0
@@ -244,8 +567,8 @@ FactorPlan factor_plan(int64_t d) {
   off = align_up(off + (size_t)d * d * sizeof(double), 256);
   p.off_dinv = off;
   off = align_up(off + (size_t)p.nblk * kNB * kNB * sizeof(double), 256);
-  p.off_tmp = off;  // Linv (d*d fp32) then the recursive-doubling temporary (d*d/2 fp32)
-  off = align_up(off + (size_t)d * d * sizeof(float) + (size_t)d * ((d + 1) / 2) * sizeof(float), 256);
+  p.off_tmp = off;  // Linv = L^-1 (d*d fp32; its lower tiles first hold partial sums)
+  off = align_up(off + (size_t)d * d * sizeof(float), 256);
   p.off_lam = off;
   off = align_up(off + 64, 256);
   p.ws_bytes = off;
@@ -259,56 +582,30 @@ hipError_t factor_launch(const FactorPlan& p, const float* H, float percdamp, fl
   double* A = (double*)(base + p.off_a64);
   double* Dinv = (double*)(base + p.off_dinv);
   float* Linv = (float*)(base + p.off_tmp);
-  float* Tmp = Linv + (size_t)d * d;
   double* lam = (double*)(base + p.off_lam);
   hipError_t e;
   hipLaunchKernelGGL(damp_kernel, dim3(1), dim3(kThreads), 0, s, H, d, percdamp, lam, lambda_out, info);
   const unsigned nt = (unsigned)p.nblk;
   hipLaunchKernelGGL(rev_copy_kernel, dim3(nt, nt), dim3(kThreads), 0, s, H, d, lam, A);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  for (int64_t k = 0; k < p.nblk; ++k) {
-    const int64_t k0 = k * kNB;
-    const int nbe = (int)std::min<int64_t>(kNB, d - k0);
-    hipLaunchKernelGGL(potrf_diag_kernel, dim3(1), dim3(kThreads), 0, s, A, d, k0, nbe,
-                       Dinv + k * kNB * kNB, info);
-    const int64_t rest = p.nblk - k - 1;
-    if (rest > 0) {
-      hipLaunchKernelGGL(chol_tile_kernel, dim3((unsigned)rest), dim3(kThreads), 0, s, A, d, k0, 0,
-                         (const double*)(Dinv + k * kNB * kNB));
-      hipLaunchKernelGGL(chol_tile_kernel, dim3((unsigned)(rest * (rest + 1) / 2)), dim3(kThreads), 0,
-                         s, A, d, k0, 1, (const double*)nullptr);
-    }
+  const int nblk = (int)p.nblk;
+  for (int k = -1; k < nblk; ++k) {
+    StepArgs a{};
+    a.A = A;
+    a.Dinv = Dinv;
+    a.Linv = Linv;
+    a.info = info;
+    a.d = (int)d;
+    a.nblk = nblk;
+    a.k = k;
+    a.np = (k + 1 < nblk) ? nblk - (k + 1) : 0;
+    a.nf = (k >= 0) ? k + 1 : 0;
+    const int m = nblk - k - 2;
+    a.nuc = (k >= 0 && m > 0) ? m * (m + 1) / 2 : 0;
+    a.nui = (k >= 1) ? (nblk - k - 1) * k : 0;
+    const int total = a.np + a.nf + a.nuc + a.nui;
+    if (total > 0) hipLaunchKernelGGL(chol_step_kernel, dim3((unsigned)total), dim3(kThreads), 0, s, a);
     if ((e = hipGetLastError()) != hipSuccess) return e;
-  }
-  float* L32 = U;  // U doubles as fp32 L storage until the final write
-  hipLaunchKernelGGL(cvt_kernel, dim3(nt, nt), dim3(kThreads), 0, s, A, d, Dinv, L32, Linv);
-  if ((e = hipGetLastError()) != hipSuccess) return e;
-  // recursive doubling: for adjacent diagonal blocks A (first) and C (second) of
-  // size S, Linv[C, A] = -Linv[C,C] * (L[C, A] * Linv[A, A])
-  for (int64_t S = kNB; S < d; S *= 2) {
-    const int64_t nfull = d / (2 * S);
-    const int64_t rag0 = nfull * 2 * S;        // start of a trailing partial pair
-    const int64_t rag2 = d - (rag0 + S);       // its second-block size
-    for (int part = 0; part < 2; ++part) {
-      int64_t M, npairs, off0;
-      if (part == 0) { M = S; npairs = nfull; off0 = 0; }
-      else { M = rag2; npairs = (rag2 > 0) ? 1 : 0; off0 = rag0; }
-      if (npairs == 0 || M <= 0) continue;
-      GemmBatch g1{};
-      g1.A = L32 + (off0 + S) * d + off0; g1.lda = d; g1.sA = 2 * S * d + 2 * S;
-      g1.B = Linv + off0 * d + off0;      g1.ldb = d; g1.sB = 2 * S * d + 2 * S;
-      g1.C = Tmp;                         g1.ldc = S; g1.sC = M * S;
-      g1.M = (int)M; g1.N = (int)S; g1.K = (int)S; g1.batch = (int)npairs;
-      g1.alpha = 1.f; g1.beta_zero = 1; g1.kmode = 1;
-      if ((e = gemm_f32_launch(g1, s)) != hipSuccess) return e;
-      GemmBatch g2{};
-      g2.A = Linv + (off0 + S) * d + (off0 + S); g2.lda = d; g2.sA = 2 * S * d + 2 * S;
-      g2.B = Tmp;                                 g2.ldb = S; g2.sB = M * S;
-      g2.C = Linv + (off0 + S) * d + off0;        g2.ldc = d; g2.sC = 2 * S * d + 2 * S;
-      g2.M = (int)M; g2.N = (int)S; g2.K = (int)M; g2.batch = (int)npairs;
-      g2.alpha = -1.f; g2.beta_zero = 1; g2.kmode = 2;
-      if ((e = gemm_f32_launch(g2, s)) != hipSuccess) return e;
-    }
   }
   hipLaunchKernelGGL(rev_out_kernel, dim3(nt, nt), dim3(kThreads), 0, s, Linv, d, U);
   return hipGetLastError();

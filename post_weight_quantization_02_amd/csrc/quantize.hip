@@ -117,44 +117,60 @@ __global__ __launch_bounds__(kThreads) void group_grid_kernel(const float* __res
 }
 
 // One block of columns [i1, i1 + width) for 16 rows per work-group.
-// group: 0 = per-row grid (read from scales/zeros), <= B = computed here at
-// group starts, > B = read (computed by group_grid_kernel at the block start).
-template <int CPL>
+// GIN: group size when groups start inside the block (a multiple of 16 that
+// divides B), else 0 (per-row grid, or groups wider than the block whose
+// parameters group_grid_kernel wrote at the block start).  FULL: width == B.
+// Both are compile-time so the fully unrolled column loop carries the group
+// code only at the group starts.
+template <int CPL, int GIN, bool FULL>
 __global__ __launch_bounds__(kThreads) void panel_kernel(
-    float* __restrict__ W, int64_t d_row, int64_t d_col, int64_t i1, int width,
-    const float* __restrict__ U, int maxq, int64_t group, int64_t ngroups,
+    float* __restrict__ W, int d_row, int d_col, int i1, int width,
+    const float* __restrict__ U, int maxq, int gwide, int ngroups,
     uint8_t* __restrict__ codes, float* __restrict__ scales, int32_t* __restrict__ zeros,
     float* __restrict__ E, double* __restrict__ part_e) {
   constexpr int B = 16 * CPL;
+  static_assert(GIN == 0 || (GIN % 16 == 0 && B % GIN == 0), "group inside block");
   __shared__ __attribute__((aligned(16))) float Us[B * B];
   __shared__ float rd[B];
   __shared__ double red[kThreads / 64];
   const int t = threadIdx.x;
-  for (int idx = t; idx < B * B; idx += kThreads) {
-    const int r = idx / B, c = idx % B;
-    Us[idx] = (r < width && c < width && c >= r) ? U[(i1 + r) * d_col + i1 + c] : 0.f;
+  const size_t ldu = (size_t)d_col;
+  // stage U's diagonal block (upper part) in LDS; all global loads are issued
+  // before the LDS stores
+  constexpr int kPer = B * B / kThreads;
+  constexpr int kBatch = kPer < 32 ? kPer : 32;
+  const float udg = (t < width) ? U[(size_t)(i1 + t) * ldu + i1 + t] : 1.f;
+#pragma unroll
+  for (int u0 = 0; u0 < kPer; u0 += kBatch) {
+    float ub[kBatch];
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) {
+      const int idx = t + (u0 + u) * kThreads;
+      const int r = idx / B, c = idx % B;
+      ub[u] = (r < width && c < width && c >= r) ? U[(size_t)(i1 + r) * ldu + i1 + c] : 0.f;
+    }
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) Us[t + (u0 + u) * kThreads] = ub[u];
   }
-  for (int r = t; r < B; r += kThreads) rd[r] = (r < width) ? 1.0f / U[(i1 + r) * d_col + i1 + r] : 0.f;
+  if (t < B) rd[t] = (t < width) ? 1.0f / udg : 0.f;
   __syncthreads();
 
   const int lane = t & 63, p = lane & 15;
-  const int64_t row = (int64_t)blockIdx.x * 16 + (t >> 6) * 4 + (lane >> 4);
+  const int row = blockIdx.x * 16 + (t >> 6) * 4 + (lane >> 4);
   const bool valid = row < d_row;
-  const int64_t rowc = valid ? row : d_row - 1;
+  const size_t rowc = (size_t)(valid ? row : d_row - 1);
   float w[CPL], cr[CPL], er[CPL];
 #pragma unroll
   for (int r = 0; r < CPL; ++r) {
     const int col = p * CPL + r;
-    w[r] = (col < width) ? W[rowc * d_col + i1 + col] : 0.f;
+    w[r] = (FULL || col < width) ? W[rowc * d_col + i1 + col] : 0.f;
     cr[r] = 0.f;
     er[r] = 0.f;
   }
   float s = 1.f, z = 0.f;
-  if (group == 0) {
-    s = scales[rowc];
-    z = (float)zeros[rowc];
-  } else if (group > B) {
-    const int64_t gi = i1 / group;
+  if (GIN == 0) {
+    // per-row grid (one column of scales) or a group wider than the block
+    const int gi = gwide ? i1 / gwide : 0;
     s = scales[rowc * ngroups + gi];
     z = (float)zeros[rowc * ngroups + gi];
   }
@@ -163,19 +179,20 @@ __global__ __launch_bounds__(kThreads) void panel_kernel(
 
   static_for<0, 16>([&](auto kc) {
     constexpr int kk = decltype(kc)::value;
-#pragma unroll
-    for (int jj = 0; jj < CPL; ++jj) {
-      const int j = kk * CPL + jj;
-      if (j < width) {
-        if (group > 0 && group <= B && (j % group) == 0) {
+    static_for<0, CPL>([&](auto jc) {
+      constexpr int jj = decltype(jc)::value;
+      constexpr int j = kk * CPL + jj;
+      if (FULL || j < width) {
+        if constexpr (GIN != 0 && j % GIN == 0) {
+          // group [j, j + GIN): lanes j/CPL .. (j+GIN)/CPL - 1 of the row hold it
+          constexpr int l0 = j / CPL, l1 = (j + GIN) / CPL;
           float mn = INFINITY, mx = -INFINITY;
+          const bool mine = (p >= l0 && p < l1);
 #pragma unroll
           for (int r = 0; r < CPL; ++r) {
-            const int col = p * CPL + r;
-            if (col >= j && col < j + group && col < width) {
-              mn = fminf(mn, w[r]);
-              mx = fmaxf(mx, w[r]);
-            }
+            const bool in = mine && (FULL || p * CPL + r < width);
+            mn = in ? fminf(mn, w[r]) : mn;
+            mx = in ? fmaxf(mx, w[r]) : mx;
           }
 #pragma unroll
           for (int o = 8; o > 0; o >>= 1) {
@@ -185,9 +202,9 @@ __global__ __launch_bounds__(kThreads) void panel_kernel(
           grid_from_minmax(mn, mx, maxq, s, z);
           rs = 1.f / s;
           if (p == 0 && valid) {
-            const int64_t gi = (i1 + j) / group;
-            scales[row * ngroups + gi] = s;
-            zeros[row * ngroups + gi] = (int32_t)z;
+            const int gi = (i1 + j) / GIN;
+            scales[rowc * ngroups + gi] = s;
+            zeros[rowc * ngroups + gi] = (int32_t)z;
           }
         }
         const float x = w[jj];
@@ -198,20 +215,30 @@ __global__ __launch_bounds__(kThreads) void panel_kernel(
           er[jj] = e;
         }
         const float eb = row_bcast<kk>(e);
-        const float* ur = &Us[j * B + p * CPL];
+        const f32x4* ur = (const f32x4*)&Us[j * B + p * CPL];
+        if constexpr (CPL >= 4) {
 #pragma unroll
-        for (int r = 0; r < CPL; ++r) w[r] = fmaf(-eb, ur[r], w[r]);
+          for (int q = 0; q < CPL / 4; ++q) {
+            const f32x4 u = ur[q];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) w[4 * q + r] = fmaf(-eb, u[r], w[4 * q + r]);
+          }
+        } else {
+          const float* u1 = &Us[j * B + p * CPL];
+#pragma unroll
+          for (int r = 0; r < CPL; ++r) w[r] = fmaf(-eb, u1[r], w[r]);
+        }
       }
-    }
+    });
   });
 
   double se = 0.0;
 #pragma unroll
   for (int r = 0; r < CPL; ++r) {
     const int col = p * CPL + r;
-    if (valid && col < width) {
-      codes[row * d_col + i1 + col] = (uint8_t)cr[r];
-      E[row * B + col] = er[r];
+    if (valid && (FULL || col < width)) {
+      codes[(size_t)row * d_col + i1 + col] = (uint8_t)cr[r];
+      E[(size_t)row * B + col] = er[r];
       se += (double)er[r] * (double)er[r];
     }
   }
@@ -221,18 +248,53 @@ __global__ __launch_bounds__(kThreads) void panel_kernel(
   if (t == 0) part_e[blockIdx.x] += (red[0] + red[1]) + (red[2] + red[3]);
 }
 
+template <int CPL, int GIN>
+hipError_t launch_panel_g(bool full, dim3 grid, hipStream_t s, float* W, int d_row, int d_col,
+                          int i1, int width, const float* U, int maxq, int gwide, int ngroups,
+                          uint8_t* codes, float* scales, int32_t* zeros, float* E, double* part_e) {
+  if (full)
+    hipLaunchKernelGGL((panel_kernel<CPL, GIN, true>), grid, dim3(kThreads), 0, s, W, d_row, d_col,
+                       i1, width, U, maxq, gwide, ngroups, codes, scales, zeros, E, part_e);
+  else
+    hipLaunchKernelGGL((panel_kernel<CPL, GIN, false>), grid, dim3(kThreads), 0, s, W, d_row, d_col,
+                       i1, width, U, maxq, gwide, ngroups, codes, scales, zeros, E, part_e);
+  return hipGetLastError();
+}
+
+template <int CPL>
+hipError_t launch_panel(int gin, bool full, dim3 grid, hipStream_t s, float* W, int d_row,
+                        int d_col, int i1, int width, const float* U, int maxq, int gwide,
+                        int ngroups, uint8_t* codes, float* scales, int32_t* zeros, float* E,
+                        double* part_e) {
+#define GPTQ_PANEL_CASE(G)                                                                  \
+  case G:                                                                                  \
+    if constexpr (G <= 16 * CPL)                                                           \
+      return launch_panel_g<CPL, G>(full, grid, s, W, d_row, d_col, i1, width, U, maxq,   \
+                                    gwide, ngroups, codes, scales, zeros, E, part_e);      \
+    return hipErrorInvalidValue;
+  switch (gin) {
+    GPTQ_PANEL_CASE(0)
+    GPTQ_PANEL_CASE(16)
+    GPTQ_PANEL_CASE(32)
+    GPTQ_PANEL_CASE(64)
+    GPTQ_PANEL_CASE(128)
+    default: return hipErrorInvalidValue;
+  }
+#undef GPTQ_PANEL_CASE
+}
+
 // sum over rows of (W0 - scale (c - zero))^2, per work-group partials
 template <typename T>
 __global__ __launch_bounds__(kThreads) void err_delta_kernel(
     const T* __restrict__ W0, int64_t ldw, int64_t d_row, int64_t d_col,
     const uint8_t* __restrict__ codes, const float* __restrict__ scales,
-    const int32_t* __restrict__ zeros, int64_t g, int64_t ngroups, double* __restrict__ part_d) {
+    const int32_t* __restrict__ zeros, int g, int64_t ngroups, double* __restrict__ part_d) {
   __shared__ double red[kThreads];
   const int t = threadIdx.x;
   double acc = 0.0;
   for (int64_t row = blockIdx.x; row < d_row; row += gridDim.x) {
     for (int64_t c = t; c < d_col; c += kThreads) {
-      const int64_t gi = c / g;
+      const int gi = (int)c / g;
       const float s = scales[row * ngroups + gi];
       const float z = (float)zeros[row * ngroups + gi];
       const float wh = s * ((float)codes[row * d_col + c] - z);
@@ -324,26 +386,22 @@ hipError_t quant_launch(const QuantPlan& p, const void* W0, int w_dtype, int64_t
       hipLaunchKernelGGL(group_grid_kernel, dim3((unsigned)cdiv(d_row, 4)), dim3(kThreads), 0, s, W,
                          d_row, d_col, i1, gw, i1 / group, ngroups, maxq, scales, zeros);
     }
-    const dim3 pg((unsigned)p.panel_wgs), pb(kThreads);
+    const dim3 pg((unsigned)p.panel_wgs);
+    const bool full = (width == B);
+    const int gin = (group > 0 && group <= B) ? (int)group : 0;
+    const int gwide = (group > B) ? (int)group : 0;
+    const int ng = (int)ngroups;
     switch (B) {
-      case 16:
-        hipLaunchKernelGGL(panel_kernel<1>, pg, pb, 0, s, W, d_row, d_col, i1, width, U, maxq, group,
-                           ngroups, codes, scales, zeros, E, part_e);
-        break;
-      case 32:
-        hipLaunchKernelGGL(panel_kernel<2>, pg, pb, 0, s, W, d_row, d_col, i1, width, U, maxq, group,
-                           ngroups, codes, scales, zeros, E, part_e);
-        break;
-      case 64:
-        hipLaunchKernelGGL(panel_kernel<4>, pg, pb, 0, s, W, d_row, d_col, i1, width, U, maxq, group,
-                           ngroups, codes, scales, zeros, E, part_e);
-        break;
-      default:
-        hipLaunchKernelGGL(panel_kernel<8>, pg, pb, 0, s, W, d_row, d_col, i1, width, U, maxq, group,
-                           ngroups, codes, scales, zeros, E, part_e);
-        break;
+      case 16: e = launch_panel<1>(gin, full, pg, s, W, (int)d_row, (int)d_col, (int)i1, width, U,
+                                   maxq, gwide, ng, codes, scales, zeros, E, part_e); break;
+      case 32: e = launch_panel<2>(gin, full, pg, s, W, (int)d_row, (int)d_col, (int)i1, width, U,
+                                   maxq, gwide, ng, codes, scales, zeros, E, part_e); break;
+      case 64: e = launch_panel<4>(gin, full, pg, s, W, (int)d_row, (int)d_col, (int)i1, width, U,
+                                   maxq, gwide, ng, codes, scales, zeros, E, part_e); break;
+      default: e = launch_panel<8>(gin, full, pg, s, W, (int)d_row, (int)d_col, (int)i1, width, U,
+                                   maxq, gwide, ng, codes, scales, zeros, E, part_e); break;
     }
-    if ((e = hipGetLastError()) != hipSuccess) return e;
+    if (e != hipSuccess) return e;
     const int64_t i2 = i1 + width;
     if (i2 < d_col) {
       GemmBatch g{};

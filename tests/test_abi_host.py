@@ -106,6 +106,7 @@ def test_quantize_validation():
     for b in (0, 8, 24, 256):
         assert call(block=b) == _status("GPTQ_ERR_BAD_BLOCK")
     assert call(group=24) == _status("GPTQ_ERR_BAD_GROUP")
+    assert call(group=8) == _status("GPTQ_ERR_BAD_GROUP")
     assert call(group=-1) == _status("GPTQ_ERR_BAD_GROUP")
     assert call(ws_bytes=need - 1) == _status("GPTQ_ERR_WORKSPACE")
     assert G.gptq_quantize_layer_workspace_size(4, 32, 24) == 0

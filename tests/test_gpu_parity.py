@@ -112,6 +112,13 @@ def test_factor_parity(name, make):
     assert _factor_case(make()) <= 1e-4
 
 
+def test_factor_parity_attn4096_size():
+    """The 4096-column factor of the bench workload's recipe (first 16384 calibration rows)."""
+    spec = wl.workload_layers(3)[0]
+    Ho = O.hessian([wl.make_x_chunk(spec, 0)])
+    assert _factor_case(Ho) <= 1e-4
+
+
 def test_factor_reports_not_positive_definite():
     for H in (np.zeros((96, 96), np.float32), -np.eye(70, dtype=np.float32)):
         pd = 0.0 if not H.any() else 0.01
