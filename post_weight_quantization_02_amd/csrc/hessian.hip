@@ -23,6 +23,8 @@
 // [row][feature] LDS layout needs no transpose; 128x128 tiles.
 #include "gptq_internal.h"
 
+#include <numeric>
+
 namespace gptq {
 namespace {
 
@@ -37,17 +39,21 @@ __device__ __forceinline__ void tile_of(int64_t t, int& ti, int& tj) {
   ti = (int)(t - (int64_t)j * (j + 1) / 2);
 }
 
-// work-group -> (tile, split).  With a multiple of 8 splits, XCD x (work-groups
-// are dispatched round-robin over the 8 XCDs) owns splits x, x + 8, ...: each
-// calibration row is read from HBM by one XCD and shared in its L2 by all the
-// tiles that XCD runs.
+// work-group -> (tile, split).  Splits are visited in order by the whole GPU
+// (split-major), so at any time the running work-groups read the same few
+// split row ranges and those stay in the Infinity Cache while every tile
+// passes over them.  When the tile count is a multiple of 8, XCD x (work-groups
+// are dispatched round-robin over the 8 XCDs) takes the contiguous tile range
+// [x * ntiles / 8, (x + 1) * ntiles / 8) of each split, so tiles that share
+// column blocks share that XCD's L2.
 __device__ __forceinline__ void wg_map(int64_t ntiles, int64_t nsplit, int64_t& tile,
                                        int64_t& split) {
   const int64_t bid = blockIdx.x;
-  if ((nsplit & 7) == 0) {
-    const int64_t loc = bid >> 3;
-    split = (bid & 7) + 8 * (loc / ntiles);
-    tile = loc % ntiles;
+  if ((ntiles & 7) == 0) {
+    const int64_t per = ntiles >> 3;
+    const int64_t j = bid >> 3;
+    split = j / per;
+    tile = (bid & 7) * per + j % per;
   } else {
     split = bid / ntiles;
     tile = bid % ntiles;
@@ -61,11 +67,25 @@ __device__ __forceinline__ int sw16(int m, int c) {
   return m * kKS16 + ((c ^ ((m ^ (m >> 3)) & 7)) << 3);
 }
 
+// Software pipeline per 64-row stage s (LDS double-buffered, one barrier):
+//   k-substep 0..3 each issue 16 MFMAs (this wave's 4x4 32x32 fragments) with
+//   the next substep's fragments read from LDS underneath;
+//   substep 1 also transposes the registers holding stage s+1 into LDS buffer
+//   (s+1)&1, substep 2 issues the global loads of stage s+2 into those
+//   registers; the barrier sits between substeps 2 and 3 so that substep 3 can
+//   already read stage s+1's first fragments.  sched_group_barrier pins the
+//   interleave (one MFMA, then a few memory or transpose instructions).
+// Full stages load unmasked from a uniform per-stage base with 32-bit offsets;
+// only a split's tail stage (or a partial last column tile) takes the masked
+// path.
+#define GPTQ_SGB(mask, n) __builtin_amdgcn_sched_group_barrier(mask, n, 0)
+constexpr int kSgMFMA = 0x008, kSgVALU = 0x002, kSgVMEMR = 0x020, kSgDSR = 0x100, kSgDSW = 0x200;
+
 template <bool VEC>
 __global__ __launch_bounds__(kThreads) void syrk_f16_kernel(
     const _Float16* __restrict__ X, int64_t ldx, int64_t n, int d, int64_t ntiles,
     int64_t nsplit, int64_t rps, float* __restrict__ part) {
-  __shared__ __attribute__((aligned(16))) _Float16 lds[2][kBT16 * kKS16];
+  __shared__ __attribute__((aligned(16))) _Float16 lds[2][2][kBT16 * kKS16];
   int64_t tile, split;
   wg_map(ntiles, nsplit, tile, split);
   int ti, tj;
@@ -74,9 +94,15 @@ __global__ __launch_bounds__(kThreads) void syrk_f16_kernel(
   const int I0 = ti * kBT16, J0 = tj * kBT16;
   const int64_t r0 = split * rps;
   const int64_t r1 = min(n, r0 + rps);
+  const int nrows = (int)(r1 - r0);
   const int t = threadIdx.x, lane = t & 63, w = t >> 6;
   const int wm = w & 1, wn = w >> 1;
   const int mg = t & 31, kg = t >> 5;
+  const bool full_cols = VEC && (I0 + kBT16 <= d) && (J0 + kBT16 <= d);
+  const _Float16* __restrict__ Xs = X + r0 * ldx;   // this split's first row
+  const uint32_t offA = (uint32_t)(kg * 8 * ldx + I0 + mg * 8);
+  const uint32_t offB = (uint32_t)(kg * 8 * ldx + J0 + mg * 8);
+  const uint32_t ld32 = (uint32_t)ldx;
 
   f32x16 acc[4][4];
 #pragma unroll
@@ -87,22 +113,24 @@ __global__ __launch_bounds__(kThreads) void syrk_f16_kernel(
       for (int r = 0; r < 16; ++r) acc[a][b][r] = 0.f;
 
   half8 ra[8], rb[8];
-  auto gload = [&](int64_t k0, int col0, half8* r) {
+  auto gload_fast = [&](int st, uint32_t off, half8* r) {
+    const _Float16* __restrict__ p = Xs + (int64_t)(st * kKS16) * ldx;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) r[i] = *(const half8*)(p + off + i * ld32);
+  };
+  auto gload_masked = [&](int st, int col0, half8* r) {
+    const int k0 = st * kKS16;
     const int col = col0 + mg * 8;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      const int64_t row = k0 + kg * 8 + i;
-      if (VEC) {
-        if (row < r1 && col < d) {
-          r[i] = *(const half8*)(X + row * ldx + col);
-        } else {
+      const int row = k0 + kg * 8 + i;
+      const bool ok = row < nrows;
+      const int64_t rowc = ok ? row : 0;
 #pragma unroll
-          for (int e = 0; e < 8; ++e) r[i][e] = (_Float16)0.f;
-        }
-      } else {
-#pragma unroll
-        for (int e = 0; e < 8; ++e)
-          r[i][e] = (row < r1 && col + e < d) ? X[row * ldx + col + e] : (_Float16)0.f;
+      for (int e = 0; e < 8; ++e) {
+        const bool cok = col + e < d;
+        const _Float16 v = Xs[rowc * ldx + (cok ? col + e : 0)];
+        r[i][e] = (ok && cok) ? v : (_Float16)0.f;
       }
     }
   };
@@ -115,38 +143,97 @@ __global__ __launch_bounds__(kThreads) void syrk_f16_kernel(
       *(half8*)(L + sw16(mg * 8 + i, kg)) = v;
     }
   };
-
-  const int64_t nst = (r1 > r0) ? (r1 - r0 + kKS16 - 1) / kKS16 : 0;
-  if (nst > 0) {
-    gload(r0, I0, ra);
-    if (!diag) gload(r0, J0, rb);
-  }
-  for (int64_t s = 0; s < nst; ++s) {
-    lstore(lds[0], ra);
-    if (!diag) lstore(lds[1], rb);
-    __syncthreads();
-    if (s + 1 < nst) {
-      gload(r0 + (s + 1) * kKS16, I0, ra);
-      if (!diag) gload(r0 + (s + 1) * kKS16, J0, rb);
+  auto frags = [&](const _Float16* LA, const _Float16* LB, int kk, half8* fa, half8* fb) {
+    const int c = 2 * kk + (lane >> 5);
+#pragma unroll
+    for (int f = 0; f < 4; ++f) {
+      fa[f] = *(const half8*)(LA + sw16(wm * 128 + f * 32 + (lane & 31), c));
+      fb[f] = *(const half8*)(LB + sw16(wn * 128 + f * 32 + (lane & 31), c));
     }
-    const _Float16* LA = lds[0];
-    const _Float16* LB = diag ? lds[0] : lds[1];
+  };
+  auto mfmas = [&](const half8* fa, const half8* fb) {
+#pragma unroll
+    for (int fm = 0; fm < 4; ++fm)
+#pragma unroll
+      for (int fn = 0; fn < 4; ++fn)
+        acc[fm][fn] = __builtin_amdgcn_mfma_f32_32x32x16_f16(fa[fm], fb[fn], acc[fm][fn], 0, 0, 0);
+  };
+
+  // full stages: pipelined, unmasked; indices are clamped so that every
+  // iteration runs the same straight-line code (surplus loads/stores at the end
+  // touch valid memory and an LDS buffer nobody reads afterwards)
+  const int nfull = full_cols ? nrows / kKS16 : 0;
+  half8 fa[2][4], fb[2][4];
+  if (nfull > 0) {
+    gload_fast(0, offA, ra);
+    if (!diag) gload_fast(0, offB, rb);
+    lstore(lds[0][0], ra);
+    if (!diag) lstore(lds[0][1], rb);
+    __syncthreads();
+    const int s1 = nfull > 1 ? 1 : 0;
+    gload_fast(s1, offA, ra);
+    if (!diag) gload_fast(s1, offB, rb);
+    frags(lds[0][0], diag ? lds[0][0] : lds[0][1], 0, fa[0], fb[0]);
+  }
+  for (int s = 0; s < nfull; ++s) {
+    const int cur = s & 1;
+    const _Float16* LA = lds[cur][0];
+    const _Float16* LB = diag ? lds[cur][0] : lds[cur][1];
+    const _Float16* NA = lds[cur ^ 1][0];
+    const _Float16* NB = diag ? lds[cur ^ 1][0] : lds[cur ^ 1][1];
+    const int s2 = min(s + 2, nfull - 1);
+    // substep 0
+    frags(LA, LB, 1, fa[1], fb[1]);
+    mfmas(fa[0], fb[0]);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) { GPTQ_SGB(kSgMFMA, 1); GPTQ_SGB(kSgDSR, 1); }
+    GPTQ_SGB(kSgMFMA, 8);
+    // substep 1: + transpose stage s+1 into the other buffer
+    frags(LA, LB, 2, fa[0], fb[0]);
+    lstore(lds[cur ^ 1][0], ra);
+    if (!diag) lstore(lds[cur ^ 1][1], rb);
+    mfmas(fa[1], fb[1]);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      GPTQ_SGB(kSgMFMA, 1);
+      if (i < 8) GPTQ_SGB(kSgDSR, 1);
+      GPTQ_SGB(kSgVALU, 4);
+      GPTQ_SGB(kSgDSW, 1);
+    }
+    // substep 2: + global loads of stage s+2
+    frags(LA, LB, 3, fa[1], fb[1]);
+    gload_fast(s2, offA, ra);
+    if (!diag) gload_fast(s2, offB, rb);
+    mfmas(fa[0], fb[0]);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      GPTQ_SGB(kSgMFMA, 1);
+      if (i < 8) GPTQ_SGB(kSgDSR, 1);
+      GPTQ_SGB(kSgVMEMR, 1);
+      GPTQ_SGB(kSgVALU, 2);
+    }
+    __syncthreads();
+    // substep 3: + first fragments of stage s+1
+    frags(NA, NB, 0, fa[0], fb[0]);
+    mfmas(fa[1], fb[1]);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) { GPTQ_SGB(kSgMFMA, 1); GPTQ_SGB(kSgDSR, 1); }
+    GPTQ_SGB(kSgMFMA, 8);
+  }
+  // tail stages (partial rows or partial column tiles): masked, not pipelined
+  const int nst = (nrows + kKS16 - 1) / kKS16;
+  for (int s = nfull; s < nst; ++s) {
+    __syncthreads();
+    gload_masked(s, I0, ra);
+    if (!diag) gload_masked(s, J0, rb);
+    lstore(lds[0][0], ra);
+    if (!diag) lstore(lds[0][1], rb);
+    __syncthreads();
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) {
-      half8 a[4], b[4];
-      const int c = 2 * kk + (lane >> 5);
-#pragma unroll
-      for (int f = 0; f < 4; ++f) {
-        a[f] = *(const half8*)(LA + sw16(wm * 128 + f * 32 + (lane & 31), c));
-        b[f] = *(const half8*)(LB + sw16(wn * 128 + f * 32 + (lane & 31), c));
-      }
-#pragma unroll
-      for (int fm = 0; fm < 4; ++fm)
-#pragma unroll
-        for (int fn = 0; fn < 4; ++fn)
-          acc[fm][fn] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[fm], b[fn], acc[fm][fn], 0, 0, 0);
+      frags(lds[0][0], diag ? lds[0][0] : lds[0][1], kk, fa[0], fb[0]);
+      mfmas(fa[0], fb[0]);
     }
-    __syncthreads();
   }
   float* P = part + (split * ntiles + tile) * (int64_t)(kBT16 * kBT16);
 #pragma unroll
@@ -309,14 +396,24 @@ HessianPlan hessian_plan(int64_t d, int64_t n, int dtype) {
     p.ws_bytes = 0;
     return p;
   }
-  // enough work-groups to fill 256 CUs several times, and at most 32768 rows
-  // per fp32 accumulation chain
-  int64_t ns = std::max<int64_t>(cdiv(1024, p.ntiles), cdiv(n, 32768));
-  const int64_t cap = std::max<int64_t>(1, cdiv(n, 1024));
-  if (ns > 8) ns = cdiv(ns, 8) * 8;
-  ns = std::min(ns, cap);
+  // At most 16384 rows per split (short fp32 accumulation chains).  When that
+  // gives fewer than 16 rounds of work-groups over the 256 CUs, the split count
+  // is raised to make tiles x splits a whole number of rounds (no idle tail),
+  // keeping >= 2048 rows per split; each split's rows stay cache-resident while
+  // all tiles pass over them.
+  const int64_t cus = 256;
+  const int64_t ns0 = cdiv(n, 16384);
+  int64_t ns = ns0;
+  if (p.ntiles * ns0 < 16 * cus) {
+    const int64_t unit = cus / std::gcd<int64_t>(p.ntiles, cus);
+    ns = cdiv(ns0, unit) * unit;
+    const int64_t cap = std::max<int64_t>(1, cdiv(n, 2048));
+    if (ns > cap) ns = std::max(ns0, std::min(cap, std::max<int64_t>(1, cdiv(4 * cus, p.ntiles))));
+  }
   int64_t rps = cdiv(n, ns);
   rps = cdiv(rps, ks) * ks;
+  const int64_t rps_max = std::max<int64_t>(ks, ((int64_t(1) << 31) / std::max<int64_t>(d, 1)) / ks * ks);
+  rps = std::min(rps, rps_max);
   p.rows_per_split = rps;
   p.nsplit = cdiv(n, rps);
   p.ws_bytes = (size_t)p.nsplit * (size_t)p.ntiles * (size_t)p.bt * (size_t)p.bt * sizeof(float);
