@@ -55,18 +55,9 @@ hipError_t quant_launch(const QuantPlan& p, const void* W0, int w_dtype, int64_t
                         uint8_t* codes, float* scales, int32_t* zeros, double* out_err,
                         void* ws, hipStream_t s);
 
-// fp32 C[m, n] += alpha * sum_k A[m, k] B[k, n] over a batch; every matrix
-// row-major.  kmode restricts k to exploit triangular operands:
-//   0: all k;  1: B lower triangular in (k, n) (k >= n);  2: A lower in (m, k) (k <= m)
-struct GemmBatch {
-  const float* A; const float* B; float* C;
-  int64_t lda, ldb, ldc;
-  int64_t sA, sB, sC;     // batch strides (elements)
-  int M, N, K, batch;
-  float alpha;
-  int beta_zero;          // 1: C = alpha*A*B (C not read)
-  int kmode;
-};
-hipError_t gemm_f32_launch(const GemmBatch& g, hipStream_t s);
+// W[:, i+B:] -= E U[i:i+B, i+B:] with E given transposed: C [M x N] (ldc) -=
+// Et^T [M x K] * Ub [K x N]; Et is [K x M] (lde), Ub [K x N] (ldu); K <= 128.
+hipError_t trail_update_launch(float* C, int64_t ldc, int M, int N, int K, const float* Et,
+                               int64_t lde, const float* Ub, int64_t ldu, hipStream_t s);
 
 }  // namespace gptq

@@ -7,7 +7,7 @@
 //   panel for each column j of a block: c = clamp(round(w/scale) + zero, 0,
 //         maxq); e = (w - scale (c - zero)) / U[j,j]; W[:, j:] -= e U[j, j:]
 //         inside the block; E[:, j] = e;
-//   GEMM  W[:, i+B:] -= E U[i:i+B, i+B:]  (gemm.hip);
+//   GEMM  W[:, i+B:] -= E U[i:i+B, i+B:]  (gemm.hip; E is kept transposed);
 //   error ||X dW^T||^2 = 1/2 ||E||^2 - lambda/2 ||dW||^2 (the damped objective
 //         is 1/2 ||E||^2 by the OBS increment of the wiki's OBQ equation).
 //
@@ -238,7 +238,7 @@ __global__ __launch_bounds__(kThreads) void panel_kernel(
     const int col = p * CPL + r;
     if (valid && (FULL || col < width)) {
       codes[(size_t)row * d_col + i1 + col] = (uint8_t)cr[r];
-      E[(size_t)row * B + col] = er[r];
+      E[(size_t)col * d_row + row] = er[r];   // E stored transposed: [B x d_row]
       se += (double)er[r] * (double)er[r];
     }
   }
@@ -404,13 +404,9 @@ hipError_t quant_launch(const QuantPlan& p, const void* W0, int w_dtype, int64_t
     if (e != hipSuccess) return e;
     const int64_t i2 = i1 + width;
     if (i2 < d_col) {
-      GemmBatch g{};
-      g.A = E; g.lda = B;
-      g.B = U + i1 * d_col + i2; g.ldb = d_col;
-      g.C = W + i2; g.ldc = d_col;
-      g.M = (int)d_row; g.N = (int)(d_col - i2); g.K = width; g.batch = 1;
-      g.alpha = -1.f; g.beta_zero = 0; g.kmode = 0;
-      if ((e = gemm_f32_launch(g, s)) != hipSuccess) return e;
+      e = trail_update_launch(W + i2, d_col, (int)d_row, (int)(d_col - i2), width, E, d_row,
+                              U + i1 * d_col + i2, d_col, s);
+      if (e != hipSuccess) return e;
     }
   }
   const unsigned nerr = (unsigned)std::min<int64_t>(kErrWGs, d_row);
