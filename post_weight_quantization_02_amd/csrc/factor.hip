@@ -195,6 +195,13 @@ __device__ __forceinline__ void load_tile_f64_as_f32(float* S, const double* __r
   }
 }
 
+// 1/x: the hardware estimate (relative error below 2^-22) refined by one
+// Newton step (error squared: below 2^-44)
+__device__ __forceinline__ double rcp_f64(double x) {
+  const double r = __builtin_amdgcn_rcp(x);
+  return fma(r, fma(-x, r, 1.0), r);
+}
+
 __device__ __forceinline__ double readlane_f64(double v, int lane) {
   const uint64_t u = __builtin_bit_cast(uint64_t, v);
   const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)u, lane);
@@ -202,121 +209,175 @@ __device__ __forceinline__ double readlane_f64(double v, int lane) {
   return __builtin_bit_cast(double, ((uint64_t)hi << 32) | lo);
 }
 
-constexpr int kMP = 9;  // pitch of the panel-multiplier buffer
-
-// rank-8 update of a 16x16 tile of C (LDS, pitch kP): C[R+m][Cc+n] -= sum_k Ak(m, k) Bk(k, n)
-// with Ak(m, k) = Mp[(R+m)*kMP + k] and Bk(k, n) = B[(k)*ldb0 + ...] supplied by the caller as
-// values; lower-only restricts the store to col <= row.
-template <bool LOWER_ONLY, typename BV>
-__device__ __forceinline__ void rank8_tile(double* Cm, const double* Mp, int R, int Cc, int rows,
-                                           int cols, int lane, BV bval) {
-  f64x4 acc;
-#pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    const int row = R + f64_row(lane, r), col = Cc + (lane & 15);
-    acc[r] = (row < rows && col < cols) ? Cm[row * kP + col] : 0.0;
-  }
-#pragma unroll
-  for (int k4 = 0; k4 < 2; ++k4) {
-    const int k = 4 * k4 + (lane >> 4);
-    const int ar = R + (lane & 15);
-    const double av = (ar < rows) ? -Mp[ar * kMP + k] : 0.0;
-    const double bv = bval(k, Cc + (lane & 15));
-    acc = __builtin_amdgcn_mfma_f64_16x16x4f64(av, bv, acc, 0, 0, 0);
-  }
-#pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    const int row = R + f64_row(lane, r), col = Cc + (lane & 15);
-    if (row < rows && col < cols && (!LOWER_ONLY || col <= row)) Cm[row * kP + col] = acc[r];
+template <int I, int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (I < N) {
+    f(std::integral_constant<int, I>{});
+    static_for<I + 1, N>(f);
   }
 }
 
-// Blocked LDL^T of the symmetric 64x64 matrix Dm (lower part used) with the
-// inverse X = M^-1 of its unit-lower factor M (M[i][j] = a_ij / d_j) built
-// alongside: X starts as the identity and receives the same row eliminations.
-// Per 8-column panel: wave 0 factors the panel with one row per lane in
-// registers (pivot values reach all lanes by readlane, no barrier) and
-// finishes X's 8 panel rows (one column per lane); then all four waves apply
-// the rank-8 updates to the trailing lower part of Dm and to X's rows below
-// the panel on fp64 MFMA.
-// On exit Dm[i][j] (i > j) holds the pivot-time column values a_ij, dv[j] =
-// d_j, and X[i][c] (c <= i) = M^-1[i][c].
-__device__ void blocked_ldl_inverse(double* Dm, double* X, double* Mp, double* dv, int t) {
-  const int lane = t & 63, w = t >> 6;
-  for (int idx = t; idx < kNB * kNB; idx += kThreads)
-    X[(idx >> 6) * kP + (idx & 63)] = ((idx >> 6) == (idx & 63)) ? 1.0 : 0.0;
-  __syncthreads();
-  for (int P = 0; P < kNB / 8; ++P) {
-    const int j0 = 8 * P;
-    if (w == 0) {
-      const int i = lane;
-      double v[8], mrow[8];
+// ---------------------------------------------------------------------------
+// Stacked LDL^T elimination of a 64-column block.
+//
+// S0 holds the symmetric diagonal block Dm (lower part; the upper part is free
+// space), S1 holds 64 further rows T that receive the same eliminations (the
+// rows of the block below the diagonal, or the identity).  Eliminating pivot j
+// turns row i into row i - m_ij * (pivot row j), m_ij = a_ij / d_j; for the
+// stacked rows that is Gaussian elimination of [Dm; T], whose multipliers are
+//   m_T = T (D M^T)^-1,   M = unit lower factor of Dm = M D M^T.
+// Hence T M^-T D^-1/2 = m_T D^1/2: the Cholesky tile of T, and for T = I the
+// transpose of D^-1/2 M^-1, the inverse of the diagonal Cholesky factor.
+//
+// Pivots go in panels of 8 columns.  Wave 0 factors a panel with one row per
+// lane in registers (pivot-row values by readlane: a_jc = a_cj sits in lane c),
+// then stores
+//   W  = pivot-time column values a_ij (i >= j) in the lower part of S0,
+//   M^T in the upper part of S0 (row j, columns i > j),
+//   m_T in place of T's panel columns, and d_j in dv.
+// The rank-8 update of everything right of the panel runs on fp64 MFMA in
+// 16x16 tiles.  Wave 0 takes the tiles of the next 16 columns and goes on to
+// factor the next panel at once; waves 1-3 take the remaining tiles; one
+// barrier per panel.  Tiles never overlap between the two groups, and neither
+// group reads what the other writes within a panel step.
+// ---------------------------------------------------------------------------
+enum : int { kTileDm = 0, kTileT = 1, kTileNone = -1 };
+struct TileDesc {
+  int kind, R, C;
+};
+
+// C[R+m][C+n] -= sum_{k<8} A[R+m][J0+k] B[C+n][J0+k] for the tiles desc(0..NT-1);
+// indices past 63 are clamped on load and masked on store.
+template <int J0, int NT, typename Desc>
+__device__ __forceinline__ void rank8_tiles(double* S0, double* S1, int lane, Desc desc) {
+  double cv[NT][4], av[NT][2], bv[NT][2];
+  TileDesc td[NT];
+  const int m = lane & 15, kq = lane >> 4;
 #pragma unroll
-      for (int jj = 0; jj < 8; ++jj) v[jj] = (i >= j0) ? Dm[i * kP + j0 + jj] : 0.0;
+  for (int u = 0; u < NT; ++u) {
+    td[u] = desc(u);
+    const bool isT = td[u].kind == kTileT;
+    const double* Cb = isT ? S1 : S0;
+    const int am = min(td[u].R + m, kNB - 1), bn = min(td[u].C + m, kNB - 1);
 #pragma unroll
-      for (int jj = 0; jj < 8; ++jj) {
-        const double dj = readlane_f64(v[jj], j0 + jj);
-        const double rd = 1.0 / dj;
-        const double mi = (i > j0 + jj) ? v[jj] * rd : 0.0;
-        mrow[jj] = mi;
+    for (int r = 0; r < 4; ++r)
+      cv[u][r] = Cb[min(td[u].R + f64_row(lane, r), kNB - 1) * kP + bn];
 #pragma unroll
-        for (int j2 = jj + 1; j2 < 8; ++j2) v[j2] -= mi * readlane_f64(v[jj], j0 + j2);
-        if (lane == 0) dv[j0 + jj] = dj;
-      }
-      if (i >= j0) {
-#pragma unroll
-        for (int jj = 0; jj < 8; ++jj) Dm[i * kP + j0 + jj] = v[jj];
-      }
-#pragma unroll
-      for (int jj = 0; jj < 8; ++jj) Mp[i * kMP + jj] = mrow[jj];
-      // X rows j0..j0+7 (column c = lane): x_jj -= sum_{jj' < jj} m[j0+jj][j0+jj'] x_jj'
-      double x[8];
-#pragma unroll
-      for (int jj = 0; jj < 8; ++jj) x[jj] = X[(j0 + jj) * kP + lane];
-#pragma unroll
-      for (int jj = 1; jj < 8; ++jj) {
-#pragma unroll
-        for (int q = 0; q < jj; ++q) x[jj] -= readlane_f64(mrow[q], j0 + jj) * x[q];
-      }
-#pragma unroll
-      for (int jj = 0; jj < 8; ++jj) X[(j0 + jj) * kP + lane] = x[jj];
+    for (int k4 = 0; k4 < 2; ++k4) {
+      const int k = J0 + 4 * k4 + kq;
+      // A: M[i][k] = S0[k][i] (transposed multipliers) or m_T[i][k] = S1[i][k]
+      av[u][k4] = -(isT ? S1[am * kP + k] : S0[k * kP + am]);
+      bv[u][k4] = S0[bn * kP + k];  // W[c][k]
     }
-    __syncthreads();
-    const int T0 = j0 + 8;
-    if (T0 < kNB) {
-      // Dm[i][c] -= sum_k Mp[i][k] Dm[c][j0 + k] for T0 <= c <= i (lower 16x16 tiles)
-      const int nT = (kNB - T0 + 15) / 16;
-      const int ntl = nT * (nT + 1) / 2;
-      // X[i][c] -= sum_k Mp[i][k] X[j0 + k][c] for i >= T0, c < T0 (16x16 tiles)
-      const int nXc = (T0 + 15) / 16;
-      const int total = ntl + nT * nXc;
-      for (int tt = w; tt < total; tt += 4) {
-        if (tt < ntl) {
-          int a = 0;
-          while ((a + 1) * (a + 2) / 2 <= tt) ++a;
-          const int b = tt - a * (a + 1) / 2;
-          rank8_tile<true>(Dm, Mp, T0 + 16 * a, T0 + 16 * b, kNB, kNB, lane,
-                           [&](int k, int n) { return n < kNB ? Dm[n * kP + j0 + k] : 0.0; });
-        } else {
-          const int u = tt - ntl;
-          const int a = u / nXc, b = u % nXc;
-          rank8_tile<false>(X, Mp, T0 + 16 * a, 16 * b, kNB, T0, lane,
-                            [&](int k, int n) { return n < T0 ? X[(j0 + k) * kP + n] : 0.0; });
-        }
-      }
-    }
-    __syncthreads();
   }
+#pragma unroll
+  for (int u = 0; u < NT; ++u) {
+    f64x4 acc = {cv[u][0], cv[u][1], cv[u][2], cv[u][3]};
+    acc = __builtin_amdgcn_mfma_f64_16x16x4f64(av[u][0], bv[u][0], acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f64_16x16x4f64(av[u][1], bv[u][1], acc, 0, 0, 0);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) cv[u][r] = acc[r];
+  }
+#pragma unroll
+  for (int u = 0; u < NT; ++u) {
+    if (td[u].kind == kTileNone) continue;
+    const bool isT = td[u].kind == kTileT;
+    double* Cb = isT ? S1 : S0;
+    const int col = td[u].C + m;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int row = td[u].R + f64_row(lane, r);
+      if (row < kNB && col < kNB && (isT || col <= row)) Cb[row * kP + col] = cv[u][r];
+    }
+  }
+}
+
+// wave 0: factor panel P (columns 8P .. 8P+7) of the stacked rows
+template <int P>
+__device__ __forceinline__ void ldl_panel(double* S0, double* S1, double* dv, int lane) {
+  constexpr int J0 = 8 * P;
+  double v[8], vt[8], mu[8];
+#pragma unroll
+  for (int c = 0; c < 8; ++c) v[c] = S0[lane * kP + J0 + c];
+#pragma unroll
+  for (int c = 0; c < 8; ++c) vt[c] = S1[lane * kP + J0 + c];
+  double dsel = 0.0;
+#pragma unroll
+  for (int jj = 0; jj < 8; ++jj) {
+    const double dj = readlane_f64(v[jj], J0 + jj);
+    double s[8];
+#pragma unroll
+    for (int j2 = jj + 1; j2 < 8; ++j2) s[j2] = readlane_f64(v[jj], J0 + j2);  // a_{j, j2}
+    const double rd = rcp_f64(dj);
+    mu[jj] = (lane > J0 + jj) ? v[jj] * rd : 0.0;
+    vt[jj] *= rd;
+#pragma unroll
+    for (int j2 = jj + 1; j2 < 8; ++j2) {
+      v[j2] = fma(-mu[jj], s[j2], v[j2]);
+      vt[j2] = fma(-vt[jj], s[j2], vt[j2]);
+    }
+    dsel = (lane == jj) ? dj : dsel;
+  }
+  if (lane < 8) dv[J0 + lane] = dsel;
+#pragma unroll
+  for (int c = 0; c < 8; ++c)
+    if (lane >= J0 + c) S0[lane * kP + J0 + c] = v[c];
+#pragma unroll
+  for (int c = 0; c < 8; ++c)
+    if (lane > J0 + c) S0[(J0 + c) * kP + lane] = mu[c];
+#pragma unroll
+  for (int c = 0; c < 8; ++c) S1[lane * kP + J0 + c] = vt[c];
+}
+
+// triangular index (a, b), 1 <= b <= a, in order (1,1) (2,1) (2,2) (3,1) ...
+__device__ __forceinline__ void tri_ab(int i, int& a, int& b) {
+  a = 1 + (i >= 1) + (i >= 3);
+  b = i - (a - 1) * a / 2 + 1;
+}
+
+__device__ __forceinline__ void ldl_stacked(double* S0, double* S1, double* dv, int t) {
+  const int lane = t & 63, w = t >> 6;
+  if (w == 0) ldl_panel<0>(S0, S1, dv, lane);
+  __syncthreads();
+  static_for<0, kNB / 8 - 1>([&](auto PP) {
+    constexpr int P = decltype(PP)::value;
+    constexpr int J0 = 8 * P, T0 = J0 + 8;
+    constexpr int nT = (kNB - T0 + 15) / 16;                    // 16-wide column blocks right of the panel
+    constexpr int nDm = nT * (nT - 1) / 2, nTr = 4 * (nT - 1);  // tiles outside column block 0
+    constexpr int nRest = nDm + nTr;
+    if (w == 0) {
+      // column block 0 (holds the next panel): Dm (a, 0) and T (q, 0)
+      rank8_tiles<J0, nT + 4>(S0, S1, lane, [&](int u) {
+        return (u < nT) ? TileDesc{kTileDm, T0 + 16 * u, T0} : TileDesc{kTileT, 16 * (u - nT), T0};
+      });
+      ldl_panel<P + 1>(S0, S1, dv, lane);
+    } else if constexpr (nRest > 0) {
+      const int wv = w - 1;
+      rank8_tiles<J0, (nRest + 2) / 3>(S0, S1, lane, [&](int u) {
+        const int i = wv + 3 * u;
+        if (i >= nRest) return TileDesc{kTileNone, 0, 0};
+        if (i < nDm) {
+          int a, b;
+          tri_ab(i, a, b);
+          return TileDesc{kTileDm, T0 + 16 * a, T0 + 16 * b};
+        }
+        const int q = (i - nDm) / (nT - 1), b = 1 + (i - nDm) % (nT - 1);
+        return TileDesc{kTileT, 16 * q, T0 + 16 * b};
+      });
+    }
+    __syncthreads();
+  });
 }
 
 struct PanelSmem {
   double S0[kNB * kP], S1[kNB * kP];
-  double Mp[kNB * kMP], dv[kNB], sq[kNB], rsq[kNB];  // Mp: 64x9 panel multipliers
+  double dv[kNB], sq[kNB], rsq[kNB];
   int fail;
 };
 
-// S0: L[c1][k], then Dm (the diagonal tile; its factor), then T.
-// S1: L[r][k], then X = M^-1, then Lcc^-1.
+// Step k applied to column block c1 = k+1, then the stacked elimination of
+// [A[c1][c1]; A[r][c1]] (or [A[c1][c1]; I] for r == c1).
+// S0: L[c1][k], then Dm.   S1: L[r][k], then T (or I), then m_T.
 __device__ void task_panel(const StepArgs& a, int b, PanelSmem& sm) {
   const int t = threadIdx.x, lane = t & 63, w = t >> 6, wm = w & 1, wn = w >> 1;
   const int64_t d = a.d;
@@ -324,6 +385,21 @@ __device__ void task_panel(const StepArgs& a, int b, PanelSmem& sm) {
   const int r = c1 + b;
   const bool own = (r == c1);
   const int64_t R0 = (int64_t)r * kNB, C0 = (int64_t)c1 * kNB, K0 = (int64_t)a.k * kNB;
+  const int nbe = (int)std::min<int64_t>(kNB, d - C0);
+  // tiles A[c1][c1] (lower part) and A[r][c1] in the MFMA output layout; their
+  // loads are in flight during the step-k product
+  double gD[16], gT[16];
+#pragma unroll
+  for (int fm = 0; fm < 2; ++fm)
+#pragma unroll
+    for (int fn = 0; fn < 2; ++fn)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int u = (fm * 2 + fn) * 4 + q;
+        const int rr = nt_row(lane, wm, fm, q), cc = nt_col(lane, wn, fn);
+        gD[u] = (cc <= rr && rr < nbe) ? a.A[(C0 + rr) * d + C0 + cc] : 0.0;
+        gT[u] = (!own && R0 + rr < d && cc < nbe) ? a.A[(R0 + rr) * d + C0 + cc] : 0.0;
+      }
   f64x4 accD[2][2], accT[2][2];
   zero_acc(accD);
   zero_acc(accT);
@@ -335,10 +411,6 @@ __device__ void task_panel(const StepArgs& a, int b, PanelSmem& sm) {
     if (!own) mma_nt_f64(sm.S1, sm.S0, accT, lane, wm, wn);
     __syncthreads();
   }
-  const int nbe = (int)std::min<int64_t>(kNB, d - C0);
-  // Dm := A[c1][c1] - L[c1][k] L[c1][k]^T (identity padding past d); T := A[r][c1] - ...
-  // (all global reads issued first)
-  double gD[16], gT[16];
 #pragma unroll
   for (int fm = 0; fm < 2; ++fm)
 #pragma unroll
@@ -347,24 +419,13 @@ __device__ void task_panel(const StepArgs& a, int b, PanelSmem& sm) {
       for (int q = 0; q < 4; ++q) {
         const int u = (fm * 2 + fn) * 4 + q;
         const int rr = nt_row(lane, wm, fm, q), cc = nt_col(lane, wn, fn);
-        const int hi = rr > cc ? rr : cc, lo = rr > cc ? cc : rr;
-        gD[u] = (rr < nbe && cc < nbe) ? a.A[(C0 + hi) * d + C0 + lo] : 0.0;
-        gT[u] = (!own && R0 + rr < d && cc < nbe) ? a.A[(R0 + rr) * d + C0 + cc] : 0.0;
-      }
-#pragma unroll
-  for (int fm = 0; fm < 2; ++fm)
-#pragma unroll
-    for (int fn = 0; fn < 2; ++fn)
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int u = (fm * 2 + fn) * 4 + q;
-        const int rr = nt_row(lane, wm, fm, q), cc = nt_col(lane, wn, fn);
-        sm.S0[rr * kP + cc] = (rr < nbe && cc < nbe) ? gD[u] - accD[fm][fn][q] : (rr == cc ? 1.0 : 0.0);
-        accT[fm][fn][q] = (!own && R0 + rr < d && cc < nbe) ? gT[u] - accT[fm][fn][q] : 0.0;
+        // identity past the end of the matrix keeps the padded pivots at 1
+        sm.S0[rr * kP + cc] = (rr < nbe) ? gD[u] - accD[fm][fn][q] : (rr == cc ? 1.0 : 0.0);
+        sm.S1[rr * kP + cc] = own ? (rr == cc ? 1.0 : 0.0) : gT[u] - accT[fm][fn][q];
       }
   if (t == 0) sm.fail = kNB;
   __syncthreads();
-  blocked_ldl_inverse(sm.S0, sm.S1, sm.Mp, sm.dv, t);
+  ldl_stacked(sm.S0, sm.S1, sm.dv, t);
   if (t < kNB) {
     const double dj = sm.dv[t];
     if (!(dj > 0.0)) atomicMin(&sm.fail, t);
@@ -372,43 +433,23 @@ __device__ void task_panel(const StepArgs& a, int b, PanelSmem& sm) {
     sm.rsq[t] = 1.0 / sm.sq[t];
   }
   __syncthreads();
-  // S1 := Lcc^-1 = diag(rsq) X (unit diagonal implied), zeros above
-  for (int idx = t; idx < kNB * kNB; idx += kThreads) {
-    const int i = idx >> 6, c = idx & 63;
-    sm.S1[i * kP + c] = (c < i) ? sm.S1[i * kP + c] * sm.rsq[i] : (c == i ? sm.rsq[i] : 0.0);
-  }
-  __syncthreads();
   if (own) {
+    // Lcc = W D^-1/2 (diagonal sqrt(d)), Lcc^-1 = (m_T D^1/2)^T
+    double* Dk = a.Dinv + (int64_t)c1 * kNB * kNB;
     for (int idx = t; idx < kNB * kNB; idx += kThreads) {
       const int i = idx >> 6, c = idx & 63;
-      a.Dinv[(int64_t)c1 * kNB * kNB + idx] = sm.S1[i * kP + c];
+      Dk[idx] = (c <= i) ? sm.S1[c * kP + i] * sm.sq[i] : 0.0;
       if (i < nbe && c <= i)
         a.A[(C0 + i) * d + C0 + c] = (c < i) ? sm.S0[i * kP + c] * sm.rsq[c] : sm.sq[i];
     }
     if (t == 0 && sm.fail < nbe && *a.info == 0) *a.info = (int32_t)(d - (C0 + sm.fail));
     return;
   }
-  // L[r][c1] = T Lcc^-T
-#pragma unroll
-  for (int fm = 0; fm < 2; ++fm)
-#pragma unroll
-    for (int fn = 0; fn < 2; ++fn)
-#pragma unroll
-      for (int q = 0; q < 4; ++q)
-        sm.S0[nt_row(lane, wm, fm, q) * kP + nt_col(lane, wn, fn)] = accT[fm][fn][q];
-  __syncthreads();
-  f64x4 acc[2][2];
-  zero_acc(acc);
-  mma_nt_f64(sm.S0, sm.S1, acc, lane, wm, wn);
-#pragma unroll
-  for (int fm = 0; fm < 2; ++fm)
-#pragma unroll
-    for (int fn = 0; fn < 2; ++fn)
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int rr = nt_row(lane, wm, fm, q), cc = nt_col(lane, wn, fn);
-        if (R0 + rr < d && cc < nbe) a.A[(R0 + rr) * d + C0 + cc] = acc[fm][fn][q];
-      }
+  // L[r][c1] = m_T D^1/2
+  for (int idx = t; idx < kNB * kNB; idx += kThreads) {
+    const int i = idx >> 6, c = idx & 63;
+    if (R0 + i < d && c < nbe) a.A[(R0 + i) * d + C0 + c] = sm.S1[i * kP + c] * sm.sq[c];
+  }
 }
 
 struct TileSmem32 {
@@ -518,7 +559,7 @@ __device__ void task_update_inverse(const StepArgs& a, int b, TileSmem32& sm) {
   }
 }
 
-__global__ __launch_bounds__(kThreads) void chol_step_kernel(StepArgs a) {
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) void chol_step_kernel(StepArgs a) {
   __shared__ union Smem {
     PanelSmem p;
     TileSmem32 f;
