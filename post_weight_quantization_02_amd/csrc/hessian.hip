@@ -11,14 +11,8 @@
 // tile into the lower triangle through LDS so both triangles are written with
 // coalesced stores.
 //
-// fp16 X: v_mfma_f32_32x32x16_f16, 256x256 tiles, 64 rows per stage.  X is
-// stored row-major (features contiguous), the MFMA wants 8 consecutive rows
-// per lane, so each thread loads an 8x8 block (8 rows x 16 bytes), transposes
-// it in registers and writes 8 features' 16-byte row chunks to LDS.  LDS rows
-// are 128 bytes; the 16-byte chunk c of feature m is stored at chunk
-// c ^ ((m ^ (m >> 3)) & 7), which keeps both these staging writes (lanes 8
-// features apart) and the fragment reads (consecutive features) free of bank
-// conflicts.
+// fp16 X: v_mfma_f32_32x32x16_f16, 256x256 tiles, X streamed into LDS by
+// direct-to-LDS buffer loads and read back transposed (details below).
 // fp32 X: v_mfma_f32_32x32x2f32 reads one row value per lane, so the natural
 // [row][feature] LDS layout needs no transpose; 128x128 tiles.
 #include "gptq_internal.h"
@@ -61,48 +55,67 @@ __device__ __forceinline__ void wg_map(int64_t ntiles, int64_t nsplit, int64_t& 
 }
 
 // ------------------------------------------------------------------ fp16
-constexpr int kBT16 = 256, kKS16 = 64;
+// 256x256 tile per work-group (four waves, 128x128 each, v_mfma_f32_32x32x16_f16),
+// 32 calibration rows per stage, four LDS stage buffers.
+//
+// X stays row-major in LDS: stage buffer = [A rows 0..31][256 features] then
+// the same for B, 512 bytes per row, with the 16-byte chunk c of row k stored
+// at chunk c ^ (4 (k & 3)).  Global memory reaches LDS by buffer loads that
+// write LDS directly (16 bytes per lane; one instruction fills two rows), so
+// no registers, transposes or LDS stores sit between memory and LDS.  The MFMA
+// wants 8 consecutive rows of one feature per lane; ds_read_b64_tr_b16 gives a
+// lane 4 consecutive rows of one feature out of a 4-row x 16-feature block
+// spread over 16 lanes, so two of them make one operand.  The swizzle spreads
+// each half-wave's 4 rows x 4 chunks over all 16 bank groups, and the loads
+// write whole rows, so neither side has bank conflicts.
+//
+// Pipeline (stage s in buffer s % 4, prefetch 3.5 stages deep):
+//   MFMAs of k-step 0 of stage s | reads of k-step 1 fragments of stage s (all
+//                                   issued under the first half of the MFMAs)
+//   wait: own reads done, own loads of stage s+1 landed; barrier
+//   loads of stage s+4 into buffer s % 4 (free: every wave is past its reads)
+//   MFMAs of k-step 1 of stage s | reads of k-step 0 fragments of stage s+1
+// The four buffers are separate LDS objects and the loop is unrolled by four,
+// so the compiler can tell the buffer being read from the ones being filled
+// and adds no waits of its own.  Waits and barriers are written out with a
+// memory clobber so that no LDS access moves across them.
+constexpr int kBT16 = 256, kKS16 = 32;
+constexpr int kOpHalfs = kKS16 * kBT16;  // one operand of one stage (16 KB)
+constexpr int kStageHalfs = 2 * kOpHalfs;
 
-__device__ __forceinline__ int sw16(int m, int c) {
-  return m * kKS16 + ((c ^ ((m ^ (m >> 3)) & 7)) << 3);
+typedef short v4s __attribute__((ext_vector_type(4)));
+typedef _Float16 half4 __attribute__((ext_vector_type(4)));
+#define GPTQ_LDS __attribute__((address_space(3)))
+
+// byte offset of (row k, feature m) in one operand block; m a multiple of 4
+__device__ __forceinline__ uint32_t swz16(int k, int m) {
+  return (uint32_t)(k * 512 + ((((m >> 3) ^ ((k & 3) << 2))) << 4) + ((m & 7) << 1));
 }
 
-// Software pipeline per 64-row stage s (LDS double-buffered, one barrier):
-//   k-substep 0..3 each issue 16 MFMAs (this wave's 4x4 32x32 fragments) with
-//   the next substep's fragments read from LDS underneath;
-//   substep 1 also transposes the registers holding stage s+1 into LDS buffer
-//   (s+1)&1, substep 2 issues the global loads of stage s+2 into those
-//   registers; the barrier sits between substeps 2 and 3 so that substep 3 can
-//   already read stage s+1's first fragments.  sched_group_barrier pins the
-//   interleave (one MFMA, then a few memory or transpose instructions).
-// Full stages load unmasked from a uniform per-stage base with 32-bit offsets;
-// only a split's tail stage (or a partial last column tile) takes the masked
-// path.
 #define GPTQ_SGB(mask, n) __builtin_amdgcn_sched_group_barrier(mask, n, 0)
-constexpr int kSgMFMA = 0x008, kSgVALU = 0x002, kSgVMEMR = 0x020, kSgDSR = 0x100, kSgDSW = 0x200;
+constexpr int kSgMFMA = 0x008, kSgVMEMR = 0x020, kSgDSR = 0x100;
 
 template <bool VEC>
 __global__ __launch_bounds__(kThreads) void syrk_f16_kernel(
     const _Float16* __restrict__ X, int64_t ldx, int64_t n, int d, int64_t ntiles,
     int64_t nsplit, int64_t rps, float* __restrict__ part) {
-  __shared__ __attribute__((aligned(16))) _Float16 lds[2][2][kBT16 * kKS16];
+  __shared__ __attribute__((aligned(16))) _Float16 L0[kStageHalfs];
+  __shared__ __attribute__((aligned(16))) _Float16 L1[kStageHalfs];
+  __shared__ __attribute__((aligned(16))) _Float16 L2[kStageHalfs];
+  __shared__ __attribute__((aligned(16))) _Float16 L3[kStageHalfs];
   int64_t tile, split;
   wg_map(ntiles, nsplit, tile, split);
   int ti, tj;
   tile_of(tile, ti, tj);
-  const bool diag = (ti == tj);
   const int I0 = ti * kBT16, J0 = tj * kBT16;
   const int64_t r0 = split * rps;
   const int64_t r1 = min(n, r0 + rps);
   const int nrows = (int)(r1 - r0);
-  const int t = threadIdx.x, lane = t & 63, w = t >> 6;
+  const int t = threadIdx.x, lane = t & 63;
+  const int w = __builtin_amdgcn_readfirstlane(t >> 6);
   const int wm = w & 1, wn = w >> 1;
-  const int mg = t & 31, kg = t >> 5;
   const bool full_cols = VEC && (I0 + kBT16 <= d) && (J0 + kBT16 <= d);
-  const _Float16* __restrict__ Xs = X + r0 * ldx;   // this split's first row
-  const uint32_t offA = (uint32_t)(kg * 8 * ldx + I0 + mg * 8);
-  const uint32_t offB = (uint32_t)(kg * 8 * ldx + J0 + mg * 8);
-  const uint32_t ld32 = (uint32_t)ldx;
+  const _Float16* __restrict__ Xs = X + r0 * ldx;  // this split's first row
 
   f32x16 acc[4][4];
 #pragma unroll
@@ -112,126 +125,133 @@ __global__ __launch_bounds__(kThreads) void syrk_f16_kernel(
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[a][b][r] = 0.f;
 
-  half8 ra[8], rb[8];
-  auto gload_fast = [&](int st, uint32_t off, half8* r) {
-    const _Float16* __restrict__ p = Xs + (int64_t)(st * kKS16) * ldx;
+  // fragment addresses: lane l reads rows 8 (l / 32) + (l % 16) / 4 (+ 4, + 16 per
+  // k-step) of feature block wm * 128 + f * 32 + 16 ((l / 16) % 2) + 4 (l % 4)
+  const int kl = 8 * (lane >> 5) + ((lane & 15) >> 2);
+  uint32_t fadA[4], fadB[4];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) r[i] = *(const half8*)(p + off + i * ld32);
-  };
-  auto gload_masked = [&](int st, int col0, half8* r) {
-    const int k0 = st * kKS16;
-    const int col = col0 + mg * 8;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int row = k0 + kg * 8 + i;
-      const bool ok = row < nrows;
-      const int64_t rowc = ok ? row : 0;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const bool cok = col + e < d;
-        const _Float16 v = Xs[rowc * ldx + (cok ? col + e : 0)];
-        r[i][e] = (ok && cok) ? v : (_Float16)0.f;
-      }
-    }
-  };
-  auto lstore = [&](_Float16* L, const half8* r) {
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      half8 v;
-#pragma unroll
-      for (int k = 0; k < 8; ++k) v[k] = r[k][i];
-      *(half8*)(L + sw16(mg * 8 + i, kg)) = v;
-    }
-  };
-  auto frags = [&](const _Float16* LA, const _Float16* LB, int kk, half8* fa, half8* fb) {
-    const int c = 2 * kk + (lane >> 5);
+  for (int f = 0; f < 4; ++f) {
+    const int mo = f * 32 + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+    fadA[f] = swz16(kl, wm * 128 + mo);
+    fadB[f] = swz16(kl, wn * 128 + mo) + kOpHalfs * 2;
+  }
+  half8 fa[2][4], fb[2][4];
+  auto frags = [&](const _Float16* L, int kk, half8* xa, half8* xb) {
+    const char GPTQ_LDS* base = (const char GPTQ_LDS*)L;
 #pragma unroll
     for (int f = 0; f < 4; ++f) {
-      fa[f] = *(const half8*)(LA + sw16(wm * 128 + f * 32 + (lane & 31), c));
-      fb[f] = *(const half8*)(LB + sw16(wn * 128 + f * 32 + (lane & 31), c));
+      const v4s a0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((v4s GPTQ_LDS*)(base + fadA[f] + kk * 16 * 512));
+      const v4s a1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((v4s GPTQ_LDS*)(base + fadA[f] + kk * 16 * 512 + 4 * 512));
+      const v4s b0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((v4s GPTQ_LDS*)(base + fadB[f] + kk * 16 * 512));
+      const v4s b1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((v4s GPTQ_LDS*)(base + fadB[f] + kk * 16 * 512 + 4 * 512));
+      xa[f] = __builtin_shufflevector(__builtin_bit_cast(half4, a0), __builtin_bit_cast(half4, a1), 0, 1, 2, 3, 4, 5, 6, 7);
+      xb[f] = __builtin_shufflevector(__builtin_bit_cast(half4, b0), __builtin_bit_cast(half4, b1), 0, 1, 2, 3, 4, 5, 6, 7);
     }
   };
-  auto mfmas = [&](const half8* fa, const half8* fb) {
+  auto mfmas = [&](const half8* xa, const half8* xb) {
 #pragma unroll
     for (int fm = 0; fm < 4; ++fm)
 #pragma unroll
       for (int fn = 0; fn < 4; ++fn)
-        acc[fm][fn] = __builtin_amdgcn_mfma_f32_32x32x16_f16(fa[fm], fb[fn], acc[fm][fn], 0, 0, 0);
+        acc[fm][fn] = __builtin_amdgcn_mfma_f32_32x32x16_f16(xa[fm], xb[fn], acc[fm][fn], 0, 0, 0);
   };
 
-  // full stages: pipelined, unmasked; indices are clamped so that every
-  // iteration runs the same straight-line code (surplus loads/stores at the end
-  // touch valid memory and an LDS buffer nobody reads afterwards)
   const int nfull = full_cols ? nrows / kKS16 : 0;
-  half8 fa[2][4], fb[2][4];
-  if (nfull > 0) {
-    gload_fast(0, offA, ra);
-    if (!diag) gload_fast(0, offB, rb);
-    lstore(lds[0][0], ra);
-    if (!diag) lstore(lds[0][1], rb);
-    __syncthreads();
-    const int s1 = nfull > 1 ? 1 : 0;
-    gload_fast(s1, offA, ra);
-    if (!diag) gload_fast(s1, offB, rb);
-    frags(lds[0][0], diag ? lds[0][0] : lds[0][1], 0, fa[0], fb[0]);
-  }
-  for (int s = 0; s < nfull; ++s) {
-    const int cur = s & 1;
-    const _Float16* LA = lds[cur][0];
-    const _Float16* LB = diag ? lds[cur][0] : lds[cur][1];
-    const _Float16* NA = lds[cur ^ 1][0];
-    const _Float16* NB = diag ? lds[cur ^ 1][0] : lds[cur ^ 1][1];
-    const int s2 = min(s + 2, nfull - 1);
-    // substep 0
-    frags(LA, LB, 1, fa[1], fb[1]);
-    mfmas(fa[0], fb[0]);
+  const int nq = nfull >> 2;  // pipelined stages come in fours
+  if (nq > 0) {
+    // buffer loads with a uniform base and per-stage offset; the launch keeps the
+    // split's byte span below 2^31
+    const uint64_t xb = (uint64_t)(uintptr_t)Xs;
+    const uint64_t xu = ((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(xb >> 32)) << 32) |
+                        (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)xb);
+    const __amdgpu_buffer_rsrc_t rsrc =
+        __builtin_amdgcn_make_buffer_rsrc((void*)(uintptr_t)xu, (short)0, 0x7FFFFFFF, 0x00020000);
+    const uint32_t ldb = (uint32_t)ldx * 2u;
+    // load j (0..3) of this wave fills rows 8 w + 2 j, + 1 of the operand; lane l
+    // brings chunk l % 32 of row 8 w + 2 j + l / 32 (its logical chunk unswizzled)
+    uint32_t voA[4], voB[4];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) { GPTQ_SGB(kSgMFMA, 1); GPTQ_SGB(kSgDSR, 1); }
-    GPTQ_SGB(kSgMFMA, 8);
-    // substep 1: + transpose stage s+1 into the other buffer
-    frags(LA, LB, 2, fa[0], fb[0]);
-    lstore(lds[cur ^ 1][0], ra);
-    if (!diag) lstore(lds[cur ^ 1][1], rb);
-    mfmas(fa[1], fb[1]);
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      GPTQ_SGB(kSgMFMA, 1);
-      if (i < 8) GPTQ_SGB(kSgDSR, 1);
-      GPTQ_SGB(kSgVALU, 4);
-      GPTQ_SGB(kSgDSW, 1);
+    for (int j = 0; j < 4; ++j) {
+      const int kr = 8 * w + 2 * j + (lane >> 5);
+      const int c = (lane & 31) ^ ((kr & 3) << 2);
+      voA[j] = (uint32_t)kr * ldb + (uint32_t)(I0 + 8 * c) * 2u;
+      voB[j] = (uint32_t)kr * ldb + (uint32_t)(J0 + 8 * c) * 2u;
     }
-    // substep 2: + global loads of stage s+2
-    frags(LA, LB, 3, fa[1], fb[1]);
-    gload_fast(s2, offA, ra);
-    if (!diag) gload_fast(s2, offB, rb);
-    mfmas(fa[0], fb[0]);
+    const int last = 4 * nq - 1;
+    auto dma = [&](_Float16* L, int st) {
+      const int so = __builtin_amdgcn_readfirstlane((int)((uint32_t)(min(st, last) * kKS16) * ldb));
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      GPTQ_SGB(kSgMFMA, 1);
-      if (i < 8) GPTQ_SGB(kSgDSR, 1);
-      GPTQ_SGB(kSgVMEMR, 1);
-      GPTQ_SGB(kSgVALU, 2);
+      for (int j = 0; j < 4; ++j) {
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (void GPTQ_LDS*)(L + (8 * w + 2 * j) * kBT16), 16,
+                                                 voA[j], so, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (void GPTQ_LDS*)(L + kOpHalfs + (8 * w + 2 * j) * kBT16),
+                                                 16, voB[j], so, 0, 0);
+      }
+    };
+    dma(L0, 0);
+    dma(L1, 1);
+    dma(L2, 2);
+    dma(L3, 3);
+    asm volatile("s_waitcnt vmcnt(24)\n\ts_barrier" ::: "memory");
+    frags(L0, 0, fa[0], fb[0]);
+    auto step = [&](_Float16* Lc, _Float16* Ln, int s) {
+      frags(Lc, 1, fa[1], fb[1]);
+      mfmas(fa[0], fb[0]);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) { GPTQ_SGB(kSgMFMA, 1); GPTQ_SGB(kSgDSR, 2); }
+      GPTQ_SGB(kSgMFMA, 8);
+      asm volatile("s_waitcnt vmcnt(16) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+      dma(Lc, s + 4);
+      frags(Ln, 0, fa[0], fb[0]);
+      mfmas(fa[1], fb[1]);
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        GPTQ_SGB(kSgMFMA, 1);
+        if (i < 8) GPTQ_SGB(kSgDSR, 2);
+        else GPTQ_SGB(kSgVMEMR, 1);
+      }
+    };
+    for (int q = 0; q < nq; ++q) {
+      step(L0, L1, 4 * q + 0);
+      step(L1, L2, 4 * q + 1);
+      step(L2, L3, 4 * q + 2);
+      step(L3, L0, 4 * q + 3);
     }
-    __syncthreads();
-    // substep 3: + first fragments of stage s+1
-    frags(NA, NB, 0, fa[0], fb[0]);
-    mfmas(fa[1], fb[1]);
-#pragma unroll
-    for (int i = 0; i < 8; ++i) { GPTQ_SGB(kSgMFMA, 1); GPTQ_SGB(kSgDSR, 1); }
-    GPTQ_SGB(kSgMFMA, 8);
+    // the surplus loads of the last steps must land before L0 is reused
+    asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
   }
-  // tail stages (partial rows or partial column tiles): masked, not pipelined
+  // remaining stages (a split's last < 4 full stages, its partial stage, or a
+  // partial column tile): masked register loads into L0, not pipelined
   const int nst = (nrows + kKS16 - 1) / kKS16;
-  for (int s = nfull; s < nst; ++s) {
-    __syncthreads();
-    gload_masked(s, I0, ra);
-    if (!diag) gload_masked(s, J0, rb);
-    lstore(lds[0][0], ra);
-    if (!diag) lstore(lds[0][1], rb);
+  for (int s = 4 * nq; s < nst; ++s) {
+    const int k0 = s * kKS16;
+    half8 va[4], vb[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int q = t + kThreads * u, k = q >> 5, c = q & 31;
+      const int row = k0 + k;
+      const bool rok = row < nrows;
+      const int64_t rowc = rok ? row : 0;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int ca = I0 + 8 * c + e, cb = J0 + 8 * c + e;
+        const _Float16 xa = Xs[rowc * ldx + (ca < d ? ca : 0)];
+        const _Float16 xbv = Xs[rowc * ldx + (cb < d ? cb : 0)];
+        va[u][e] = (rok && ca < d) ? xa : (_Float16)0.f;
+        vb[u][e] = (rok && cb < d) ? xbv : (_Float16)0.f;
+      }
+    }
     __syncthreads();
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk) {
-      frags(lds[0][0], diag ? lds[0][0] : lds[0][1], kk, fa[0], fb[0]);
+    for (int u = 0; u < 4; ++u) {
+      const int q = t + kThreads * u, k = q >> 5, c = q & 31;
+      *(half8*)((char*)L0 + swz16(k, 8 * c)) = va[u];
+      *(half8*)((char*)L0 + kOpHalfs * 2 + swz16(k, 8 * c)) = vb[u];
+    }
+    __syncthreads();
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+      frags(L0, kk, fa[0], fb[0]);
       mfmas(fa[0], fb[0]);
     }
   }
@@ -387,7 +407,8 @@ HessianPlan hessian_plan(int64_t d, int64_t n, int dtype) {
   HessianPlan p{};
   p.dtype = dtype;
   p.bt = (dtype == 1) ? kBT16 : kBT32;
-  const int ks = (dtype == 1) ? kKS16 : kKS32;
+  // fp16 splits are whole multiples of the four-stage pipelined unit
+  const int ks = (dtype == 1) ? 4 * kKS16 : kKS32;
   p.tiles_side = cdiv(d, p.bt);
   p.ntiles = p.tiles_side * (p.tiles_side + 1) / 2;
   if (n <= 0) {
@@ -396,19 +417,21 @@ HessianPlan hessian_plan(int64_t d, int64_t n, int dtype) {
     p.ws_bytes = 0;
     return p;
   }
-  // At most 16384 rows per split (short fp32 accumulation chains).  When that
-  // gives fewer than 16 rounds of work-groups over the 256 CUs, the split count
-  // is raised to make tiles x splits a whole number of rounds (no idle tail),
-  // keeping >= 2048 rows per split; each split's rows stay cache-resident while
-  // all tiles pass over them.
+  // Splits: at least cdiv(n, 32768) (fp32 accumulation chains of at most 32768
+  // rows), at least 4 work-group rounds over the 256 CUs when n allows 1024-row
+  // splits, and the first count from there whose work-groups fill their last
+  // round to >= 97% (tiles x splits just below a multiple of 256).  Fewer
+  // splits means fewer partial tiles to write and reduce.
   const int64_t cus = 256;
-  const int64_t ns0 = cdiv(n, 16384);
-  int64_t ns = ns0;
-  if (p.ntiles * ns0 < 16 * cus) {
-    const int64_t unit = cus / std::gcd<int64_t>(p.ntiles, cus);
-    ns = cdiv(ns0, unit) * unit;
-    const int64_t cap = std::max<int64_t>(1, cdiv(n, 2048));
-    if (ns > cap) ns = std::max(ns0, std::min(cap, std::max<int64_t>(1, cdiv(4 * cus, p.ntiles))));
+  int64_t ns = cdiv(n, 32768);
+  const int64_t ns_cap = std::max<int64_t>(1, cdiv(n, 1024));
+  ns = std::max(ns, std::min(ns_cap, cdiv(4 * cus, p.ntiles)));
+  for (int64_t c = ns; c <= std::min<int64_t>(ns_cap, ns + 64); ++c) {
+    const int64_t wg = p.ntiles * c, rounds = cdiv(wg, cus);
+    if (wg * 100 >= rounds * cus * 97) {
+      ns = c;
+      break;
+    }
   }
   int64_t rps = cdiv(n, ns);
   rps = cdiv(rps, ks) * ks;
@@ -426,7 +449,9 @@ hipError_t hessian_launch(const HessianPlan& p, float* H, int64_t d, const void*
   float* part = (float*)ws;
   const int64_t grid = p.ntiles * p.nsplit;
   if (p.dtype == 1) {
-    const bool vec = (d % 8 == 0) && (ldx % 8 == 0) && (((uintptr_t)X & 15) == 0);
+    // the fast path addresses a split with 32-bit byte offsets
+    const bool fits = (p.rows_per_split + kKS16) * ldx * 2 < (int64_t(1) << 31);
+    const bool vec = fits && (d % 8 == 0) && (ldx % 8 == 0) && (((uintptr_t)X & 15) == 0);
     if (vec)
       hipLaunchKernelGGL(syrk_f16_kernel<true>, dim3((unsigned)grid), dim3(kThreads), 0, s,
                          (const _Float16*)X, ldx, n, (int)d, p.ntiles, p.nsplit, p.rows_per_split, part);
