@@ -16,7 +16,8 @@
 // row, 8 consecutive block columns per lane (B = 128).  Per column the owner
 // lane's scaled error reaches the other 15 lanes of its row with one DPP
 // row_newbcast, and every lane applies the rank-1 update to its own columns
-// with U[j, :] read from LDS (the block's diagonal part of U lives there).
+// with U[j, :] read from LDS (the block's diagonal part of U lives there),
+// prefetched a few columns ahead so the serial column chain never waits on LDS.
 // Per-group min/max is a 16-lane butterfly.  No block-wide barrier is needed
 // after U is staged.
 #include "gptq_internal.h"
@@ -176,6 +177,24 @@ __global__ __launch_bounds__(kThreads) void panel_kernel(
   }
   float rs = 1.f / s;
   const float fmaxq = (float)maxq;
+  // 1 / U[j][j] for this lane's own columns (only the owner's error is used)
+  float rdl[CPL];
+#pragma unroll
+  for (int r = 0; r < CPL; ++r) rdl[r] = rd[p * CPL + r];
+  // U rows of the block, this lane's CPL columns, prefetched kPF columns ahead
+  constexpr int kPF = 4, kQ = (CPL + 3) / 4;
+  f32x4 ub[kPF][kQ];
+  auto uload = [&](int j, f32x4* dst) {
+    if constexpr (CPL >= 4) {
+#pragma unroll
+      for (int q = 0; q < kQ; ++q) dst[q] = *(const f32x4*)&Us[j * B + p * CPL + 4 * q];
+    } else {
+#pragma unroll
+      for (int r = 0; r < CPL; ++r) dst[0][r] = Us[j * B + p * CPL + r];
+    }
+  };
+#pragma unroll
+  for (int j = 0; j < kPF; ++j) uload(j, ub[j]);
 
   static_for<0, 16>([&](auto kc) {
     constexpr int kk = decltype(kc)::value;
@@ -209,25 +228,22 @@ __global__ __launch_bounds__(kThreads) void panel_kernel(
         }
         const float x = w[jj];
         const float c = fminf(fmaxf(rintf(x * rs) + z, 0.f), fmaxq);
-        const float e = (x - s * (c - z)) * rd[j];
-        if (p == kk) {
-          cr[jj] = c;
-          er[jj] = e;
-        }
+        const float e = (x - s * (c - z)) * rdl[jj];
+        const bool own = (p == kk);
+        cr[jj] = own ? c : cr[jj];
+        er[jj] = own ? e : er[jj];
         const float eb = row_bcast<kk>(e);
-        const f32x4* ur = (const f32x4*)&Us[j * B + p * CPL];
+        const f32x4* u = ub[j % kPF];
         if constexpr (CPL >= 4) {
 #pragma unroll
-          for (int q = 0; q < CPL / 4; ++q) {
-            const f32x4 u = ur[q];
+          for (int q = 0; q < kQ; ++q)
 #pragma unroll
-            for (int r = 0; r < 4; ++r) w[4 * q + r] = fmaf(-eb, u[r], w[4 * q + r]);
-          }
+            for (int r = 0; r < 4; ++r) w[4 * q + r] = fmaf(-eb, u[q][r], w[4 * q + r]);
         } else {
-          const float* u1 = &Us[j * B + p * CPL];
 #pragma unroll
-          for (int r = 0; r < CPL; ++r) w[r] = fmaf(-eb, u1[r], w[r]);
+          for (int r = 0; r < CPL; ++r) w[r] = fmaf(-eb, u[0][r], w[r]);
         }
+        if constexpr (j + kPF < B) uload(j + kPF, ub[j % kPF]);
       }
     });
   });
