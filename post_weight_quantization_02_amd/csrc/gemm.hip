@@ -17,6 +17,7 @@ namespace gptq {
 namespace {
 
 constexpr int kT = 128, kKP = 64, kP = kT + 4, kThreads = 256;
+#define GPTQ_LDS __attribute__((address_space(3)))
 
 __device__ __forceinline__ int64_t xcd_remap(int64_t bid, int64_t total) {
   const int64_t q = total / 8, r = total % 8;
@@ -136,6 +137,174 @@ __global__ __launch_bounds__(kThreads) void trail_kernel(float* __restrict__ C, 
       }
 }
 
+
+// ---------------------------------------------------------------------------
+// Aligned operands (the usual case): the same 128x128 tile, with Et and U rows
+// streamed by buffer loads straight into LDS (their row-major [k][m] / [k][n]
+// layout is already what the 32x32x2 MFMA reads), K in sub-phases of 32 rows
+// double-buffered, and the C tile read under the last sub-phase's MFMAs in a
+// coalesced per-wave layout.  Each wave finishes its own 64x64 quadrant through a
+// private LDS array: accumulators in, row-major out, C - acc, store.
+// Rows past K and columns past N read zeros or neighbouring data that only
+// reaches discarded outputs; the buffer extents keep every read inside Et and U.
+constexpr int kKS = 32;
+
+template <int NSUB>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) void trail_dma_kernel(float* __restrict__ C, int64_t ldc,
+                                                             int M, int N, int K,
+                                                             const float* __restrict__ Et, int64_t lde,
+                                                             const float* __restrict__ Ub, int64_t ldu,
+                                                             int64_t tiles_m, int64_t tiles_n) {
+  __shared__ __attribute__((aligned(16))) float E0[kKS * kT];
+  __shared__ __attribute__((aligned(16))) float U0[kKS * kT];
+  __shared__ __attribute__((aligned(16))) float E1[kKS * kT];
+  __shared__ __attribute__((aligned(16))) float U1[kKS * kT];
+  const int64_t lid = xcd_remap(blockIdx.x, tiles_m * tiles_n);
+  const int m0 = (int)(lid / tiles_n) * kT, n0 = (int)(lid % tiles_n) * kT;
+  const int t = threadIdx.x, lane = t & 63;
+  const int w = __builtin_amdgcn_readfirstlane(t >> 6);
+  const int wm = w & 1, wn = w >> 1;
+
+  auto uniform_ptr = [](const float* p) {
+    const uint64_t b = (uint64_t)(uintptr_t)p;
+    return (const float*)(uintptr_t)(((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(b >> 32)) << 32) |
+                                     (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)b));
+  };
+  // buffer extents: K rows of Et from column m0, K rows of U from column n0
+  const float* eb = uniform_ptr(Et + m0);
+  const float* ub = uniform_ptr(Ub + n0);
+  const uint32_t ebytes = (uint32_t)(((int64_t)(K - 1) * lde + (M - m0)) * 4);
+  const uint32_t ubytes = (uint32_t)(((int64_t)(K - 1) * ldu + (N - n0)) * 4);
+  const __amdgpu_buffer_rsrc_t er = __builtin_amdgcn_make_buffer_rsrc((void*)eb, (short)0, (int)ebytes, 0x00020000);
+  const __amdgpu_buffer_rsrc_t ur = __builtin_amdgcn_make_buffer_rsrc((void*)ub, (short)0, (int)ubytes, 0x00020000);
+  // load j of this wave fills rows 8 w + 2 j, + 1 (lane / 32) of a 32-row sub-phase
+  uint32_t voE[4], voU[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int kr = 8 * w + 2 * j + (lane >> 5);
+    voE[j] = (uint32_t)(kr * lde + (lane & 31) * 4) * 4u;
+    voU[j] = (uint32_t)(kr * ldu + (lane & 31) * 4) * 4u;
+  }
+  auto dma = [&](float* LE, float* LU, int sub) {
+    const int soE = __builtin_amdgcn_readfirstlane((int)((uint32_t)(sub * kKS) * (uint32_t)lde * 4u));
+    const int soU = __builtin_amdgcn_readfirstlane((int)((uint32_t)(sub * kKS) * (uint32_t)ldu * 4u));
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(er, (void GPTQ_LDS*)(LE + (8 * w + 2 * j) * kT), 16, voE[j], soE, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(ur, (void GPTQ_LDS*)(LU + (8 * w + 2 * j) * kT), 16, voU[j], soU, 0, 0);
+    }
+  };
+  // C quadrant of this wave, coalesced: rows lane / 16 + 4 i, columns 4 (lane % 16) .. + 3
+  const int qr0 = m0 + wm * 64 + (lane >> 4), qc = n0 + wn * 64 + (lane & 15) * 4;
+  f32x4 cq[16];
+  auto cload = [&]() {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int row = qr0 + 4 * i;
+      if (row < M && qc + 3 < N) {
+        cq[i] = *(const f32x4*)(C + (int64_t)row * ldc + qc);
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) cq[i][e] = (row < M && qc + e < N) ? C[(int64_t)row * ldc + qc + e] : 0.f;
+      }
+    }
+  };
+
+  f32x16 acc[2][2];
+#pragma unroll
+  for (int a = 0; a < 2; ++a)
+#pragma unroll
+    for (int b = 0; b < 2; ++b)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[a][b][r] = 0.f;
+  auto compute = [&](const float* LE, const float* LU, int sub) {
+    const int kv = K - sub * kKS;  // valid rows in this sub-phase
+#pragma unroll
+    for (int kk = 0; kk < kKS / 2; ++kk) {
+      const int k = 2 * kk + (lane >> 5);
+      float a[2], b[2];
+#pragma unroll
+      for (int f = 0; f < 2; ++f) {
+        a[f] = LE[k * kT + wm * 64 + f * 32 + (lane & 31)];
+        b[f] = LU[k * kT + wn * 64 + f * 32 + (lane & 31)];
+        if (kv < kKS) a[f] = (k < kv) ? a[f] : 0.f;
+      }
+#pragma unroll
+      for (int fm = 0; fm < 2; ++fm)
+#pragma unroll
+        for (int fn = 0; fn < 2; ++fn)
+          acc[fm][fn] = __builtin_amdgcn_mfma_f32_32x32x2f32(a[fm], b[fn], acc[fm][fn], 0, 0, 0);
+    }
+  };
+
+  // sub-phase s lives in buffer s % 2; the loads of s + 1 run under the MFMAs of
+  // s; C is read under the MFMAs of the last sub-phase
+  dma(E0, U0, 0);
+  if constexpr (NSUB > 1) {
+    dma(E1, U1, 1);
+    asm volatile("s_waitcnt vmcnt(8)\n\ts_barrier" ::: "memory");
+  } else {
+    asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
+    cload();
+  }
+  compute(E0, U0, 0);
+  if constexpr (NSUB > 1) {
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    if constexpr (NSUB > 2) {
+      dma(E0, U0, 2);
+      asm volatile("s_waitcnt vmcnt(8)\n\ts_barrier" ::: "memory");
+    } else {
+      asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
+      cload();
+    }
+    compute(E1, U1, 1);
+  }
+  if constexpr (NSUB > 2) {
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    if constexpr (NSUB > 3) {
+      dma(E1, U1, 3);
+      asm volatile("s_waitcnt vmcnt(8)\n\ts_barrier" ::: "memory");
+    } else {
+      asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
+      cload();
+    }
+    compute(E0, U0, 2);
+  }
+  if constexpr (NSUB > 3) {
+    asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
+    cload();
+    compute(E1, U1, 3);
+  }
+  // epilogue: every wave is done with the operand buffers after this barrier
+  asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  float* Q = (w == 0) ? E0 : (w == 1) ? U0 : (w == 2) ? E1 : U1;  // 64x64 private quadrant
+#pragma unroll
+  for (int fm = 0; fm < 2; ++fm)
+#pragma unroll
+    for (int fn = 0; fn < 2; ++fn)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int row = fm * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+        const int col = fn * 32 + (lane & 31);
+        Q[row * 64 + col] = acc[fm][fn][r];
+      }
+  __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): own writes done before own reads
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const int lr = (lane >> 4) + 4 * i;
+    const f32x4 a = *(const f32x4*)&Q[lr * 64 + (lane & 15) * 4];
+    const int row = qr0 + 4 * i;
+    const f32x4 v = cq[i] - a;
+    if (row < M && qc + 3 < N) {
+      *(f32x4*)(C + (int64_t)row * ldc + qc) = v;
+    } else {
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        if (row < M && qc + e < N) C[(int64_t)row * ldc + qc + e] = v[e];
+    }
+  }
+}
+
 }  // namespace
 
 hipError_t trail_update_launch(float* C, int64_t ldc, int M, int N, int K, const float* Et,
@@ -144,7 +313,18 @@ hipError_t trail_update_launch(float* C, int64_t ldc, int M, int N, int K, const
   const int64_t tm = cdiv(M, kT), tn = cdiv(N, kT);
   const bool vec = (lde % 4 == 0) && (ldu % 4 == 0) && (((uintptr_t)Et & 15) == 0) &&
                    (((uintptr_t)Ub & 15) == 0);
-  if (vec)
+  // buffer loads need 32-bit byte extents and 16-byte rows
+  const bool dma = vec && (ldc % 4 == 0) && (((uintptr_t)C & 15) == 0) && K <= 4 * kKS &&
+                   (int64_t)K * std::max(lde, ldu) * 4 < (int64_t(1) << 31);
+  if (dma) {
+    const dim3 g((unsigned)(tm * tn)), b(kThreads);
+    switch ((K + kKS - 1) / kKS) {
+      case 1: hipLaunchKernelGGL(trail_dma_kernel<1>, g, b, 0, s, C, ldc, M, N, K, Et, lde, Ub, ldu, tm, tn); break;
+      case 2: hipLaunchKernelGGL(trail_dma_kernel<2>, g, b, 0, s, C, ldc, M, N, K, Et, lde, Ub, ldu, tm, tn); break;
+      case 3: hipLaunchKernelGGL(trail_dma_kernel<3>, g, b, 0, s, C, ldc, M, N, K, Et, lde, Ub, ldu, tm, tn); break;
+      default: hipLaunchKernelGGL(trail_dma_kernel<4>, g, b, 0, s, C, ldc, M, N, K, Et, lde, Ub, ldu, tm, tn); break;
+    }
+  } else if (vec)
     hipLaunchKernelGGL(trail_kernel<true>, dim3((unsigned)(tm * tn)), dim3(kThreads), 0, s, C, ldc,
                        M, N, K, Et, lde, Ub, ldu, tm, tn);
   else
