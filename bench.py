@@ -39,6 +39,9 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--traffic", default=os.path.join(ROOT, "profiles", "syrk_f16_attn4096_traffic.json"),
                     help="rocprofv3 --pmc derived HBM bytes of the dominant kernel (JSON), if any")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
+                    help="run two plain device-to-device copies of BYTES bytes and exit (the reference "
+                         "kernel for scaling the FETCH_SIZE / WRITE_SIZE counters)")
     return ap.parse_args()
 
 
@@ -85,6 +88,15 @@ def main():
     import numpy as np
     import torch
 
+    if args.copy_calibration:
+        src = torch.ones(args.copy_calibration, dtype=torch.uint8, device="cuda:0")
+        dst = torch.empty_like(src)
+        for _ in range(2):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"bench: copied {args.copy_calibration} bytes twice")
+        return
+
     import post_weight_quantization_02_amd as G
     import workloads as wl
 
@@ -120,9 +132,9 @@ def main():
     stream = torch.cuda.current_stream()
 
     def step(ev=None):
+        H.zero_()
         if ev:
             ev[0].record(stream)
-        H.zero_()
         G.gptq_hessian_accumulate(H, Xd, ws=ws_h, stream=stream)
         if ev:
             ev[1].record(stream)

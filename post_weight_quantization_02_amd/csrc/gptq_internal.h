@@ -19,6 +19,14 @@ inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 // ---------------------------------------------------------------- Hessian
+// Tile visiting order for the Hessian work-groups (upper-triangle tile ids),
+// passed by value as a kernel argument.
+struct TileOrder {
+  static constexpr int kMax = 1024;
+  int n;                  // 0: natural order
+  uint16_t id[kMax];
+};
+
 struct HessianPlan {
   int dtype;              // 0 = f32, 1 = f16
   int bt;                 // square tile edge
@@ -27,6 +35,7 @@ struct HessianPlan {
   int64_t nsplit;         // row ranges reduced in a fixed order
   int64_t rows_per_split;
   size_t ws_bytes;        // partial tiles
+  TileOrder order;        // tiles grouped per XCD to share column blocks in its L2
 };
 HessianPlan hessian_plan(int64_t d, int64_t n, int dtype);
 hipError_t hessian_launch(const HessianPlan& p, float* H, int64_t d, const void* X, int64_t n,

@@ -18,6 +18,7 @@
 #include "gptq_internal.h"
 
 #include <numeric>
+#include <vector>
 
 namespace gptq {
 namespace {
@@ -36,18 +37,19 @@ __device__ __forceinline__ void tile_of(int64_t t, int& ti, int& tj) {
 // work-group -> (tile, split).  Splits are visited in order by the whole GPU
 // (split-major), so at any time the running work-groups read the same few
 // split row ranges and those stay in the Infinity Cache while every tile
-// passes over them.  When the tile count is a multiple of 8, XCD x (work-groups
-// are dispatched round-robin over the 8 XCDs) takes the contiguous tile range
-// [x * ntiles / 8, (x + 1) * ntiles / 8) of each split, so tiles that share
-// column blocks share that XCD's L2.
-__device__ __forceinline__ void wg_map(int64_t ntiles, int64_t nsplit, int64_t& tile,
-                                       int64_t& split) {
+// passes over them.  Work-groups are dispatched round-robin over the 8 XCDs,
+// so with the tile count a multiple of 8, XCD x takes tiles
+// ord[x * ntiles / 8 .. (x + 1) * ntiles / 8) of every split: the plan groups
+// tiles that share column blocks there, so each XCD's L2 serves few blocks.
+__device__ __forceinline__ void wg_map(int64_t ntiles, int64_t nsplit, const TileOrder& ord,
+                                       int64_t& tile, int64_t& split) {
   const int64_t bid = blockIdx.x;
   if ((ntiles & 7) == 0) {
     const int64_t per = ntiles >> 3;
     const int64_t j = bid >> 3;
     split = j / per;
-    tile = (bid & 7) * per + j % per;
+    const int64_t k = (bid & 7) * per + j % per;
+    tile = ord.n ? (int64_t)ord.id[k] : k;
   } else {
     split = bid / ntiles;
     tile = bid % ntiles;
@@ -98,13 +100,13 @@ constexpr int kSgMFMA = 0x008, kSgVMEMR = 0x020, kSgDSR = 0x100;
 template <bool VEC>
 __global__ __launch_bounds__(kThreads) void syrk_f16_kernel(
     const _Float16* __restrict__ X, int64_t ldx, int64_t n, int d, int64_t ntiles,
-    int64_t nsplit, int64_t rps, float* __restrict__ part) {
+    int64_t nsplit, int64_t rps, float* __restrict__ part, const TileOrder ord) {
   __shared__ __attribute__((aligned(16))) _Float16 L0[kStageHalfs];
   __shared__ __attribute__((aligned(16))) _Float16 L1[kStageHalfs];
   __shared__ __attribute__((aligned(16))) _Float16 L2[kStageHalfs];
   __shared__ __attribute__((aligned(16))) _Float16 L3[kStageHalfs];
   int64_t tile, split;
-  wg_map(ntiles, nsplit, tile, split);
+  wg_map(ntiles, nsplit, ord, tile, split);
   int ti, tj;
   tile_of(tile, ti, tj);
   const int I0 = ti * kBT16, J0 = tj * kBT16;
@@ -274,10 +276,10 @@ constexpr int kBT32 = 128, kKS32 = 16, kP32 = kBT32 + 4;
 template <bool VEC>
 __global__ __launch_bounds__(kThreads) void syrk_f32_kernel(
     const float* __restrict__ X, int64_t ldx, int64_t n, int d, int64_t ntiles, int64_t nsplit,
-    int64_t rps, float* __restrict__ part) {
+    int64_t rps, float* __restrict__ part, const TileOrder ord) {
   __shared__ __attribute__((aligned(16))) float lds[2][kKS32 * kP32];
   int64_t tile, split;
-  wg_map(ntiles, nsplit, tile, split);
+  wg_map(ntiles, nsplit, ord, tile, split);
   int ti, tj;
   tile_of(tile, ti, tj);
   const bool diag = (ti == tj);
@@ -401,6 +403,53 @@ __global__ __launch_bounds__(kThreads) void syrk_reduce_kernel(
   }
 }
 
+// Per-XCD tile sets, greedily: each XCD in turn takes ntiles / 8 tiles, always
+// one that adds the fewest new column blocks to the blocks it already reads
+// (ties: the farthest tile first).  Fewer blocks per XCD = fewer L2 misses.
+// Depends on the tile count only; the last result is kept per host thread.
+void tile_order(int64_t T, int64_t ntiles, TileOrder& out) {
+  thread_local int64_t cached_T = -1;
+  thread_local TileOrder cached;
+  if (cached_T == T) {
+    out = cached;
+    return;
+  }
+  out.n = 0;
+  if (ntiles % 8 == 0 && ntiles <= TileOrder::kMax && ntiles > 8) {
+    const int64_t per = ntiles / 8;
+    std::vector<int> ti(ntiles), tj(ntiles);
+    for (int64_t j = 0, t = 0; j < T; ++j)
+      for (int64_t i = 0; i <= j; ++i, ++t) {
+        ti[t] = (int)i;
+        tj[t] = (int)j;
+      }
+    std::vector<char> used(ntiles, 0);
+    int64_t k = 0;
+    for (int x = 0; x < 8; ++x) {
+      std::vector<char> have(T, 0);
+      for (int64_t q = 0; q < per; ++q) {
+        int64_t best = -1;
+        int bkey = 1 << 30;
+        for (int64_t t = 0; t < ntiles; ++t) {
+          if (used[t]) continue;
+          const int add = !have[ti[t]] + (ti[t] != tj[t] && !have[tj[t]]);
+          const int key = add * (1 << 20) - tj[t] * 1024 - ti[t];
+          if (key < bkey) {
+            bkey = key;
+            best = t;
+          }
+        }
+        used[best] = 1;
+        have[ti[best]] = have[tj[best]] = 1;
+        out.id[k++] = (uint16_t)best;
+      }
+    }
+    out.n = (int)ntiles;
+  }
+  cached_T = T;
+  cached = out;
+}
+
 }  // namespace
 
 HessianPlan hessian_plan(int64_t d, int64_t n, int dtype) {
@@ -440,6 +489,7 @@ HessianPlan hessian_plan(int64_t d, int64_t n, int dtype) {
   p.rows_per_split = rps;
   p.nsplit = cdiv(n, rps);
   p.ws_bytes = (size_t)p.nsplit * (size_t)p.ntiles * (size_t)p.bt * (size_t)p.bt * sizeof(float);
+  tile_order(p.tiles_side, p.ntiles, p.order);
   return p;
 }
 
@@ -454,18 +504,18 @@ hipError_t hessian_launch(const HessianPlan& p, float* H, int64_t d, const void*
     const bool vec = fits && (d % 8 == 0) && (ldx % 8 == 0) && (((uintptr_t)X & 15) == 0);
     if (vec)
       hipLaunchKernelGGL(syrk_f16_kernel<true>, dim3((unsigned)grid), dim3(kThreads), 0, s,
-                         (const _Float16*)X, ldx, n, (int)d, p.ntiles, p.nsplit, p.rows_per_split, part);
+                         (const _Float16*)X, ldx, n, (int)d, p.ntiles, p.nsplit, p.rows_per_split, part, p.order);
     else
       hipLaunchKernelGGL(syrk_f16_kernel<false>, dim3((unsigned)grid), dim3(kThreads), 0, s,
-                         (const _Float16*)X, ldx, n, (int)d, p.ntiles, p.nsplit, p.rows_per_split, part);
+                         (const _Float16*)X, ldx, n, (int)d, p.ntiles, p.nsplit, p.rows_per_split, part, p.order);
   } else {
     const bool vec = (d % 4 == 0) && (ldx % 4 == 0) && (((uintptr_t)X & 15) == 0);
     if (vec)
       hipLaunchKernelGGL(syrk_f32_kernel<true>, dim3((unsigned)grid), dim3(kThreads), 0, s,
-                         (const float*)X, ldx, n, (int)d, p.ntiles, p.nsplit, p.rows_per_split, part);
+                         (const float*)X, ldx, n, (int)d, p.ntiles, p.nsplit, p.rows_per_split, part, p.order);
     else
       hipLaunchKernelGGL(syrk_f32_kernel<false>, dim3((unsigned)grid), dim3(kThreads), 0, s,
-                         (const float*)X, ldx, n, (int)d, p.ntiles, p.nsplit, p.rows_per_split, part);
+                         (const float*)X, ldx, n, (int)d, p.ntiles, p.nsplit, p.rows_per_split, part, p.order);
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
