@@ -378,7 +378,7 @@ struct PanelSmem {
 // Step k applied to column block c1 = k+1, then the stacked elimination of
 // [A[c1][c1]; A[r][c1]] (or [A[c1][c1]; I] for r == c1).
 // S0: L[c1][k], then Dm.   S1: L[r][k], then T (or I), then m_T.
-__device__ void task_panel(const StepArgs& a, int b, PanelSmem& sm) {
+__device__ __forceinline__ void task_panel(const StepArgs a, int b, PanelSmem& sm) {
   const int t = threadIdx.x, lane = t & 63, w = t >> 6, wm = w & 1, wn = w >> 1;
   const int64_t d = a.d;
   const int c1 = a.k + 1;
@@ -434,13 +434,14 @@ __device__ void task_panel(const StepArgs& a, int b, PanelSmem& sm) {
   }
   __syncthreads();
   if (own) {
-    // Lcc = W D^-1/2 (diagonal sqrt(d)), Lcc^-1 = (m_T D^1/2)^T
+    // Lcc^-1 = (m_T D^1/2)^T.  Lcc itself is not stored: nothing reads the
+    // diagonal blocks of L again, and the other panel work-groups of this launch
+    // may still be reading A[c1][c1] (with more of them than the GPU runs at
+    // once, late ones start after this one ends).
     double* Dk = a.Dinv + (int64_t)c1 * kNB * kNB;
     for (int idx = t; idx < kNB * kNB; idx += kThreads) {
       const int i = idx >> 6, c = idx & 63;
       Dk[idx] = (c <= i) ? sm.S1[c * kP + i] * sm.sq[i] : 0.0;
-      if (i < nbe && c <= i)
-        a.A[(C0 + i) * d + C0 + c] = (c < i) ? sm.S0[i * kP + c] * sm.rsq[c] : sm.sq[i];
     }
     if (t == 0 && sm.fail < nbe && *a.info == 0) *a.info = (int32_t)(d - (C0 + sm.fail));
     return;
@@ -456,7 +457,7 @@ struct TileSmem32 {
   float F0[kNB * kP], F1[kNB * kP];
 };
 
-__device__ void task_finish_inverse_row(const StepArgs& a, int j, TileSmem32& sm) {
+__device__ __forceinline__ void task_finish_inverse_row(const StepArgs a, int j, TileSmem32& sm) {
   const int t = threadIdx.x, lane = t & 63, w = t >> 6, wm = w & 1, wn = w >> 1;
   const int64_t d = a.d;
   const int k = a.k;
@@ -498,7 +499,7 @@ __device__ void task_finish_inverse_row(const StepArgs& a, int j, TileSmem32& sm
   }
 }
 
-__device__ void task_update_chol(const StepArgs& a, int b, PanelSmem& sm) {
+__device__ __forceinline__ void task_update_chol(const StepArgs a, int b, PanelSmem& sm) {
   const int t = threadIdx.x, lane = t & 63, w = t >> 6, wm = w & 1, wn = w >> 1;
   const int64_t d = a.d;
   int i = (int)((sqrt(8.0 * (double)b + 1.0) - 1.0) * 0.5);
@@ -535,7 +536,7 @@ __device__ void task_update_chol(const StepArgs& a, int b, PanelSmem& sm) {
       }
 }
 
-__device__ void task_update_inverse(const StepArgs& a, int b, TileSmem32& sm) {
+__device__ __forceinline__ void task_update_inverse(const StepArgs a, int b, TileSmem32& sm) {
   const int t = threadIdx.x, lane = t & 63, w = t >> 6, wm = w & 1, wn = w >> 1;
   const int64_t d = a.d;
   const int k = a.k;
