@@ -17,8 +17,9 @@
 //
 // Kernels: damp (lambda, info = 0) -> reversed fp64 copy with lambda on the
 // diagonal -> one launch per 64-column block (blocked right-looking Cholesky
-// with look-ahead, the triangular inverse fused into the same sweep) ->
-// reversed write of U.
+// with look-ahead; each diagonal block's inverse comes out of its
+// factorization) -> recursive-doubling triangular inverse, two batched fp32
+// MFMA products per level -> reversed write of U.
 #include "gptq_internal.h"
 
 namespace gptq {
@@ -73,27 +74,23 @@ __global__ __launch_bounds__(kThreads) void rev_copy_kernel(const float* __restr
 }
 
 // ---------------------------------------------------------------------------
-// One step of the blocked Cholesky (64-column blocks), with look-ahead and the
-// triangular inverse fused in.  Launch k (k = -1 .. nblk-1) runs four kinds of
-// independent work-groups; every input a work-group reads was finished by an
-// earlier launch, so no work-group ever waits on another:
+// One step of the blocked Cholesky (64-column blocks) with look-ahead.  Launch
+// k (k = -1 .. nblk-2) runs two kinds of independent work-groups; every input
+// a work-group reads was finished by an earlier launch, so no work-group ever
+// waits on another:
 //   P  (rows r = k+1 .. nblk-1): apply step k to column block c = k+1 (tile
 //      (r, c) and the diagonal tile (c, c)), factor the diagonal tile in LDS
 //      (each P work-group redundantly), and solve its own tile:
-//      L[r][c] = T Lcc^-T.  The r == c work-group writes Lcc and Lcc^-1.
-//   F  (row k, tiles j = 0 .. k): finish block row k of Linv = L^-1:
-//      Linv[k][k] = Lkk^-1, Linv[k][j] = -Lkk^-1 (S[k][j] + L[k][k-1] Linv[k-1][j]).
-//   UC (tiles (i, j), i >= j >= k+2): A[i][j] -= L[i][k] L[j][k]^T      (fp64 MFMA)
-//   UI (tiles (i, j), i >= k+1, j <= k-1): S[i][j] += L[i][k-1] Linv[k-1][j]
-//      (fp32 MFMA; S accumulates in the Linv buffer, first touch writes).
+//      L[r][c] = T Lcc^-T.  The r == c work-group writes Lcc^-1 as the
+//      diagonal block of L^-1 (Lcc itself is never needed again).
+//   UC (tiles (i, j), i >= j >= k+2): A[i][j] -= L[i][k] L[j][k]^T (fp64 MFMA)
 // ---------------------------------------------------------------------------
 struct StepArgs {
   double* A;
-  double* Dinv;
   float* Linv;
   int32_t* info;
   int d, nblk, k;
-  int np, nf, nuc, nui;
+  int np, nuc;
 };
 
 // C[m][n] (this wave's 32x32 quadrant) += sum_k SA[m][k] SB[n][k], fp64 MFMA
@@ -116,27 +113,11 @@ __device__ __forceinline__ void mma_nt_f64(const double* SA, const double* SB, f
   }
 }
 
-// C[m][n] (this wave's 32x32 quadrant) += sum_k SA[m][k] SB[k][n], fp32 MFMA
-__device__ __forceinline__ void mma_nn_f32(const float* SA, const float* SB, f32x16& acc, int lane,
-                                           int wm, int wn) {
-#pragma unroll 8
-  for (int kk = 0; kk < kNB / 2; ++kk) {
-    const int k = 2 * kk + (lane >> 5);
-    const float a = SA[(wm * 32 + (lane & 31)) * kP + k];
-    const float b = SB[k * kP + wn * 32 + (lane & 31)];
-    acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, acc, 0, 0, 0);
-  }
-}
-
-// tile coordinates held by acc[fm][fn][r] of mma_nt_f64 / acc[r] of mma_nn_f32
+// tile coordinates held by acc[fm][fn][r] of mma_nt_f64
 __device__ __forceinline__ int nt_row(int lane, int wm, int fm, int r) {
   return wm * 32 + fm * 16 + f64_row(lane, r);
 }
 __device__ __forceinline__ int nt_col(int lane, int wn, int fn) { return wn * 32 + fn * 16 + (lane & 15); }
-__device__ __forceinline__ int nn_row(int lane, int wm, int r) {
-  return wm * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-}
-__device__ __forceinline__ int nn_col(int lane, int wn) { return wn * 32 + (lane & 31); }
 
 __device__ __forceinline__ void zero_acc(f64x4 (&acc)[2][2]) {
 #pragma unroll
@@ -160,38 +141,6 @@ __device__ __forceinline__ void load_tile_f64(double* S, const double* __restric
   for (int u = 0; u < 16; ++u) {
     const int idx = t + u * kThreads;
     S[(idx >> 6) * kP + (idx & 63)] = v[u];
-  }
-}
-
-// same for an fp32 tile of Linv and an fp64 tile of L converted to fp32
-__device__ __forceinline__ void load_tile_f32(float* S, const float* __restrict__ A, int64_t d,
-                                              int64_t R0, int64_t C0, int t) {
-  float v[16];
-#pragma unroll
-  for (int u = 0; u < 16; ++u) {
-    const int idx = t + u * kThreads;
-    const int r = idx >> 6, c = idx & 63;
-    v[u] = (R0 + r < d && C0 + c < d) ? A[(R0 + r) * d + C0 + c] : 0.f;
-  }
-#pragma unroll
-  for (int u = 0; u < 16; ++u) {
-    const int idx = t + u * kThreads;
-    S[(idx >> 6) * kP + (idx & 63)] = v[u];
-  }
-}
-__device__ __forceinline__ void load_tile_f64_as_f32(float* S, const double* __restrict__ A,
-                                                     int64_t d, int64_t R0, int64_t C0, int t) {
-  double v[16];
-#pragma unroll
-  for (int u = 0; u < 16; ++u) {
-    const int idx = t + u * kThreads;
-    const int r = idx >> 6, c = idx & 63;
-    v[u] = (R0 + r < d && C0 + c < d) ? A[(R0 + r) * d + C0 + c] : 0.0;
-  }
-#pragma unroll
-  for (int u = 0; u < 16; ++u) {
-    const int idx = t + u * kThreads;
-    S[(idx >> 6) * kP + (idx & 63)] = (float)v[u];
   }
 }
 
@@ -379,6 +328,9 @@ struct PanelSmem {
 // [A[c1][c1]; A[r][c1]] (or [A[c1][c1]; I] for r == c1).
 // S0: L[c1][k], then Dm.   S1: L[r][k], then T (or I), then m_T.
 __device__ __forceinline__ void task_panel(const StepArgs a, int b, PanelSmem& sm) {
+  // the panel chain is the critical path of the whole factorization: its waves
+  // take issue priority over update work-groups sharing the CU
+  __builtin_amdgcn_s_setprio(3);
   const int t = threadIdx.x, lane = t & 63, w = t >> 6, wm = w & 1, wn = w >> 1;
   const int64_t d = a.d;
   const int c1 = a.k + 1;
@@ -434,14 +386,14 @@ __device__ __forceinline__ void task_panel(const StepArgs a, int b, PanelSmem& s
   }
   __syncthreads();
   if (own) {
-    // Lcc^-1 = (m_T D^1/2)^T.  Lcc itself is not stored: nothing reads the
-    // diagonal blocks of L again, and the other panel work-groups of this launch
-    // may still be reading A[c1][c1] (with more of them than the GPU runs at
-    // once, late ones start after this one ends).
-    double* Dk = a.Dinv + (int64_t)c1 * kNB * kNB;
+    // Lcc^-1 = (m_T D^1/2)^T, the diagonal block of L^-1.  Lcc itself is not
+    // stored: nothing reads the diagonal blocks of L again, and the other panel
+    // work-groups of this launch may still be reading A[c1][c1] (with more of
+    // them than the GPU runs at once, late ones start after this one ends).
     for (int idx = t; idx < kNB * kNB; idx += kThreads) {
       const int i = idx >> 6, c = idx & 63;
-      Dk[idx] = (c <= i) ? sm.S1[c * kP + i] * sm.sq[i] : 0.0;
+      if (C0 + i < d && C0 + c < d)
+        a.Linv[(C0 + i) * d + C0 + c] = (c <= i) ? (float)(sm.S1[c * kP + i] * sm.sq[i]) : 0.f;
     }
     if (t == 0 && sm.fail < nbe && *a.info == 0) *a.info = (int32_t)(d - (C0 + sm.fail));
     return;
@@ -450,52 +402,6 @@ __device__ __forceinline__ void task_panel(const StepArgs a, int b, PanelSmem& s
   for (int idx = t; idx < kNB * kNB; idx += kThreads) {
     const int i = idx >> 6, c = idx & 63;
     if (R0 + i < d && c < nbe) a.A[(R0 + i) * d + C0 + c] = sm.S1[i * kP + c] * sm.sq[c];
-  }
-}
-
-struct TileSmem32 {
-  float F0[kNB * kP], F1[kNB * kP];
-};
-
-__device__ __forceinline__ void task_finish_inverse_row(const StepArgs a, int j, TileSmem32& sm) {
-  const int t = threadIdx.x, lane = t & 63, w = t >> 6, wm = w & 1, wn = w >> 1;
-  const int64_t d = a.d;
-  const int k = a.k;
-  const int64_t R0 = (int64_t)k * kNB, J0 = (int64_t)j * kNB;
-  const double* Dk = a.Dinv + (int64_t)k * kNB * kNB;
-  if (j == k) {
-    for (int idx = t; idx < kNB * kNB; idx += kThreads) {
-      const int i = idx >> 6, c = idx & 63;
-      if (R0 + i < d && R0 + c < d) a.Linv[(R0 + i) * d + R0 + c] = (float)Dk[idx];
-    }
-    return;
-  }
-  // T = S[k][j] + L[k][k-1] Linv[k-1][j]
-  const int64_t P0 = (int64_t)(k - 1) * kNB;
-  f32x16 acc;
-#pragma unroll
-  for (int r = 0; r < 16; ++r) {
-    const int64_t rr = R0 + nn_row(lane, wm, r);
-    acc[r] = (j <= k - 2 && rr < d) ? a.Linv[rr * d + J0 + nn_col(lane, wn)] : 0.f;
-  }
-  load_tile_f64_as_f32(sm.F0, a.A, d, R0, P0, t);  // L[k][k-1]
-  load_tile_f32(sm.F1, a.Linv, d, P0, J0, t);      // Linv[k-1][j]
-  __syncthreads();
-  mma_nn_f32(sm.F0, sm.F1, acc, lane, wm, wn);
-  __syncthreads();
-#pragma unroll
-  for (int r = 0; r < 16; ++r) sm.F1[nn_row(lane, wm, r) * kP + nn_col(lane, wn)] = acc[r];
-  for (int idx = t; idx < kNB * kNB; idx += kThreads)
-    sm.F0[(idx >> 6) * kP + (idx & 63)] = (float)Dk[idx];
-  __syncthreads();
-  f32x16 out;
-#pragma unroll
-  for (int r = 0; r < 16; ++r) out[r] = 0.f;
-  mma_nn_f32(sm.F0, sm.F1, out, lane, wm, wn);
-#pragma unroll
-  for (int r = 0; r < 16; ++r) {
-    const int64_t rr = R0 + nn_row(lane, wm, r);
-    if (rr < d) a.Linv[rr * d + J0 + nn_col(lane, wn)] = -out[r];
   }
 }
 
@@ -536,52 +442,147 @@ __device__ __forceinline__ void task_update_chol(const StepArgs a, int b, PanelS
       }
 }
 
-__device__ __forceinline__ void task_update_inverse(const StepArgs a, int b, TileSmem32& sm) {
-  const int t = threadIdx.x, lane = t & 63, w = t >> 6, wm = w & 1, wn = w >> 1;
-  const int64_t d = a.d;
-  const int k = a.k;
-  const int i = k + 1 + b / k, j = b % k;
-  const int64_t R0 = (int64_t)i * kNB, J0 = (int64_t)j * kNB, P0 = (int64_t)(k - 1) * kNB;
-  f32x16 acc;
-  const bool first = (j == k - 1);
-#pragma unroll
-  for (int r = 0; r < 16; ++r) {
-    const int64_t rr = R0 + nn_row(lane, wm, r);
-    acc[r] = (!first && rr < d) ? a.Linv[rr * d + J0 + nn_col(lane, wn)] : 0.f;
-  }
-  load_tile_f64_as_f32(sm.F0, a.A, d, R0, P0, t);  // L[i][k-1]
-  load_tile_f32(sm.F1, a.Linv, d, P0, J0, t);      // Linv[k-1][j]
-  __syncthreads();
-  mma_nn_f32(sm.F0, sm.F1, acc, lane, wm, wn);
-#pragma unroll
-  for (int r = 0; r < 16; ++r) {
-    const int64_t rr = R0 + nn_row(lane, wm, r);
-    if (rr < d) a.Linv[rr * d + J0 + nn_col(lane, wn)] = acc[r];
-  }
-}
-
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) void chol_step_kernel(StepArgs a) {
-  __shared__ union Smem {
-    PanelSmem p;
-    TileSmem32 f;
-  } sm;
+  __shared__ PanelSmem sm;
   int b = blockIdx.x;
   if (b < a.np) {
-    task_panel(a, b, sm.p);
+    task_panel(a, b, sm);
     return;
   }
   b -= a.np;
-  if (b < a.nf) {
-    task_finish_inverse_row(a, b, sm.f);
-    return;
+  if (b < a.nuc) task_update_chol(a, b, sm);
+}
+
+// ---------------------------------------------------------------------------
+// Triangular inverse L^-1 by recursive doubling over the 64-blocks (fp32 MFMA).
+// A diagonal super-block [[A, 0], [B, C]] of L has the inverse
+//   [[A^-1, 0], [-C^-1 B A^-1, C^-1]].
+// Level sb (sb = 1, 2, 4, ... blocks) pairs A = blocks [2 p sb, 2 p sb + sb)
+// with C = the next sb blocks (clipped at the end of the matrix).  With A^-1
+// and C^-1 from the levels below it runs two batched products:
+//   mode 0:  T = B A^-1   (B = L[C][A], the fp64 factor rounded to fp32; A^-1
+//                          is lower triangular, so output block column j sums
+//                          k = j .. sb-1)
+//   mode 1:  X = -C^-1 T  (C^-1 lower: output block row i sums k = 0 .. i)
+// X is L^-1[C][A]; T goes to a scratch buffer.  The one block that may stop
+// short of d (the last) can only sit in a C range -- an A range there has no C
+// and is skipped -- so masking rows and columns >= d of C is enough.
+// ---------------------------------------------------------------------------
+struct TriArgs {
+  const double* L;  // fp64 factor, ld d (off-diagonal blocks)
+  float* Linv;      // ld d
+  float* Tw;        // scratch: pair p at p (64 sb)^2, ld 64 sb
+  int64_t d;
+  int nblk, sb, npairs;
+};
+
+constexpr int kTPa = kNB + 1;   // LDS pitch of the [m][k] operand tile
+constexpr int kTPb = kNB + 32;  // LDS pitch of the [k][n] operand tile (the two k rows of one read use disjoint banks)
+
+template <int MODE, bool VEC>
+__global__ __launch_bounds__(kThreads) void tri_gemm_kernel(TriArgs a) {
+  __shared__ float SA[kNB * kTPa];
+  __shared__ __attribute__((aligned(16))) float SB[kNB * kTPb];
+  const int sb = a.sb, np = a.npairs;
+  // longest K ranges first: mode 0 by block column, mode 1 by block row (descending)
+  const int outer = blockIdx.x / (np * sb), rem = blockIdx.x % (np * sb);
+  const int p = rem / sb, q = rem % sb;
+  const int bi = (MODE == 0) ? q : sb - 1 - outer;
+  const int bj = (MODE == 0) ? outer : q;
+  const int A0 = 2 * p * sb, C0 = A0 + sb;
+  const int nC = min(sb, a.nblk - C0);
+  if (bi >= nC) return;
+  const int64_t d = a.d;
+  const int64_t ldt = (int64_t)kNB * sb;
+  float* Tp = a.Tw + (int64_t)p * ldt * ldt;
+  const int kb0 = (MODE == 0) ? bj : 0, kb1 = (MODE == 0) ? sb : bi + 1;
+  const int t = threadIdx.x, lane = t & 63, w = t >> 6, wm = w & 1, wn = w >> 1;
+  // staging: thread t covers tile row t / 4, 16 columns from (t % 4) * 16
+  const int sr = t >> 2, sc = (t & 3) * 16;
+  const int64_t arow = (int64_t)(C0 + bi) * kNB + sr;
+  float ra[16], rb[16];
+  auto gload = [&](int kb) {
+    if (MODE == 0) {
+      // A operand: L[C0+bi][A0+kb] (fp64; its columns lie in the A range, < d)
+      const double* src = a.L + arow * d + (int64_t)(A0 + kb) * kNB + sc;
+#pragma unroll
+      for (int e = 0; e < 16; e += 2) {
+        if (VEC) {
+          const double2 v = (arow < d) ? *(const double2*)(src + e) : double2{0.0, 0.0};
+          ra[e] = (float)v.x;
+          ra[e + 1] = (float)v.y;
+        } else {
+          ra[e] = (arow < d) ? (float)src[e] : 0.f;
+          ra[e + 1] = (arow < d) ? (float)src[e + 1] : 0.f;
+        }
+      }
+      // B operand: L^-1[A0+kb][A0+bj] (inside the A range)
+      const float* bsrc = a.Linv + ((int64_t)(A0 + kb) * kNB + sr) * d + (int64_t)(A0 + bj) * kNB + sc;
+#pragma unroll
+      for (int e = 0; e < 16; e += 4) {
+        if (VEC) {
+          const f32x4 v = *(const f32x4*)(bsrc + e);
+          rb[e] = v[0]; rb[e + 1] = v[1]; rb[e + 2] = v[2]; rb[e + 3] = v[3];
+        } else {
+#pragma unroll
+          for (int u = 0; u < 4; ++u) rb[e + u] = bsrc[e + u];
+        }
+      }
+    } else {
+      // A operand: L^-1[C0+bi][C0+kb] (rows and columns may pass d in the last block)
+      const int64_t col = (int64_t)(C0 + kb) * kNB + sc;
+      const float* src = a.Linv + arow * d + col;
+#pragma unroll
+      for (int e = 0; e < 16; e += 4) {
+        if (VEC && arow < d && col + e + 3 < d) {
+          const f32x4 v = *(const f32x4*)(src + e);
+          ra[e] = v[0]; ra[e + 1] = v[1]; ra[e + 2] = v[2]; ra[e + 3] = v[3];
+        } else {
+#pragma unroll
+          for (int u = 0; u < 4; ++u) ra[e + u] = (arow < d && col + e + u < d) ? src[e + u] : 0.f;
+        }
+      }
+      // B operand: T[kb][bj] of this pair (always inside the scratch)
+      const float* bsrc = Tp + ((int64_t)kb * kNB + sr) * ldt + (int64_t)bj * kNB + sc;
+#pragma unroll
+      for (int e = 0; e < 16; e += 4) {
+        const f32x4 v = *(const f32x4*)(bsrc + e);
+        rb[e] = v[0]; rb[e + 1] = v[1]; rb[e + 2] = v[2]; rb[e + 3] = v[3];
+      }
+    }
+  };
+  f32x16 acc;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) acc[r] = 0.f;
+  gload(kb0);
+  for (int kb = kb0; kb < kb1; ++kb) {
+    __syncthreads();
+#pragma unroll
+    for (int e = 0; e < 16; ++e) SA[sr * kTPa + sc + e] = ra[e];
+#pragma unroll
+    for (int e = 0; e < 16; e += 4)
+      *(f32x4*)&SB[sr * kTPb + sc + e] = f32x4{rb[e], rb[e + 1], rb[e + 2], rb[e + 3]};
+    __syncthreads();
+    if (kb + 1 < kb1) gload(kb + 1);
+#pragma unroll 8
+    for (int kk = 0; kk < kNB / 2; ++kk) {
+      const int k = 2 * kk + (lane >> 5);
+      const float av = SA[(wm * 32 + (lane & 31)) * kTPa + k];
+      const float bv = SB[k * kTPb + wn * 32 + (lane & 31)];
+      acc = __builtin_amdgcn_mfma_f32_32x32x2f32(av, bv, acc, 0, 0, 0);
+    }
   }
-  b -= a.nf;
-  if (b < a.nuc) {
-    task_update_chol(a, b, sm.p);
-    return;
+  // v_mfma_f32_32x32x2f32 output: lane l, register r holds D[8 (r / 4) + 4 (l / 32) + r % 4][l % 32]
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    const int row = wm * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3), col = wn * 32 + (lane & 31);
+    if (MODE == 0) {
+      Tp[((int64_t)bi * kNB + row) * ldt + (int64_t)bj * kNB + col] = acc[r];
+    } else {
+      const int64_t grow = (int64_t)(C0 + bi) * kNB + row;
+      if (grow < d) a.Linv[grow * d + (int64_t)(A0 + bj) * kNB + col] = -acc[r];
+    }
   }
-  b -= a.nuc;
-  if (b < a.nui) task_update_inverse(a, b, sm.f);
 }
 
 // U[i][j] = Linv[d-1-i][d-1-j] for j >= i, else 0
@@ -599,17 +600,28 @@ __global__ __launch_bounds__(kThreads) void rev_out_kernel(const float* __restri
 
 }  // namespace
 
+// pairs of level sb of the recursive inverse (those whose C range is not empty)
+static int64_t tri_pairs(int64_t nblk, int64_t sb) { return (nblk > sb) ? cdiv(nblk - sb, 2 * sb) : 0; }
+
 FactorPlan factor_plan(int64_t d) {
   FactorPlan p{};
   p.d = d;
   p.nb = kNB;
   p.nblk = cdiv(d, kNB);
+  // scratch for T: pair p at p (64 sb)^2; the last pair holds only its nC block rows
+  size_t tw = 0;
+  for (int64_t sb = 1; sb < p.nblk; sb *= 2) {
+    const int64_t np = tri_pairs(p.nblk, sb);
+    const int64_t nc_last = std::min<int64_t>(sb, p.nblk - ((np - 1) * 2 * sb + sb));
+    const size_t e = (size_t)kNB * (size_t)sb;
+    tw = std::max(tw, (size_t)(np - 1) * e * e + (size_t)nc_last * kNB * e);
+  }
   size_t off = 0;
   p.off_a64 = off;
   off = align_up(off + (size_t)d * d * sizeof(double), 256);
-  p.off_dinv = off;
-  off = align_up(off + (size_t)p.nblk * kNB * kNB * sizeof(double), 256);
-  p.off_tmp = off;  // Linv = L^-1 (d*d fp32; its lower tiles first hold partial sums)
+  p.off_tw = off;
+  off = align_up(off + tw * sizeof(float), 256);
+  p.off_tmp = off;  // L^-1 (d*d fp32)
   off = align_up(off + (size_t)d * d * sizeof(float), 256);
   p.off_lam = off;
   off = align_up(off + 64, 256);
@@ -622,7 +634,7 @@ hipError_t factor_launch(const FactorPlan& p, const float* H, float percdamp, fl
   const int64_t d = p.d;
   char* base = (char*)ws;
   double* A = (double*)(base + p.off_a64);
-  double* Dinv = (double*)(base + p.off_dinv);
+  float* Tw = (float*)(base + p.off_tw);
   float* Linv = (float*)(base + p.off_tmp);
   double* lam = (double*)(base + p.off_lam);
   hipError_t e;
@@ -631,22 +643,31 @@ hipError_t factor_launch(const FactorPlan& p, const float* H, float percdamp, fl
   hipLaunchKernelGGL(rev_copy_kernel, dim3(nt, nt), dim3(kThreads), 0, s, H, d, lam, A);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   const int nblk = (int)p.nblk;
-  for (int k = -1; k < nblk; ++k) {
+  for (int k = -1; k < nblk - 1; ++k) {
     StepArgs a{};
     a.A = A;
-    a.Dinv = Dinv;
     a.Linv = Linv;
     a.info = info;
     a.d = (int)d;
     a.nblk = nblk;
     a.k = k;
-    a.np = (k + 1 < nblk) ? nblk - (k + 1) : 0;
-    a.nf = (k >= 0) ? k + 1 : 0;
+    a.np = nblk - (k + 1);
     const int m = nblk - k - 2;
     a.nuc = (k >= 0 && m > 0) ? m * (m + 1) / 2 : 0;
-    a.nui = (k >= 1) ? (nblk - k - 1) * k : 0;
-    const int total = a.np + a.nf + a.nuc + a.nui;
-    if (total > 0) hipLaunchKernelGGL(chol_step_kernel, dim3((unsigned)total), dim3(kThreads), 0, s, a);
+    hipLaunchKernelGGL(chol_step_kernel, dim3((unsigned)(a.np + a.nuc)), dim3(kThreads), 0, s, a);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
+  const bool vec = (d % 4) == 0;
+  for (int64_t sb = 1; sb < p.nblk; sb *= 2) {
+    TriArgs t{A, Linv, Tw, d, nblk, (int)sb, (int)tri_pairs(p.nblk, sb)};
+    const dim3 grid((unsigned)(t.npairs * sb * sb));
+    if (vec) {
+      hipLaunchKernelGGL((tri_gemm_kernel<0, true>), grid, dim3(kThreads), 0, s, t);
+      hipLaunchKernelGGL((tri_gemm_kernel<1, true>), grid, dim3(kThreads), 0, s, t);
+    } else {
+      hipLaunchKernelGGL((tri_gemm_kernel<0, false>), grid, dim3(kThreads), 0, s, t);
+      hipLaunchKernelGGL((tri_gemm_kernel<1, false>), grid, dim3(kThreads), 0, s, t);
+    }
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   hipLaunchKernelGGL(rev_out_kernel, dim3(nt, nt), dim3(kThreads), 0, s, Linv, d, U);

@@ -14,6 +14,7 @@ typedef _Float16 half8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef double f64x4 __attribute__((ext_vector_type(4)));
+typedef double f64x2 __attribute__((ext_vector_type(2)));
 
 inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
@@ -46,7 +47,7 @@ struct FactorPlan {
   int64_t d;
   int nb;                 // Cholesky block
   int64_t nblk;
-  size_t off_a64, off_dinv, off_tmp, off_lam, ws_bytes;
+  size_t off_a64, off_tw, off_tmp, off_lam, ws_bytes;
 };
 FactorPlan factor_plan(int64_t d);
 hipError_t factor_launch(const FactorPlan& p, const float* H, float percdamp, float* U,
