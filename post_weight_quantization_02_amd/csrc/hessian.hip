@@ -385,12 +385,34 @@ __global__ __launch_bounds__(kThreads) void syrk_reduce_kernel(
   const int t = threadIdx.x;
   const int col = t & 63;
   const int64_t tsz = (int64_t)bt * bt;
+  // 16 rows per thread; four splits' loads in flight per round trip, added in
+  // split order
+  const float* p0 = part + tile * tsz + (int64_t)(sa * 64 + (t >> 6)) * bt + sc * 64 + col;
+  const int64_t sstride = ntiles * tsz;
+  float acc[16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) acc[i] = 0.f;
+  int64_t sp = 0;
+  for (; sp + 4 <= nsplit; sp += 4) {
+    float x[4][16];
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) x[j][i] = p0[(sp + j) * sstride + (int64_t)(4 * i) * bt];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) acc[i] = (((acc[i] + x[0][i]) + x[1][i]) + x[2][i]) + x[3][i];
+  }
+  for (; sp < nsplit; ++sp) {
+    float x[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) x[i] = p0[sp * sstride + (int64_t)(4 * i) * bt];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) acc[i] += x[i];
+  }
+#pragma unroll
   for (int i = 0; i < 16; ++i) {
     const int row = (t >> 6) + 4 * i;
-    const float* p = part + tile * tsz + (int64_t)(sa * 64 + row) * bt + sc * 64 + col;
-    float s = 0.f;
-    for (int64_t sp = 0; sp < nsplit; ++sp) s += p[sp * ntiles * tsz];
-    s *= 2.f;
+    const float s = 2.f * acc[i];
     if (R0 + row < d && C0 + col < d && (!subdiag || row <= col)) H[(R0 + row) * d + C0 + col] += s;
     tr[row][col] = s;
   }
