@@ -136,25 +136,63 @@ __global__ __launch_bounds__(kThreads) void panel_kernel(
   __shared__ double red[kThreads / 64];
   const int t = threadIdx.x;
   const size_t ldu = (size_t)d_col;
-  // stage U's diagonal block (upper part) in LDS; all global loads are issued
-  // before the LDS stores
-  constexpr int kPer = B * B / kThreads;
-  constexpr int kBatch = kPer < 32 ? kPer : 32;
+  // stage U's diagonal block in LDS.  Full blocks of 64 or 128 columns: whole
+  // rows by direct-to-LDS buffer loads in two parts, the first kRows0 rows
+  // waited for before the column loop, the rest at column kRows0 - kPF (just
+  // before the prefetch reaches them); entries left of the diagonal are read
+  // too but only ever update columns already quantized.  Otherwise: the upper
+  // part through registers, with zeros outside it.
+  constexpr bool kDma = FULL && (B == 64 || B == 128);
+  constexpr int kPF = 4;
+  constexpr int kRowsPerLoad = 256 / B;                 // rows per 64-lane 16-byte load
+  constexpr int kLoads = B / kRowsPerLoad;              // loads for the whole block
+  constexpr int kRows0 = 32;                            // rows of the first part
+  constexpr int kLoads0 = kRows0 / kRowsPerLoad;
+  static_assert(!kDma || (kLoads0 % 4 == 0 && kLoads % 4 == 0), "loads per wave");
   const float udg = (t < width) ? U[(size_t)(i1 + t) * ldu + i1 + t] : 1.f;
+  if constexpr (kDma) {
+    const int w4 = __builtin_amdgcn_readfirstlane(t >> 6), l = t & 63;
+    const float* ubase = U + (size_t)i1 * ldu + i1;
+    const uint64_t ba = (uint64_t)(uintptr_t)ubase;
+    const float* ubu = (const float*)(uintptr_t)(((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(ba >> 32)) << 32) |
+                                                 (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)ba));
+    const __amdgpu_buffer_rsrc_t ur = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)ubu, (short)0, (int)((((int64_t)B - 1) * (int64_t)ldu + B) * 4), 0x00020000);
+    constexpr int kLanesPerRow = B / 4;
+    const uint32_t vo = (uint32_t)(((l / kLanesPerRow) * ldu + (l % kLanesPerRow) * 4) * 4);
 #pragma unroll
-  for (int u0 = 0; u0 < kPer; u0 += kBatch) {
-    float ub[kBatch];
-#pragma unroll
-    for (int u = 0; u < kBatch; ++u) {
-      const int idx = t + (u0 + u) * kThreads;
-      const int r = idx / B, c = idx % B;
-      ub[u] = (r < width && c < width && c >= r) ? U[(size_t)(i1 + r) * ldu + i1 + c] : 0.f;
+    for (int i = 0; i < kLoads / 4; ++i) {
+      const int q = w4 + 4 * i;  // load q fills rows q * kRowsPerLoad ..
+      const int so = __builtin_amdgcn_readfirstlane((int)((uint32_t)(q * kRowsPerLoad) * (uint32_t)ldu * 4u));
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(ur, (void __attribute__((address_space(3)))*)(Us + q * kRowsPerLoad * B),
+                                               16, vo, so, 0, 0);
     }
+    if (t < B) rd[t] = (t < width) ? 1.0f / udg : 0.f;
+    // this wave's first-part loads are its first kLoads0 / 4; the rest may still be in flight
+    if constexpr (kLoads / 4 - kLoads0 / 4 == 12)
+      asm volatile("s_waitcnt vmcnt(12)\n\ts_barrier" ::: "memory");
+    else if constexpr (kLoads / 4 - kLoads0 / 4 == 2)
+      asm volatile("s_waitcnt vmcnt(2)\n\ts_barrier" ::: "memory");
+    else
+      asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
+  } else {
+    constexpr int kPer = B * B / kThreads;
+    constexpr int kBatch = kPer < 32 ? kPer : 32;
 #pragma unroll
-    for (int u = 0; u < kBatch; ++u) Us[t + (u0 + u) * kThreads] = ub[u];
+    for (int u0 = 0; u0 < kPer; u0 += kBatch) {
+      float ub[kBatch];
+#pragma unroll
+      for (int u = 0; u < kBatch; ++u) {
+        const int idx = t + (u0 + u) * kThreads;
+        const int r = idx / B, c = idx % B;
+        ub[u] = (r < width && c < width && c >= r) ? U[(size_t)(i1 + r) * ldu + i1 + c] : 0.f;
+      }
+#pragma unroll
+      for (int u = 0; u < kBatch; ++u) Us[t + (u0 + u) * kThreads] = ub[u];
+    }
+    if (t < B) rd[t] = (t < width) ? 1.0f / udg : 0.f;
+    __syncthreads();
   }
-  if (t < B) rd[t] = (t < width) ? 1.0f / udg : 0.f;
-  __syncthreads();
 
   const int lane = t & 63, p = lane & 15;
   const int row = blockIdx.x * 16 + (t >> 6) * 4 + (lane >> 4);
@@ -177,12 +215,14 @@ __global__ __launch_bounds__(kThreads) void panel_kernel(
   }
   float rs = 1.f / s;
   const float fmaxq = (float)maxq;
+  // c - z = clamp(round(x / s), -z, maxq - z), exact on integer-valued floats
+  float nz = -z, mz = fmaxq - z;
   // 1 / U[j][j] for this lane's own columns (only the owner's error is used)
   float rdl[CPL];
 #pragma unroll
   for (int r = 0; r < CPL; ++r) rdl[r] = rd[p * CPL + r];
   // U rows of the block, this lane's CPL columns, prefetched kPF columns ahead
-  constexpr int kPF = 4, kQ = (CPL + 3) / 4;
+  constexpr int kQ = (CPL + 3) / 4;
   f32x4 ub[kPF][kQ];
   auto uload = [&](int j, f32x4* dst) {
     if constexpr (CPL >= 4) {
@@ -220,15 +260,20 @@ __global__ __launch_bounds__(kThreads) void panel_kernel(
           }
           grid_from_minmax(mn, mx, maxq, s, z);
           rs = 1.f / s;
+          nz = -z;
+          mz = fmaxq - z;
           if (p == 0 && valid) {
             const int gi = (i1 + j) / GIN;
             scales[rowc * ngroups + gi] = s;
             zeros[rowc * ngroups + gi] = (int32_t)z;
           }
         }
+        if constexpr (kDma && kRows0 < B && j == kRows0 - kPF)
+          asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
         const float x = w[jj];
-        const float c = fminf(fmaxf(rintf(x * rs) + z, 0.f), fmaxq);
-        const float e = (x - s * (c - z)) * rdl[jj];
+        const float cz = __builtin_amdgcn_fmed3f(rintf(x * rs), nz, mz);
+        const float e = fmaf(-s, cz, x) * rdl[jj];
+        const float c = cz + z;
         const bool own = (p == kk);
         cr[jj] = own ? c : cr[jj];
         er[jj] = own ? e : er[jj];
