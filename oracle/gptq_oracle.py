@@ -284,6 +284,64 @@ def _replay_zero(z, v, replay_zeros, gi, tol):
 
 
 # ---------------------------------------------------------------------------
+# act-order (wiki "실무 변형": an option of later implementations quantizes the
+# columns with the largest Hessian diagonal -- the largest input activations --
+# first; with groups it needs a column-to-group map at inference)
+# ---------------------------------------------------------------------------
+
+def act_order_perm(H: np.ndarray) -> np.ndarray:
+    """Quantization order: position i takes original column perm[i].
+
+    Columns by descending diag(H), compared in H's own precision; equal
+    diagonals keep ascending column index (a stable sort), and a NaN diagonal
+    counts as -inf.  (Readings: the pages name the criterion only.)
+    """
+    dg = np.array(np.diag(np.asarray(H)), copy=True)
+    dg[np.isnan(dg)] = -np.inf
+    return np.argsort(-dg, kind="stable")
+
+
+@dataclasses.dataclass
+class ActOrderResult:
+    perm: np.ndarray         # int64 [d_col]: position i quantizes original column perm[i]
+    g_idx: np.ndarray        # int64 [d_col]: group of original column j
+    codes: np.ndarray        # uint8 [d_row x d_col], original column order
+    scales: np.ndarray       # fp64 [d_row x n_groups], groups of consecutive positions
+    zeros: np.ndarray        # int64 [d_row x n_groups]
+    w_hat: np.ndarray        # fp64 [d_row x d_col], original column order
+    err_sq_sum: float
+    in_order: GPTQResult     # the loop's own result, in quantization order
+
+
+def gptq_quantize_act_order(W0: np.ndarray, U_perm: np.ndarray, perm: np.ndarray, bits: int,
+                            group_size: int = 0, block_size: int = 128,
+                            replay_codes: Optional[np.ndarray] = None,
+                            replay_zeros: Optional[np.ndarray] = None,
+                            replay_tol: float = 1e-3) -> ActOrderResult:
+    """The lazy-batch loop over the columns in the order ``perm``.
+
+    U_perm is the factor of the Hessian with rows and columns in that order
+    (H[perm][:, perm]).  Groups are runs of ``group_size`` consecutive
+    positions of the quantization order (their parameters come from the
+    then-current weights as in natural order), so original column j belongs to
+    group g_idx[j] = (position of j) // group_size.  ``replay_codes`` is in the
+    original column order; ``replay_zeros`` per group as returned.
+    """
+    perm = np.asarray(perm, dtype=np.int64)
+    d_col = W0.shape[1]
+    if sorted(perm.tolist()) != list(range(d_col)):
+        raise ValueError("perm is not a permutation of the columns")
+    inv = np.empty_like(perm)
+    inv[perm] = np.arange(d_col)
+    rc = None if replay_codes is None else np.asarray(replay_codes)[:, perm]
+    res = gptq_quantize(np.asarray(W0)[:, perm], U_perm, bits, group_size, block_size,
+                        replay_codes=rc, replay_zeros=replay_zeros, replay_tol=replay_tol)
+    g = group_size if group_size else d_col
+    return ActOrderResult(perm, inv // g, res.codes[:, inv], res.scales, res.zeros,
+                          res.w_hat[:, inv], res.err_sq_sum, res)
+
+
+# ---------------------------------------------------------------------------
 # output error (wiki "문제 설정": ||W X - What X||^2)
 # ---------------------------------------------------------------------------
 
@@ -407,4 +465,21 @@ def solve_layer(W0: np.ndarray, x_chunks: Iterable[np.ndarray], bits: int,
     H_lam, lam = damp(H, percdamp)
     U = inv_hessian_factor(H_lam)
     res = gptq_quantize(W0, U, bits, group_size, block_size)
+    return LayerSolution(H, lam, U, res, output_error(W0, res.w_hat, H))
+
+
+def solve_layer_act_order(W0: np.ndarray, x_chunks: Iterable[np.ndarray], bits: int,
+                          group_size: int = 0, block_size: int = 128,
+                          percdamp: float = 0.01) -> LayerSolution:
+    """As solve_layer, quantizing the columns in act-order.
+
+    H -> order by its diagonal -> damping of H[perm][:, perm] -> its factor ->
+    the loop in that order -> error against W0 with the undamped H (an order-free
+    quantity).  ``result`` is an ActOrderResult.
+    """
+    H = hessian(x_chunks, W0.shape[1])
+    perm = act_order_perm(H)
+    H_lam, lam = damp(H[np.ix_(perm, perm)], percdamp)
+    U = inv_hessian_factor(H_lam)
+    res = gptq_quantize_act_order(W0, U, perm, bits, group_size, block_size)
     return LayerSolution(H, lam, U, res, output_error(W0, res.w_hat, H))
