@@ -6,7 +6,9 @@ already resident in HBM: H := 0; H += 2 X^T X over all calibration rows;
 damping + U; the lazy-batch loop with the output error.  Workload: a
 4096 x 4096 fp16 attention projection, X = 262144 x 4096 fp16 (rank-64
 covariance, 1% outlier channels at 20x), 4-bit asymmetric grid, group 128,
-block 128, 1% damping.
+block 128, 1% damping.  With --act-order the same layer is quantized with the
+columns in descending-diagonal order (order from the GPU's H, then the
+reordered factor and loop), as a separate measurement.
 
 Prints one JSON line.  The metric is seconds per layer (lower is better), with
 per-stage TFLOP/s and the dominant kernel's roofline fraction.  The CPU
@@ -37,6 +39,8 @@ def parse():
     ap.add_argument("--steps", type=int, default=5)
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--act-order", action="store_true",
+                    help="quantize the columns in act-order (descending Hessian diagonal)")
     ap.add_argument("--traffic", default=os.path.join(ROOT, "profiles", "syrk_f16_attn4096_traffic.json"),
                     help="rocprofv3 --pmc derived HBM bytes of the dominant kernel (JSON), if any")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
@@ -49,7 +53,7 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def cpu_baseline(spec, W, X_chunk0):
+def cpu_baseline(spec, W, X_chunk0, act_order=False):
     """The fp64 oracle on a bounded sample of the same layer, scaled to one layer."""
     import numpy as np
     import oracle as O
@@ -63,12 +67,20 @@ def cpu_baseline(spec, W, X_chunk0):
     H = O.hessian([X_chunk0])
     t_h = (time.perf_counter() - t0) * n_chunks
     t0 = time.perf_counter()
-    Hl, lam = O.damp(H * n_chunks, spec.percdamp)
+    if act_order:
+        perm = O.act_order_perm(H)
+        Hl, lam = O.damp((H * n_chunks)[np.ix_(perm, perm)], spec.percdamp)
+    else:
+        Hl, lam = O.damp(H * n_chunks, spec.percdamp)
     U = O.inv_hessian_factor(Hl)
     t_f = time.perf_counter() - t0
     rows = 256
     t0 = time.perf_counter()
-    O.gptq_quantize(W[:rows].astype(np.float64), U, spec.bits, spec.group_size, spec.block_size)
+    if act_order:
+        O.gptq_quantize_act_order(W[:rows].astype(np.float64), U, perm, spec.bits, spec.group_size,
+                                  spec.block_size)
+    else:
+        O.gptq_quantize(W[:rows].astype(np.float64), U, spec.bits, spec.group_size, spec.block_size)
     t_q = (time.perf_counter() - t0) * (spec.d_row / rows)
     total = t_h + t_f + t_q
     return {"value": total, "unit": "s/layer", "cores": int(threads), "kind": "oracle",
@@ -126,6 +138,8 @@ def main():
     scales = torch.empty(dr, ng, dtype=torch.float32, device=dev)
     zeros = torch.empty(dr, ng, dtype=torch.int32, device=dev)
     err = torch.empty(1, dtype=torch.float64, device=dev)
+    perm = torch.empty(d, dtype=torch.int32, device=dev)
+    g_idx = torch.empty(d, dtype=torch.int32, device=dev)
     ws_h = torch.empty(G.gptq_hessian_accumulate_workspace_size(d, n, G.GPTQ_F16), dtype=torch.uint8, device=dev)
     ws_f = torch.empty(G.gptq_prepare_hinv_workspace_size(d), dtype=torch.uint8, device=dev)
     ws_q = torch.empty(G.gptq_quantize_layer_workspace_size(dr, d, spec.block_size), dtype=torch.uint8, device=dev)
@@ -138,11 +152,19 @@ def main():
         G.gptq_hessian_accumulate(H, Xd, ws=ws_h, stream=stream)
         if ev:
             ev[1].record(stream)
-        G.gptq_prepare_hinv(H, spec.percdamp, U, lam, info, ws=ws_f, stream=stream)
+        if args.act_order:
+            G.gptq_act_order_perm(H, perm, stream=stream)
+            G.gptq_prepare_hinv_perm(H, perm, spec.percdamp, U, lam, info, ws=ws_f, stream=stream)
+        else:
+            G.gptq_prepare_hinv(H, spec.percdamp, U, lam, info, ws=ws_f, stream=stream)
         if ev:
             ev[2].record(stream)
-        G.gptq_quantize_layer(Wd, U, lam, spec.bits, spec.group_size, spec.block_size, codes, scales,
-                              zeros, err, ws=ws_q, stream=stream)
+        if args.act_order:
+            G.gptq_quantize_layer_perm(Wd, U, lam, perm, spec.bits, spec.group_size, spec.block_size,
+                                       codes, scales, zeros, g_idx, err, ws=ws_q, stream=stream)
+        else:
+            G.gptq_quantize_layer(Wd, U, lam, spec.bits, spec.group_size, spec.block_size, codes,
+                                  scales, zeros, err, ws=ws_q, stream=stream)
         if ev:
             ev[3].record(stream)
 
@@ -195,7 +217,9 @@ def main():
         "dtype": "f16-mfma(f32 acc) syrk / f64 Cholesky / f32 loop",
         "data": "synthetic",
         "config": {"workload": "attn_4096: W 4096x4096 fp16, X 262144x4096 fp16 rank-64 + 1% 20x outliers, "
-                               "4-bit asymmetric, group 128, block 128, 1% damping",
+                               "4-bit asymmetric, group 128, block 128, 1% damping"
+                               + (", act-order" if args.act_order else ""),
+                   "act_order": bool(args.act_order),
                    "d_row": dr, "d_col": d, "n_rows": n, "bits": spec.bits,
                    "group_size": spec.group_size, "block_size": spec.block_size,
                    "parallelism": "single-gpu"},
@@ -210,7 +234,7 @@ def main():
     }
     if not args.no_cpu_baseline:
         log("bench: timing the fp64 oracle on a bounded sample (CPU)")
-        cb = cpu_baseline(spec, W, x0)
+        cb = cpu_baseline(spec, W, x0, args.act_order)
         out["cpu_baseline"] = cb
         out["gpu_speedup_vs_cpu_oracle"] = round(cb["value"] / per_step, 1)
     print(json.dumps(out), flush=True)

@@ -158,6 +158,49 @@ gptq_status gptq_quantize_layer(const void* W0, int32_t w_dtype, int64_t d_row, 
                                 size_t ws_bytes, void* stream);
 size_t gptq_quantize_layer_workspace_size(int64_t d_row, int64_t d_col, int64_t block_size);
 
+/*
+ * Act-order (itwiki "GPTQ", section "실무 변형" (practical variants): an option of
+ * later implementations quantizes the columns with the largest Hessian
+ * diagonal -- the largest input activations -- first; combined with groups it
+ * needs a column-to-group map).  Three calls mirror the natural-order ones:
+ *
+ * gptq_act_order_perm: the quantization order.
+ *   H      [device] float [d_col x d_col] (only the diagonal is read).
+ *   perm   [device] int32 [d_col] output: position i quantizes original column
+ *          perm[i].  Columns by descending diag(H) compared as fp32; equal
+ *          diagonals keep ascending column index; a NaN diagonal counts as
+ *          -inf.  Always a permutation of 0 .. d_col-1.  Needs no workspace.
+ *
+ * gptq_prepare_hinv_perm: as gptq_prepare_hinv for the Hessian with rows and
+ *   columns in that order, Hp[a][b] = H[perm[a]][perm[b]] (H is not modified
+ *   and not copied).  U is the factor of the damped Hp, in the quantization
+ *   order; info's pivot index counts positions of that order.  lambda is the
+ *   same as for H.  perm [device] int32 [d_col], a permutation of
+ *   0 .. d_col-1 (entries out of range are clamped, giving unspecified
+ *   results but no out-of-bounds access).  Workspace as gptq_prepare_hinv.
+ *
+ * gptq_quantize_layer_perm: as gptq_quantize_layer with the columns of W0
+ *   quantized in the order perm, using the U of gptq_prepare_hinv_perm.
+ *   codes  are written in the ORIGINAL column order.
+ *   groups are runs of group_size consecutive positions of the quantization
+ *          order: scales / zeros [d_row x n_groups] are indexed by that run,
+ *          and original column j belongs to run
+ *   g_idx  [device] int32 [d_col] output: g_idx[j] = (position of j) /
+ *          group_size (0 for every column when group_size == 0).
+ *   out_err is the same order-free quantity as in gptq_quantize_layer.
+ *   Workspace as gptq_quantize_layer.
+ */
+gptq_status gptq_act_order_perm(const float* H, int64_t d_col, int32_t* perm, void* stream);
+gptq_status gptq_prepare_hinv_perm(const float* H, int64_t d_col, const int32_t* perm,
+                                   float percdamp, float* U, float* lambda_out, int32_t* info,
+                                   void* ws, size_t ws_bytes, void* stream);
+gptq_status gptq_quantize_layer_perm(const void* W0, int32_t w_dtype, int64_t d_row,
+                                     int64_t d_col, int64_t ld_w, const float* U,
+                                     const float* lambda, const int32_t* perm, int32_t bits,
+                                     int64_t group_size, int64_t block_size, uint8_t* codes,
+                                     float* scales, int32_t* zeros, int32_t* g_idx,
+                                     double* out_err, void* ws, size_t ws_bytes, void* stream);
+
 /* [host] static description of a status code; never NULL. */
 const char* gptq_status_string(int32_t status);
 /* [host] library version string, e.g. "gptq-gfx950 0.1.0". */

@@ -23,6 +23,7 @@ __all__ = [
     "gptq_hessian_accumulate", "gptq_hessian_accumulate_workspace_size",
     "gptq_prepare_hinv", "gptq_prepare_hinv_workspace_size",
     "gptq_quantize_layer", "gptq_quantize_layer_workspace_size",
+    "gptq_act_order_perm", "gptq_prepare_hinv_perm", "gptq_quantize_layer_perm",
     "gptq_status_string", "gptq_version", "quantize_layer",
 ]
 
@@ -74,6 +75,13 @@ def library() -> ctypes.CDLL:
     lib.gptq_quantize_layer.restype = i32
     lib.gptq_quantize_layer_workspace_size.argtypes = [i64, i64, i64]
     lib.gptq_quantize_layer_workspace_size.restype = sz
+    lib.gptq_act_order_perm.argtypes = [vp, i64, vp, vp]
+    lib.gptq_act_order_perm.restype = i32
+    lib.gptq_prepare_hinv_perm.argtypes = [vp, i64, vp, ctypes.c_float, vp, vp, vp, vp, sz, vp]
+    lib.gptq_prepare_hinv_perm.restype = i32
+    lib.gptq_quantize_layer_perm.argtypes = [vp, i32, i64, i64, i64, vp, vp, vp, i32, i64, i64, vp,
+                                             vp, vp, vp, vp, vp, sz, vp]
+    lib.gptq_quantize_layer_perm.restype = i32
     lib.gptq_status_string.argtypes = [i32]
     lib.gptq_status_string.restype = ctypes.c_char_p
     lib.gptq_version.argtypes = []
@@ -202,20 +210,86 @@ def gptq_quantize_layer(W0, U, lam=None, bits: int = 4, group_size: int = 0,
     return codes, scales, zeros, out_err
 
 
+def gptq_act_order_perm(H, perm=None, stream=None):
+    """Act-order quantization order: int32 [d] with perm[i] the column quantized at
+    position i (descending diag(H), equal diagonals in ascending index order)."""
+    torch = _torch()
+    d = H.shape[0]
+    perm = perm if perm is not None else torch.empty(d, dtype=torch.int32, device=H.device)
+    st = library().gptq_act_order_perm(H.data_ptr(), d, perm.data_ptr(), _stream(stream))
+    _check(st, "gptq_act_order_perm")
+    return perm
+
+
+def gptq_prepare_hinv_perm(H, perm, percdamp: float = 0.01, U=None, lam=None, info=None,
+                           ws=None, stream=None):
+    """gptq_prepare_hinv for H with rows and columns in the order ``perm``; U is in
+    that order.  Returns (U, lambda, info)."""
+    torch = _torch()
+    d = H.shape[0]
+    dev = H.device
+    U = U if U is not None else torch.empty(d, d, dtype=torch.float32, device=dev)
+    lam = lam if lam is not None else torch.empty(1, dtype=torch.float32, device=dev)
+    info = info if info is not None else torch.empty(1, dtype=torch.int32, device=dev)
+    ws = _workspace(gptq_prepare_hinv_workspace_size(d), dev, ws)
+    st = library().gptq_prepare_hinv_perm(H.data_ptr(), d, perm.data_ptr(), float(percdamp),
+                                          U.data_ptr(), lam.data_ptr(), info.data_ptr(),
+                                          ws.data_ptr(), ws.numel(), _stream(stream))
+    _check(st, "gptq_prepare_hinv_perm")
+    return U, lam, info
+
+
+def gptq_quantize_layer_perm(W0, U, lam, perm, bits: int = 4, group_size: int = 0,
+                             block_size: int = 128, codes=None, scales=None, zeros=None,
+                             g_idx=None, out_err=None, ws=None, stream=None):
+    """The loop over the columns in the order ``perm`` (U from gptq_prepare_hinv_perm).
+    Returns (codes in the original column order, scales, zeros, g_idx, err)."""
+    torch = _torch()
+    _rowmajor(W0, "W0")
+    d_row, d_col = W0.shape
+    dev = W0.device
+    ng = -(-d_col // group_size) if group_size else 1
+    codes = codes if codes is not None else torch.empty(d_row, d_col, dtype=torch.uint8, device=dev)
+    scales = scales if scales is not None else torch.empty(d_row, ng, dtype=torch.float32, device=dev)
+    zeros = zeros if zeros is not None else torch.empty(d_row, ng, dtype=torch.int32, device=dev)
+    g_idx = g_idx if g_idx is not None else torch.empty(d_col, dtype=torch.int32, device=dev)
+    out_err = out_err if out_err is not None else torch.empty(1, dtype=torch.float64, device=dev)
+    ws = _workspace(gptq_quantize_layer_workspace_size(d_row, d_col, block_size), dev, ws)
+    st = library().gptq_quantize_layer_perm(W0.data_ptr(), _dtype_code(W0), d_row, d_col,
+                                            W0.stride(0), U.data_ptr(), _ptr(lam), perm.data_ptr(),
+                                            int(bits), int(group_size), int(block_size),
+                                            codes.data_ptr(), scales.data_ptr(), zeros.data_ptr(),
+                                            g_idx.data_ptr(), out_err.data_ptr(), ws.data_ptr(),
+                                            ws.numel(), _stream(stream))
+    _check(st, "gptq_quantize_layer_perm")
+    return codes, scales, zeros, g_idx, out_err
+
+
 def quantize_layer(W0, x_chunks: Iterable, bits: int = 4, group_size: int = 0,
-                   block_size: int = 128, percdamp: float = 0.01, stream=None):
-    """All three calls for one layer; raises NotPositiveDefinite after synchronising
-    if the damped Hessian could not be factored.  Returns a dict of device tensors."""
+                   block_size: int = 128, percdamp: float = 0.01, act_order: bool = False,
+                   stream=None):
+    """All three calls for one layer (natural order, or act-order with
+    ``act_order=True``); raises NotPositiveDefinite after synchronising if the
+    damped Hessian could not be factored.  Returns a dict of device tensors."""
     torch = _torch()
     d_col = W0.shape[1]
     H = torch.zeros(d_col, d_col, dtype=torch.float32, device=W0.device)
     for xc in x_chunks:
         gptq_hessian_accumulate(H, xc, stream=stream)
-    U, lam, info = gptq_prepare_hinv(H, percdamp, stream=stream)
-    codes, scales, zeros, err = gptq_quantize_layer(W0, U, lam, bits, group_size, block_size,
-                                                    stream=stream)
+    out = {"H": H}
+    if act_order:
+        perm = gptq_act_order_perm(H, stream=stream)
+        U, lam, info = gptq_prepare_hinv_perm(H, perm, percdamp, stream=stream)
+        codes, scales, zeros, g_idx, err = gptq_quantize_layer_perm(
+            W0, U, lam, perm, bits, group_size, block_size, stream=stream)
+        out.update(perm=perm, g_idx=g_idx)
+    else:
+        U, lam, info = gptq_prepare_hinv(H, percdamp, stream=stream)
+        codes, scales, zeros, err = gptq_quantize_layer(W0, U, lam, bits, group_size, block_size,
+                                                        stream=stream)
     (stream or torch.cuda.current_stream()).synchronize()
     if int(info.item()) != 0:
         raise NotPositiveDefinite(int(info.item()))
-    return {"H": H, "U": U, "lambda": lam, "codes": codes, "scales": scales, "zeros": zeros,
-            "err": err}
+    out.update(U=U, codes=codes, scales=scales, zeros=zeros, err=err)
+    out["lambda"] = lam
+    return out

@@ -52,9 +52,9 @@ size_t gptq_prepare_hinv_workspace_size(int64_t d_col) {
   return gptq::factor_plan(d_col).ws_bytes;
 }
 
-gptq_status gptq_prepare_hinv(const float* H, int64_t d_col, float percdamp, float* U,
-                              float* lambda_out, int32_t* info, void* ws, size_t ws_bytes,
-                              void* stream) {
+static gptq_status prepare_hinv(const float* H, int64_t d_col, const int32_t* perm, float percdamp,
+                                float* U, float* lambda_out, int32_t* info, void* ws, size_t ws_bytes,
+                                void* stream) {
   if (d_col <= 0) return GPTQ_ERR_BAD_SIZE;
   if (d_col > kMaxDim) return GPTQ_ERR_TOO_LARGE;
   if (H == nullptr || U == nullptr || lambda_out == nullptr || info == nullptr)
@@ -62,7 +62,27 @@ gptq_status gptq_prepare_hinv(const float* H, int64_t d_col, float percdamp, flo
   if (!std::isfinite(percdamp) || percdamp < 0.f) return GPTQ_ERR_BAD_DAMP;
   const gptq::FactorPlan plan = gptq::factor_plan(d_col);
   if (gptq_status st = ws_check(ws, ws_bytes, plan.ws_bytes)) return st;
-  return from_hip(gptq::factor_launch(plan, H, percdamp, U, lambda_out, info, ws, (hipStream_t)stream));
+  return from_hip(gptq::factor_launch(plan, H, perm, percdamp, U, lambda_out, info, ws, (hipStream_t)stream));
+}
+
+gptq_status gptq_prepare_hinv(const float* H, int64_t d_col, float percdamp, float* U,
+                              float* lambda_out, int32_t* info, void* ws, size_t ws_bytes,
+                              void* stream) {
+  return prepare_hinv(H, d_col, nullptr, percdamp, U, lambda_out, info, ws, ws_bytes, stream);
+}
+
+gptq_status gptq_act_order_perm(const float* H, int64_t d_col, int32_t* perm, void* stream) {
+  if (d_col <= 0) return GPTQ_ERR_BAD_SIZE;
+  if (d_col > kMaxDim) return GPTQ_ERR_TOO_LARGE;
+  if (H == nullptr || perm == nullptr) return GPTQ_ERR_NULL_POINTER;
+  return from_hip(gptq::act_order_launch(H, d_col, perm, (hipStream_t)stream));
+}
+
+gptq_status gptq_prepare_hinv_perm(const float* H, int64_t d_col, const int32_t* perm, float percdamp,
+                                   float* U, float* lambda_out, int32_t* info, void* ws,
+                                   size_t ws_bytes, void* stream) {
+  if (perm == nullptr && d_col > 0 && d_col <= kMaxDim) return GPTQ_ERR_NULL_POINTER;
+  return prepare_hinv(H, d_col, perm, percdamp, U, lambda_out, info, ws, ws_bytes, stream);
 }
 
 size_t gptq_quantize_layer_workspace_size(int64_t d_row, int64_t d_col, int64_t block_size) {
@@ -71,11 +91,12 @@ size_t gptq_quantize_layer_workspace_size(int64_t d_row, int64_t d_col, int64_t 
   return gptq::quant_plan(d_row, d_col, block_size).ws_bytes;
 }
 
-gptq_status gptq_quantize_layer(const void* W0, int32_t w_dtype, int64_t d_row, int64_t d_col,
-                                int64_t ld_w, const float* U, const float* lambda, int32_t bits,
-                                int64_t group_size, int64_t block_size, uint8_t* codes,
-                                float* scales, int32_t* zeros, double* out_err, void* ws,
-                                size_t ws_bytes, void* stream) {
+static gptq_status quantize_layer(const void* W0, int32_t w_dtype, int64_t d_row, int64_t d_col,
+                                  int64_t ld_w, const float* U, const float* lambda,
+                                  const int32_t* perm, int32_t bits, int64_t group_size,
+                                  int64_t block_size, uint8_t* codes, float* scales, int32_t* zeros,
+                                  int32_t* g_idx, double* out_err, void* ws, size_t ws_bytes,
+                                  void* stream) {
   if (d_row <= 0 || d_col <= 0) return GPTQ_ERR_BAD_SIZE;
   if (d_row > kMaxDim || d_col > kMaxDim) return GPTQ_ERR_TOO_LARGE;
   if (w_dtype != GPTQ_F32 && w_dtype != GPTQ_F16) return GPTQ_ERR_BAD_DTYPE;
@@ -91,8 +112,28 @@ gptq_status gptq_quantize_layer(const void* W0, int32_t w_dtype, int64_t d_row, 
     return GPTQ_ERR_BAD_GROUP;
   const gptq::QuantPlan plan = gptq::quant_plan(d_row, d_col, block_size);
   if (gptq_status st = ws_check(ws, ws_bytes, plan.ws_bytes)) return st;
-  return from_hip(gptq::quant_launch(plan, W0, w_dtype, ld_w, U, lambda, bits, group_size, codes,
-                                     scales, zeros, out_err, ws, (hipStream_t)stream));
+  return from_hip(gptq::quant_launch(plan, W0, w_dtype, ld_w, U, lambda, perm, bits, group_size, codes,
+                                     scales, zeros, g_idx, out_err, ws, (hipStream_t)stream));
+}
+
+gptq_status gptq_quantize_layer(const void* W0, int32_t w_dtype, int64_t d_row, int64_t d_col,
+                                int64_t ld_w, const float* U, const float* lambda, int32_t bits,
+                                int64_t group_size, int64_t block_size, uint8_t* codes,
+                                float* scales, int32_t* zeros, double* out_err, void* ws,
+                                size_t ws_bytes, void* stream) {
+  return quantize_layer(W0, w_dtype, d_row, d_col, ld_w, U, lambda, nullptr, bits, group_size,
+                        block_size, codes, scales, zeros, nullptr, out_err, ws, ws_bytes, stream);
+}
+
+gptq_status gptq_quantize_layer_perm(const void* W0, int32_t w_dtype, int64_t d_row, int64_t d_col,
+                                     int64_t ld_w, const float* U, const float* lambda,
+                                     const int32_t* perm, int32_t bits, int64_t group_size,
+                                     int64_t block_size, uint8_t* codes, float* scales,
+                                     int32_t* zeros, int32_t* g_idx, double* out_err, void* ws,
+                                     size_t ws_bytes, void* stream) {
+  if (perm == nullptr || g_idx == nullptr) return GPTQ_ERR_NULL_POINTER;
+  return quantize_layer(W0, w_dtype, d_row, d_col, ld_w, U, lambda, perm, bits, group_size,
+                        block_size, codes, scales, zeros, g_idx, out_err, ws, ws_bytes, stream);
 }
 
 const char* gptq_status_string(int32_t status) {

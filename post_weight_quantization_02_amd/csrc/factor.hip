@@ -54,9 +54,12 @@ __global__ __launch_bounds__(kThreads) void damp_kernel(const float* __restrict_
   }
 }
 
-// A[i][j] = H[d-1-i][d-1-j] (+ lambda on the diagonal), lower 64x64 tiles only
+// A[i][j] = Hp[d-1-i][d-1-j] (+ lambda on the diagonal), lower 64x64 tiles only;
+// Hp = H, or H with rows and columns taken in the order perm (Hp[a][b] =
+// H[perm[a]][perm[b]]; indices clamped into range)
 __global__ __launch_bounds__(kThreads) void rev_copy_kernel(const float* __restrict__ H, int64_t d,
                                                             const double* lam64,
+                                                            const int32_t* __restrict__ perm,
                                                             double* __restrict__ A) {
   const int bj = blockIdx.x, bi = blockIdx.y;
   if (bj > bi) return;
@@ -66,7 +69,12 @@ __global__ __launch_bounds__(kThreads) void rev_copy_kernel(const float* __restr
   for (int k = 0; k < 16; ++k) {
     const int64_t i = (int64_t)bi * 64 + (t >> 6) + 4 * k;
     if (i < d && j < d && j <= i) {
-      double v = (double)H[(d - 1 - i) * d + (d - 1 - j)];
+      int64_t si = d - 1 - i, sj = d - 1 - j;
+      if (perm) {
+        si = min<int64_t>(max<int32_t>(perm[si], 0), d - 1);
+        sj = min<int64_t>(max<int32_t>(perm[sj], 0), d - 1);
+      }
+      double v = (double)H[si * d + sj];
       if (i == j) v += lam;
       A[i * d + j] = v;
     }
@@ -600,6 +608,62 @@ __global__ __launch_bounds__(kThreads) void rev_out_kernel(const float* __restri
 
 }  // namespace
 
+namespace {
+// Act-order (itwiki "GPTQ", practical variants: the columns with the largest
+// Hessian diagonal are quantized first).  Column j goes to position
+// #{i : key_i > key_j} with the 64-bit key (ord(diag_i) << 32) | ~i, where
+// ord maps floats to unsigned integers in the same order (-0 taken as +0, NaN
+// as -inf): descending diagonal, equal diagonals in ascending index order.
+// The keys are distinct, so the ranks are always a permutation.
+__device__ __forceinline__ uint64_t act_order_key(float v, uint32_t i) {
+  if (v != v) v = -INFINITY;
+  if (v == 0.f) v = 0.f;
+  uint32_t u = __float_as_uint(v);
+  u = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+  return ((uint64_t)u << 32) | (uint64_t)(~i);
+}
+
+constexpr int kRankTile = 128;    // columns j per work-group (one per thread)
+constexpr int kKeyTile = 4096;    // keys staged in LDS at a time (32 KB)
+__global__ __launch_bounds__(kRankTile) void act_order_rank_kernel(const float* __restrict__ H,
+                                                                   int64_t d,
+                                                                   int32_t* __restrict__ perm) {
+  __shared__ __attribute__((aligned(16))) uint64_t key[kKeyTile];
+  const int j = blockIdx.x * kRankTile + threadIdx.x;  // d <= 2^20
+  const uint64_t kj = (j < d) ? act_order_key(H[(int64_t)j * (d + 1)], (uint32_t)j) : ~0ull;
+  int rank = 0;
+  for (int i0 = 0; i0 < d; i0 += kKeyTile) {
+    __syncthreads();
+    // this tile's keys: every thread's loads in flight together; entries past
+    // d get key 0, below every real key, so they never count
+    constexpr int kPer = kKeyTile / kRankTile;
+    uint64_t kv[kPer];
+#pragma unroll
+    for (int u = 0; u < kPer; ++u) {
+      const int i = i0 + threadIdx.x + u * kRankTile;
+      kv[u] = (i < d) ? act_order_key(H[(int64_t)i * (d + 1)], (uint32_t)i) : 0ull;
+    }
+#pragma unroll
+    for (int u = 0; u < kPer; ++u) key[threadIdx.x + u * kRankTile] = kv[u];
+    __syncthreads();
+    const int n = (int)min<int64_t>(kKeyTile, d - i0);
+    const int n2 = (n + 1) & ~1;
+#pragma unroll 8
+    for (int u = 0; u < n2; u += 2) {
+      const uint64_t a0 = key[u], a1 = key[u + 1];
+      rank += (int)(a0 > kj) + (int)(a1 > kj);
+    }
+  }
+  if (j < d) perm[rank] = j;
+}
+}  // namespace
+
+hipError_t act_order_launch(const float* H, int64_t d, int32_t* perm, hipStream_t s) {
+  hipLaunchKernelGGL(act_order_rank_kernel, dim3((unsigned)cdiv(d, kRankTile)), dim3(kRankTile), 0, s, H, d,
+                     perm);
+  return hipGetLastError();
+}
+
 // pairs of level sb of the recursive inverse (those whose C range is not empty)
 static int64_t tri_pairs(int64_t nblk, int64_t sb) { return (nblk > sb) ? cdiv(nblk - sb, 2 * sb) : 0; }
 
@@ -629,8 +693,8 @@ FactorPlan factor_plan(int64_t d) {
   return p;
 }
 
-hipError_t factor_launch(const FactorPlan& p, const float* H, float percdamp, float* U,
-                         float* lambda_out, int32_t* info, void* ws, hipStream_t s) {
+hipError_t factor_launch(const FactorPlan& p, const float* H, const int32_t* perm, float percdamp,
+                         float* U, float* lambda_out, int32_t* info, void* ws, hipStream_t s) {
   const int64_t d = p.d;
   char* base = (char*)ws;
   double* A = (double*)(base + p.off_a64);
@@ -640,7 +704,7 @@ hipError_t factor_launch(const FactorPlan& p, const float* H, float percdamp, fl
   hipError_t e;
   hipLaunchKernelGGL(damp_kernel, dim3(1), dim3(kThreads), 0, s, H, d, percdamp, lam, lambda_out, info);
   const unsigned nt = (unsigned)p.nblk;
-  hipLaunchKernelGGL(rev_copy_kernel, dim3(nt, nt), dim3(kThreads), 0, s, H, d, lam, A);
+  hipLaunchKernelGGL(rev_copy_kernel, dim3(nt, nt), dim3(kThreads), 0, s, H, d, lam, perm, A);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   const int nblk = (int)p.nblk;
   for (int k = -1; k < nblk - 1; ++k) {

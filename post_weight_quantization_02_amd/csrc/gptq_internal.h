@@ -50,20 +50,26 @@ struct FactorPlan {
   size_t off_a64, off_tw, off_tmp, off_lam, ws_bytes;
 };
 FactorPlan factor_plan(int64_t d);
-hipError_t factor_launch(const FactorPlan& p, const float* H, float percdamp, float* U,
-                         float* lambda_out, int32_t* info, void* ws, hipStream_t s);
+// perm: NULL, or the order in which the columns are factored (H[perm][:, perm])
+hipError_t factor_launch(const FactorPlan& p, const float* H, const int32_t* perm, float percdamp,
+                         float* U, float* lambda_out, int32_t* info, void* ws, hipStream_t s);
+// act-order: perm[i] = the column taken at position i (descending diag(H), stable)
+hipError_t act_order_launch(const float* H, int64_t d, int32_t* perm, hipStream_t s);
 
 // ---------------------------------------------------------------- quantize
 struct QuantPlan {
   int64_t d_row, d_col, B, nblk;
   int64_t panel_wgs;      // work-groups of the panel kernel
-  size_t off_w, off_e, off_part, off_err, ws_bytes;
+  size_t off_w, off_e, off_part, off_err, off_cpos, ws_bytes;
 };
 QuantPlan quant_plan(int64_t d_row, int64_t d_col, int64_t B);
+// perm: NULL (natural order) or the quantization order (position c takes column
+// perm[c] of W0; codes land in the original columns; groups are runs of
+// positions); g_idx: NULL or the group of every original column
 hipError_t quant_launch(const QuantPlan& p, const void* W0, int w_dtype, int64_t ldw,
-                        const float* U, const float* lambda, int bits, int64_t group,
-                        uint8_t* codes, float* scales, int32_t* zeros, double* out_err,
-                        void* ws, hipStream_t s);
+                        const float* U, const float* lambda, const int32_t* perm, int bits,
+                        int64_t group, uint8_t* codes, float* scales, int32_t* zeros,
+                        int32_t* g_idx, double* out_err, void* ws, hipStream_t s);
 
 // W[:, i+B:] -= E U[i:i+B, i+B:] with E given transposed: C [M x N] (ldc) -=
 // Et^T [M x K] * Ub [K x N]; Et is [K x M] (lde), Ub [K x N] (ldu); K <= 128.

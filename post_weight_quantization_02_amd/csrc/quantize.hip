@@ -53,10 +53,17 @@ __global__ void zero_f64_kernel(double* p, int64_t n) {
     p[i] = 0.0;
 }
 
-// fp32 working copy of W0; with a per-row grid also that row's scale / zero
+// a column index from a caller's permutation, clamped into range
+__device__ __forceinline__ int64_t perm_col(const int32_t* __restrict__ perm, int64_t c, int64_t d_col) {
+  return perm ? min<int64_t>(max<int32_t>(perm[c], 0), d_col - 1) : c;
+}
+
+// fp32 working copy of W0 (column c of the copy is column perm[c] of W0 when a
+// quantization order is given); with a per-row grid also that row's scale / zero
 template <typename T>
 __global__ __launch_bounds__(kThreads) void prep_kernel(const T* __restrict__ W0, int64_t ldw,
-                                                        int64_t d_col, float* __restrict__ W,
+                                                        int64_t d_col, const int32_t* __restrict__ perm,
+                                                        float* __restrict__ W,
                                                         int per_row, int maxq,
                                                         float* __restrict__ scales,
                                                         int32_t* __restrict__ zeros) {
@@ -65,7 +72,7 @@ __global__ __launch_bounds__(kThreads) void prep_kernel(const T* __restrict__ W0
   const int t = threadIdx.x;
   float mn = INFINITY, mx = -INFINITY;
   for (int64_t c = t; c < d_col; c += kThreads) {
-    const float v = (float)W0[row * ldw + c];
+    const float v = (float)W0[row * ldw + perm_col(perm, c, d_col)];
     W[row * d_col + c] = v;
     mn = fminf(mn, v);
     mx = fmaxf(mx, v);
@@ -348,18 +355,23 @@ hipError_t launch_panel(int gin, bool full, dim3 grid, hipStream_t s, float* W, 
 template <typename T>
 __global__ __launch_bounds__(kThreads) void err_delta_kernel(
     const T* __restrict__ W0, int64_t ldw, int64_t d_row, int64_t d_col,
-    const uint8_t* __restrict__ codes, const float* __restrict__ scales,
-    const int32_t* __restrict__ zeros, int g, int64_t ngroups, double* __restrict__ part_d) {
+    const uint8_t* __restrict__ cpos, const float* __restrict__ scales,
+    const int32_t* __restrict__ zeros, int g, int64_t ngroups, const int32_t* __restrict__ perm,
+    uint8_t* __restrict__ codes, double* __restrict__ part_d) {
   __shared__ double red[kThreads];
   const int t = threadIdx.x;
   double acc = 0.0;
   for (int64_t row = blockIdx.x; row < d_row; row += gridDim.x) {
     for (int64_t c = t; c < d_col; c += kThreads) {
+      // c: position in the quantization order (groups are runs of positions)
       const int gi = (int)c / g;
+      const int64_t oc = perm_col(perm, c, d_col);
       const float s = scales[row * ngroups + gi];
       const float z = (float)zeros[row * ngroups + gi];
-      const float wh = s * ((float)codes[row * d_col + c] - z);
-      const double dlt = (double)(float)W0[row * ldw + c] - (double)wh;
+      const uint8_t cv = cpos[row * d_col + c];
+      if (perm) codes[row * d_col + oc] = cv;  // back to the original column
+      const float wh = s * ((float)cv - z);
+      const double dlt = (double)(float)W0[row * ldw + oc] - (double)wh;
       acc += dlt * dlt;
     }
   }
@@ -395,6 +407,13 @@ __global__ __launch_bounds__(kThreads) void err_final_kernel(const double* __res
   if (t == 0) *out = 0.5 * re[0] - (lambda ? 0.5 * (double)*lambda * rdd[0] : 0.0);
 }
 
+// group of each original column: g_idx[perm[c]] = c / g
+__global__ __launch_bounds__(kThreads) void g_idx_kernel(const int32_t* __restrict__ perm, int64_t d_col,
+                                                         int64_t g, int32_t* __restrict__ g_idx) {
+  const int64_t c = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+  if (c < d_col) g_idx[perm_col(perm, c, d_col)] = (int32_t)(c / g);
+}
+
 constexpr int64_t kErrWGs = 1024;
 
 }  // namespace
@@ -415,30 +434,35 @@ QuantPlan quant_plan(int64_t d_row, int64_t d_col, int64_t B) {
   off = align_up(off + (size_t)p.panel_wgs * sizeof(double), 256);
   p.off_err = off;
   off = align_up(off + (size_t)kErrWGs * sizeof(double), 256);
+  p.off_cpos = off;  // codes in quantization order (used under a permutation)
+  off = align_up(off + (size_t)d_row * d_col, 256);
   p.ws_bytes = off;
   return p;
 }
 
 hipError_t quant_launch(const QuantPlan& p, const void* W0, int w_dtype, int64_t ldw,
-                        const float* U, const float* lambda, int bits, int64_t group,
-                        uint8_t* codes, float* scales, int32_t* zeros, double* out_err, void* ws,
-                        hipStream_t s) {
+                        const float* U, const float* lambda, const int32_t* perm, int bits,
+                        int64_t group, uint8_t* codes, float* scales, int32_t* zeros,
+                        int32_t* g_idx, double* out_err, void* ws, hipStream_t s) {
   const int64_t d_row = p.d_row, d_col = p.d_col, B = p.B;
   char* base = (char*)ws;
   float* W = (float*)(base + p.off_w);
   float* E = (float*)(base + p.off_e);
   double* part_e = (double*)(base + p.off_part);
   double* part_d = (double*)(base + p.off_err);
+  // codes by position of the quantization order: the caller's array in natural
+  // order, a workspace copy under a permutation (scattered back at the end)
+  uint8_t* cpos = perm ? (uint8_t*)(base + p.off_cpos) : codes;
   const int maxq = (1 << bits) - 1;
   const int64_t ngroups = group ? cdiv(d_col, group) : 1;
   hipError_t e;
   hipLaunchKernelGGL(zero_f64_kernel, dim3(64), dim3(kThreads), 0, s, part_e, p.panel_wgs);
   if (w_dtype == 1)
     hipLaunchKernelGGL(prep_kernel<_Float16>, dim3((unsigned)d_row), dim3(kThreads), 0, s,
-                       (const _Float16*)W0, ldw, d_col, W, group == 0, maxq, scales, zeros);
+                       (const _Float16*)W0, ldw, d_col, perm, W, group == 0, maxq, scales, zeros);
   else
     hipLaunchKernelGGL(prep_kernel<float>, dim3((unsigned)d_row), dim3(kThreads), 0, s,
-                       (const float*)W0, ldw, d_col, W, group == 0, maxq, scales, zeros);
+                       (const float*)W0, ldw, d_col, perm, W, group == 0, maxq, scales, zeros);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   for (int64_t i1 = 0; i1 < d_col; i1 += B) {
     const int width = (int)std::min<int64_t>(B, d_col - i1);
@@ -454,13 +478,13 @@ hipError_t quant_launch(const QuantPlan& p, const void* W0, int w_dtype, int64_t
     const int ng = (int)ngroups;
     switch (B) {
       case 16: e = launch_panel<1>(gin, full, pg, s, W, (int)d_row, (int)d_col, (int)i1, width, U,
-                                   maxq, gwide, ng, codes, scales, zeros, E, part_e); break;
+                                   maxq, gwide, ng, cpos, scales, zeros, E, part_e); break;
       case 32: e = launch_panel<2>(gin, full, pg, s, W, (int)d_row, (int)d_col, (int)i1, width, U,
-                                   maxq, gwide, ng, codes, scales, zeros, E, part_e); break;
+                                   maxq, gwide, ng, cpos, scales, zeros, E, part_e); break;
       case 64: e = launch_panel<4>(gin, full, pg, s, W, (int)d_row, (int)d_col, (int)i1, width, U,
-                                   maxq, gwide, ng, codes, scales, zeros, E, part_e); break;
+                                   maxq, gwide, ng, cpos, scales, zeros, E, part_e); break;
       default: e = launch_panel<8>(gin, full, pg, s, W, (int)d_row, (int)d_col, (int)i1, width, U,
-                                   maxq, gwide, ng, codes, scales, zeros, E, part_e); break;
+                                   maxq, gwide, ng, cpos, scales, zeros, E, part_e); break;
     }
     if (e != hipSuccess) return e;
     const int64_t i2 = i1 + width;
@@ -474,12 +498,15 @@ hipError_t quant_launch(const QuantPlan& p, const void* W0, int w_dtype, int64_t
   const int64_t gsz = group ? group : d_col;
   if (w_dtype == 1)
     hipLaunchKernelGGL(err_delta_kernel<_Float16>, dim3(nerr), dim3(kThreads), 0, s,
-                       (const _Float16*)W0, ldw, d_row, d_col, codes, scales, zeros, gsz, ngroups, part_d);
+                       (const _Float16*)W0, ldw, d_row, d_col, cpos, scales, zeros, gsz, ngroups, perm, codes, part_d);
   else
     hipLaunchKernelGGL(err_delta_kernel<float>, dim3(nerr), dim3(kThreads), 0, s, (const float*)W0, ldw,
-                       d_row, d_col, codes, scales, zeros, gsz, ngroups, part_d);
+                       d_row, d_col, cpos, scales, zeros, gsz, ngroups, perm, codes, part_d);
   hipLaunchKernelGGL(err_final_kernel, dim3(1), dim3(kThreads), 0, s, part_e, p.panel_wgs, part_d,
                      (int64_t)nerr, lambda, out_err);
+  if (g_idx)
+    hipLaunchKernelGGL(g_idx_kernel, dim3((unsigned)cdiv(d_col, kThreads)), dim3(kThreads), 0, s, perm, d_col,
+                       gsz, g_idx);
   return hipGetLastError();
 }
 

@@ -118,3 +118,29 @@ def test_workspace_sizes_are_monotone():
     assert 0 < a < b
     assert G.gptq_prepare_hinv_workspace_size(4096) > G.gptq_prepare_hinv_workspace_size(512)
     assert G.gptq_hessian_accumulate_workspace_size(4096, 262144, 1) > 0
+
+
+def test_act_order_validation():
+    lib = G.library()
+    f = lib.gptq_act_order_perm
+    assert f(FAKE, 0, FAKE, None) == _status("GPTQ_ERR_BAD_SIZE")
+    assert f(None, 8, FAKE, None) == _status("GPTQ_ERR_NULL_POINTER")
+    assert f(FAKE, 8, None, None) == _status("GPTQ_ERR_NULL_POINTER")
+    assert f(FAKE, 1 << 21, FAKE, None) == _status("GPTQ_ERR_TOO_LARGE")
+    p = lib.gptq_prepare_hinv_perm
+    assert p(FAKE, 8, None, 0.01, FAKE, FAKE, FAKE, FAKE, 1 << 40, None) == _status("GPTQ_ERR_NULL_POINTER")
+    assert p(FAKE, 0, FAKE, 0.01, FAKE, FAKE, FAKE, FAKE, 1 << 40, None) == _status("GPTQ_ERR_BAD_SIZE")
+    assert p(FAKE, 8, FAKE, -1.0, FAKE, FAKE, FAKE, FAKE, 1 << 40, None) == _status("GPTQ_ERR_BAD_DAMP")
+    need = G.gptq_prepare_hinv_workspace_size(8)
+    assert p(FAKE, 8, FAKE, 0.01, FAKE, FAKE, FAKE, FAKE, need - 1, None) == _status("GPTQ_ERR_WORKSPACE")
+    q = lib.gptq_quantize_layer_perm
+    needq = G.gptq_quantize_layer_workspace_size(4, 32, 16)
+    args = [FAKE, 0, 4, 32, 32, FAKE, FAKE, FAKE, 4, 0, 16, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, needq, None]
+    a = list(args); a[7] = None
+    assert q(*a) == _status("GPTQ_ERR_NULL_POINTER")     # perm
+    a = list(args); a[14] = None
+    assert q(*a) == _status("GPTQ_ERR_NULL_POINTER")     # g_idx
+    a = list(args); a[8] = 9
+    assert q(*a) == _status("GPTQ_ERR_BAD_BITS")
+    a = list(args); a[17] = needq - 1
+    assert q(*a) == _status("GPTQ_ERR_WORKSPACE")
