@@ -342,6 +342,71 @@ def gptq_quantize_act_order(W0: np.ndarray, U_perm: np.ndarray, perm: np.ndarray
 
 
 # ---------------------------------------------------------------------------
+# packed low-bit codes and the dequantizing product (the consumer of the codes:
+# wiki "결과" reports the speed of such kernels; the pages fix no format)
+# ---------------------------------------------------------------------------
+
+def pack_codes(codes: np.ndarray, bits: int, perm: Optional[np.ndarray] = None) -> np.ndarray:
+    """Row-major bitstream of ``bits``-bit fields in little-endian uint32 words.
+
+    Position i of a row holds column perm[i] (or column i): its field occupies
+    bits [bits*i, bits*i + bits) of the row's stream, bit b of the stream being
+    bit b % 32 of word b // 32.  Rows are padded to whole 32-code chunks, so a
+    row takes ceil(d_col / 32) * bits words.  (Reading: the pages name packed
+    low-bit storage but no layout.)
+    """
+    c = np.asarray(codes, dtype=np.uint64)
+    d_row, d_col = c.shape
+    if perm is not None:
+        c = c[:, np.asarray(perm, dtype=np.int64)]
+    if np.any(c >> np.uint64(bits)):
+        raise ValueError("code does not fit in the field width")
+    words = -(-d_col // 32) * bits
+    out = np.zeros((d_row, words), dtype=np.uint64)
+    for i in range(d_col):
+        off = bits * i
+        w, sh = off // 32, off % 32
+        out[:, w] |= (c[:, i] << np.uint64(sh)) & np.uint64(0xFFFFFFFF)
+        if sh + bits > 32:                       # the field runs into the next word
+            out[:, w + 1] |= c[:, i] >> np.uint64(32 - sh)
+    return out.astype(np.uint32)
+
+
+def unpack_codes(packed: np.ndarray, bits: int, d_col: int) -> np.ndarray:
+    """Inverse of pack_codes (codes by position)."""
+    p = np.asarray(packed, dtype=np.uint64)
+    out = np.zeros((p.shape[0], d_col), dtype=np.uint64)
+    mask = np.uint64((1 << bits) - 1)
+    for i in range(d_col):
+        off = bits * i
+        w, sh = off // 32, off % 32
+        v = p[:, w] >> np.uint64(sh)
+        if sh + bits > 32:
+            v |= p[:, w + 1] << np.uint64(32 - sh)
+        out[:, i] = v & mask
+    return out.astype(np.uint8)
+
+
+def dequant_matmul(packed: np.ndarray, bits: int, scales: np.ndarray, zeros: np.ndarray,
+                   group_size: int, X: np.ndarray, d_col: int,
+                   perm: Optional[np.ndarray] = None) -> np.ndarray:
+    """Y = X What^T with What dequantized from packed codes, in fp64.
+
+    What by position i: scale[:, g] * (code_i - zero[:, g]) with g = i // group_size
+    (one group when group_size == 0); position i multiplies column perm[i] of X
+    (or column i).  X is [m x d_col]; Y is [m x d_row].
+    """
+    c = unpack_codes(packed, bits, d_col).astype(np.float64)
+    g = group_size if group_size else d_col
+    gi = np.arange(d_col) // g
+    w_hat = np.asarray(scales, dtype=np.float64)[:, gi] * (c - np.asarray(zeros, dtype=np.float64)[:, gi])
+    Xp = np.asarray(X, dtype=np.float64)
+    if perm is not None:
+        Xp = Xp[:, np.asarray(perm, dtype=np.int64)]
+    return Xp @ w_hat.T
+
+
+# ---------------------------------------------------------------------------
 # output error (wiki "문제 설정": ||W X - What X||^2)
 # ---------------------------------------------------------------------------
 
