@@ -201,6 +201,42 @@ gptq_status gptq_quantize_layer_perm(const void* W0, int32_t w_dtype, int64_t d_
                                      float* scales, int32_t* zeros, int32_t* g_idx,
                                      double* out_err, void* ws, size_t ws_bytes, void* stream);
 
+/*
+ * Packed codes and the dequantizing product -- the consumer of the codes (itwiki
+ * "GPTQ", section "결과": kernels that unpack the weights on the fly).
+ *
+ * Layout (packed): each row is a little-endian bitstream of `bits`-bit fields
+ * in 32-bit words; position i of a row occupies bits [bits*i, bits*i + bits)
+ * of the stream (bit b of the stream = bit b % 32 of word b / 32).  Rows are
+ * padded to whole chunks of 32 codes (a chunk is exactly `bits` words);
+ * gptq_packed_words_per_row() = ceil(d_col / 32) * bits.  bits is 2, 3, 4 or 8.
+ *
+ * gptq_pack_codes: codes [device] uint8 [d_row x d_col] (leading dimension
+ *   ld_codes >= d_col, values < 2^bits; higher bits are dropped) -> packed
+ *   [device] uint32 [d_row x ld_packed], ld_packed >= words per row.  perm:
+ *   NULL, or [device] int32 [d_col] with position i holding column perm[i]
+ *   (pass the act-order permutation so that groups of positions are
+ *   contiguous; entries out of range are clamped).  Needs no workspace.
+ *
+ * gptq_dequant_matmul: Y [device] float [m x d_row] (leading dimension ld_y >=
+ *   d_row) = X What^T for 1 <= m <= 8 rows of X [device] [m x d_col]
+ *   (x_dtype GPTQ_F16 or GPTQ_F32, leading dimension ld_x >= d_col), with
+ *     What by position i = scales[r][g] * (code_i - zeros[r][g]),
+ *     g = i / group_size (0 when group_size == 0; group_size a multiple of 16),
+ *   and position i multiplying column perm[i] of X (or column i when perm is
+ *   NULL).  scales / zeros as written by gptq_quantize_layer(_perm).  fp32
+ *   accumulation; no workspace.
+ */
+int64_t gptq_packed_words_per_row(int64_t d_col, int32_t bits);
+gptq_status gptq_pack_codes(const uint8_t* codes, int64_t d_row, int64_t d_col, int64_t ld_codes,
+                            int32_t bits, const int32_t* perm, uint32_t* packed, int64_t ld_packed,
+                            void* stream);
+gptq_status gptq_dequant_matmul(const uint32_t* packed, int64_t ld_packed, int32_t bits,
+                                const float* scales, const int32_t* zeros, int64_t group_size,
+                                const int32_t* perm, int64_t d_row, int64_t d_col, const void* X,
+                                int32_t x_dtype, int64_t m, int64_t ld_x, float* Y, int64_t ld_y,
+                                void* stream);
+
 /* [host] static description of a status code; never NULL. */
 const char* gptq_status_string(int32_t status);
 /* [host] library version string, e.g. "gptq-gfx950 0.1.0". */

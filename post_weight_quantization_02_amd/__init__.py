@@ -24,6 +24,7 @@ __all__ = [
     "gptq_prepare_hinv", "gptq_prepare_hinv_workspace_size",
     "gptq_quantize_layer", "gptq_quantize_layer_workspace_size",
     "gptq_act_order_perm", "gptq_prepare_hinv_perm", "gptq_quantize_layer_perm",
+    "gptq_packed_words_per_row", "gptq_pack_codes", "gptq_dequant_matmul",
     "gptq_status_string", "gptq_version", "quantize_layer",
 ]
 
@@ -82,6 +83,13 @@ def library() -> ctypes.CDLL:
     lib.gptq_quantize_layer_perm.argtypes = [vp, i32, i64, i64, i64, vp, vp, vp, i32, i64, i64, vp,
                                              vp, vp, vp, vp, vp, sz, vp]
     lib.gptq_quantize_layer_perm.restype = i32
+    lib.gptq_packed_words_per_row.argtypes = [i64, i32]
+    lib.gptq_packed_words_per_row.restype = i64
+    lib.gptq_pack_codes.argtypes = [vp, i64, i64, i64, i32, vp, vp, i64, vp]
+    lib.gptq_pack_codes.restype = i32
+    lib.gptq_dequant_matmul.argtypes = [vp, i64, i32, vp, vp, i64, vp, i64, i64, vp, i32, i64, i64, vp,
+                                        i64, vp]
+    lib.gptq_dequant_matmul.restype = i32
     lib.gptq_status_string.argtypes = [i32]
     lib.gptq_status_string.restype = ctypes.c_char_p
     lib.gptq_version.argtypes = []
@@ -263,6 +271,41 @@ def gptq_quantize_layer_perm(W0, U, lam, perm, bits: int = 4, group_size: int = 
                                             ws.numel(), _stream(stream))
     _check(st, "gptq_quantize_layer_perm")
     return codes, scales, zeros, g_idx, out_err
+
+
+def gptq_packed_words_per_row(d_col: int, bits: int) -> int:
+    return int(library().gptq_packed_words_per_row(d_col, bits))
+
+
+def gptq_pack_codes(codes, bits: int, perm=None, packed=None, stream=None):
+    """Pack uint8 codes [d_row x d_col] into 32-bit words (position i holds column
+    perm[i] when perm is given).  Returns the packed int32 tensor (bit patterns)."""
+    torch = _torch()
+    _rowmajor(codes, "codes")
+    d_row, d_col = codes.shape
+    words = gptq_packed_words_per_row(d_col, bits)
+    packed = packed if packed is not None else torch.empty(d_row, words, dtype=torch.int32,
+                                                             device=codes.device)
+    st = library().gptq_pack_codes(codes.data_ptr(), d_row, d_col, codes.stride(0), int(bits),
+                                   _ptr(perm), packed.data_ptr(), packed.stride(0), _stream(stream))
+    _check(st, "gptq_pack_codes")
+    return packed
+
+
+def gptq_dequant_matmul(packed, bits: int, scales, zeros, group_size: int, X, d_col: int,
+                        perm=None, Y=None, stream=None):
+    """Y [m x d_row] fp32 = X What^T from packed codes (1 <= m <= 8)."""
+    torch = _torch()
+    _rowmajor(X, "X")
+    d_row = packed.shape[0]
+    m = X.shape[0]
+    Y = Y if Y is not None else torch.empty(m, d_row, dtype=torch.float32, device=X.device)
+    st = library().gptq_dequant_matmul(packed.data_ptr(), packed.stride(0), int(bits), scales.data_ptr(),
+                                       zeros.data_ptr(), int(group_size), _ptr(perm), d_row, d_col,
+                                       X.data_ptr(), _dtype_code(X), m, X.stride(0), Y.data_ptr(),
+                                       Y.stride(0), _stream(stream))
+    _check(st, "gptq_dequant_matmul")
+    return Y
 
 
 def quantize_layer(W0, x_chunks: Iterable, bits: int = 4, group_size: int = 0,

@@ -136,6 +136,44 @@ gptq_status gptq_quantize_layer_perm(const void* W0, int32_t w_dtype, int64_t d_
                         block_size, codes, scales, zeros, g_idx, out_err, ws, ws_bytes, stream);
 }
 
+static bool pack_bits_ok(int32_t b) { return b == 2 || b == 3 || b == 4 || b == 8; }
+
+int64_t gptq_packed_words_per_row(int64_t d_col, int32_t bits) {
+  if (d_col <= 0 || d_col > kMaxDim || !pack_bits_ok(bits)) return 0;
+  return gptq::packed_words_per_row(d_col, bits);
+}
+
+gptq_status gptq_pack_codes(const uint8_t* codes, int64_t d_row, int64_t d_col, int64_t ld_codes,
+                            int32_t bits, const int32_t* perm, uint32_t* packed, int64_t ld_packed,
+                            void* stream) {
+  if (d_row <= 0 || d_col <= 0) return GPTQ_ERR_BAD_SIZE;
+  if (d_row > kMaxDim || d_col > kMaxDim) return GPTQ_ERR_TOO_LARGE;
+  if (codes == nullptr || packed == nullptr) return GPTQ_ERR_NULL_POINTER;
+  if (!pack_bits_ok(bits)) return GPTQ_ERR_BAD_BITS;
+  if (ld_codes < d_col || ld_packed < gptq::packed_words_per_row(d_col, bits)) return GPTQ_ERR_BAD_LEADING_DIM;
+  return from_hip(gptq::pack_launch(codes, d_row, d_col, ld_codes, bits, perm, packed, ld_packed,
+                                    (hipStream_t)stream));
+}
+
+gptq_status gptq_dequant_matmul(const uint32_t* packed, int64_t ld_packed, int32_t bits,
+                                const float* scales, const int32_t* zeros, int64_t group_size,
+                                const int32_t* perm, int64_t d_row, int64_t d_col, const void* X,
+                                int32_t x_dtype, int64_t m, int64_t ld_x, float* Y, int64_t ld_y,
+                                void* stream) {
+  if (d_row <= 0 || d_col <= 0 || m <= 0) return GPTQ_ERR_BAD_SIZE;
+  if (d_row > kMaxDim || d_col > kMaxDim || m > 8) return GPTQ_ERR_TOO_LARGE;
+  if (packed == nullptr || scales == nullptr || zeros == nullptr || X == nullptr || Y == nullptr)
+    return GPTQ_ERR_NULL_POINTER;
+  if (!pack_bits_ok(bits)) return GPTQ_ERR_BAD_BITS;
+  if (x_dtype != GPTQ_F32 && x_dtype != GPTQ_F16) return GPTQ_ERR_BAD_DTYPE;
+  if (group_size < 0 || (group_size > 0 && group_size % 16 != 0)) return GPTQ_ERR_BAD_GROUP;
+  if (ld_packed < gptq::packed_words_per_row(d_col, bits) || ld_x < d_col || ld_y < d_row)
+    return GPTQ_ERR_BAD_LEADING_DIM;
+  return from_hip(gptq::dequant_matmul_launch(packed, ld_packed, bits, scales, zeros, group_size, perm,
+                                              d_row, d_col, X, x_dtype, (int)m, ld_x, Y, ld_y,
+                                              (hipStream_t)stream));
+}
+
 const char* gptq_status_string(int32_t status) {
   switch (status) {
     case GPTQ_OK: return "ok";
@@ -143,7 +181,7 @@ const char* gptq_status_string(int32_t status) {
     case GPTQ_ERR_BAD_SIZE: return "a size is zero or negative";
     case GPTQ_ERR_BAD_LEADING_DIM: return "leading dimension smaller than the row width";
     case GPTQ_ERR_BAD_DTYPE: return "unsupported element type";
-    case GPTQ_ERR_BAD_BITS: return "bits must be in [2, 8]";
+    case GPTQ_ERR_BAD_BITS: return "bits must be in [2, 8] (2, 3, 4 or 8 for packed codes)";
     case GPTQ_ERR_BAD_BLOCK: return "block_size must be 16, 32, 64 or 128";
     case GPTQ_ERR_BAD_GROUP: return "group_size must be 0, or a multiple of 16 that divides or is divided by block_size";
     case GPTQ_ERR_WORKSPACE: return "workspace missing or smaller than the query";

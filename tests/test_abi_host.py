@@ -144,3 +144,30 @@ def test_act_order_validation():
     assert q(*a) == _status("GPTQ_ERR_BAD_BITS")
     a = list(args); a[17] = needq - 1
     assert q(*a) == _status("GPTQ_ERR_WORKSPACE")
+
+
+def test_packed_validation():
+    lib = G.library()
+    assert G.gptq_packed_words_per_row(100, 3) == 4 * 3
+    assert G.gptq_packed_words_per_row(32, 4) == 4
+    assert G.gptq_packed_words_per_row(100, 5) == 0
+    f = lib.gptq_pack_codes
+    assert f(FAKE, 0, 64, 64, 4, None, FAKE, 8, None) == _status("GPTQ_ERR_BAD_SIZE")
+    assert f(None, 4, 64, 64, 4, None, FAKE, 8, None) == _status("GPTQ_ERR_NULL_POINTER")
+    assert f(FAKE, 4, 64, 64, 5, None, FAKE, 8, None) == _status("GPTQ_ERR_BAD_BITS")
+    assert f(FAKE, 4, 64, 63, 4, None, FAKE, 8, None) == _status("GPTQ_ERR_BAD_LEADING_DIM")
+    assert f(FAKE, 4, 64, 64, 4, None, FAKE, 7, None) == _status("GPTQ_ERR_BAD_LEADING_DIM")
+    d = lib.gptq_dequant_matmul
+    ok = [FAKE, 8, 4, FAKE, FAKE, 16, None, 4, 64, FAKE, 1, 2, 64, FAKE, 4, None]
+    a = list(ok); a[11] = 9
+    assert d(*a) == _status("GPTQ_ERR_TOO_LARGE")      # m > 8
+    a = list(ok); a[11] = 0
+    assert d(*a) == _status("GPTQ_ERR_BAD_SIZE")
+    a = list(ok); a[5] = 24
+    assert d(*a) == _status("GPTQ_ERR_BAD_GROUP")
+    a = list(ok); a[10] = 7
+    assert d(*a) == _status("GPTQ_ERR_BAD_DTYPE")
+    a = list(ok); a[14] = 3
+    assert d(*a) == _status("GPTQ_ERR_BAD_LEADING_DIM")  # ld_y < d_row
+    a = list(ok); a[3] = None
+    assert d(*a) == _status("GPTQ_ERR_NULL_POINTER")
