@@ -43,6 +43,11 @@ def parse():
                     help="quantize the columns in act-order (descending Hessian diagonal)")
     ap.add_argument("--traffic", default=os.path.join(ROOT, "profiles", "syrk_f16_attn4096_traffic.json"),
                     help="rocprofv3 --pmc derived HBM bytes of the dominant kernel (JSON), if any")
+    ap.add_argument("--packed-gemv", action="store_true",
+                    help="time the dequantizing product Y = X What^T from packed codes on a "
+                         "49152 x 12288 3-bit group-128 layer (one token) instead of the solver")
+    ap.add_argument("--gemv-m", type=int, default=1, help="rows of X for --packed-gemv (1..8)")
+    ap.add_argument("--gemv-iters", type=int, default=200, help="products per step for --packed-gemv")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="run two plain device-to-device copies of BYTES bytes and exit (the reference "
                          "kernel for scaling the FETCH_SIZE / WRITE_SIZE counters)")
@@ -90,6 +95,146 @@ def cpu_baseline(spec, W, X_chunk0, act_order=False):
             "stages_s": {"hessian": t_h, "factor": t_f, "loop": t_q}}
 
 
+GEMV_TRAFFIC = os.path.join(ROOT, "profiles", "dequant_gemv_fc49152_traffic.json")
+
+
+def packed_gemv_cpu_baseline(packed, bits, scales, zeros, group, X, d_col, d_row):
+    """The fp64 oracle's product on the sample rows given (the first rows of the
+    layer), scaled to all d_row rows."""
+    import oracle as O
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = len(os.sched_getaffinity(0))
+    rows = packed.shape[0]
+    t0 = time.perf_counter()
+    O.dequant_matmul(packed, bits, scales, zeros, group, X, d_col)
+    t = (time.perf_counter() - t0) * (d_row / rows)
+    return {"value": round(t * 1e6, 1), "unit": "us/product", "cores": int(threads), "kind": "oracle",
+            "sample": f"{rows} of {d_row} weight rows (x{d_row // rows}), scaled to the whole layer"}
+
+
+def packed_gemv(args):
+    """Y = X What^T from packed 3-bit codes (the consumer of the solver's codes) on
+    the 175B-class MLP shape.  Four distinct layers are cycled so that the packed
+    words (4 x 226 MB) come from HBM rather than the 256 MB last-level cache."""
+    import numpy as np
+    import torch
+    import post_weight_quantization_02_amd as G
+
+    d_row, d_col, bits, group, m = 49152, 12288, 3, 128, args.gemv_m
+    nlay = 4
+    dev = torch.device("cuda:0")
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(20221031)
+    words = G.gptq_packed_words_per_row(d_col, bits)
+    ng = d_col // group
+    layers = []
+    for _ in range(nlay):
+        codes = torch.randint(0, 1 << bits, (d_row, d_col), dtype=torch.uint8, device=dev, generator=gen)
+        packed = G.gptq_pack_codes(codes, bits)
+        del codes
+        scales = torch.rand(d_row, ng, device=dev, generator=gen) * 0.01 + 1e-3
+        zeros = torch.randint(0, 1 << bits, (d_row, ng), dtype=torch.int32, device=dev, generator=gen)
+        layers.append((packed, scales, zeros))
+    X = torch.randn(m, d_col, device=dev, generator=gen).to(torch.float16)
+    Y = torch.empty(m, d_row, dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def step():
+        for i in range(args.gemv_iters):
+            p, s, z = layers[i % nlay]
+            G.gptq_dequant_matmul(p, bits, s, z, group, X, d_col, Y=Y, stream=stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    e0.record(stream)
+    for _ in range(args.steps):
+        step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    n_launch = args.steps * args.gemv_iters
+    t_launch = e0.elapsed_time(e1) / 1e3 / n_launch
+    # algorithmic bytes of one product: packed words, per-group scale and zero, X once, Y once
+    alg = d_row * words * 4 + d_row * ng * 8 + m * d_col * 2 + m * d_row * 4
+    ach = alg / t_launch / 1e9
+    traffic = None
+    if os.path.exists(GEMV_TRAFFIC):
+        try:
+            with open(GEMV_TRAFFIC) as f:
+                tr = json.load(f)
+            if tr.get("m") == m:
+                traffic = tr.get("hbm_bytes_per_launch")
+        except Exception:
+            traffic = None
+
+    # context: the same product with the fp16 weights through torch (hipBLASLt / rocBLAS)
+    W16 = torch.randn(d_row, d_col, device=dev, generator=gen).to(torch.float16)
+    for _ in range(5):
+        torch.matmul(X, W16.t())
+    torch.cuda.synchronize()
+    f0, f1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    f0.record(stream)
+    for _ in range(50):
+        torch.matmul(X, W16.t())
+    f1.record(stream)
+    torch.cuda.synchronize()
+    t_f16 = f0.elapsed_time(f1) / 1e3 / 50
+    del W16
+    # context: a plain device copy of the same packed bytes (read + write)
+    src = torch.cat([p.view(-1) for p, _, _ in layers])
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    f0.record(stream)
+    for _ in range(10):
+        dst.copy_(src)
+    f1.record(stream)
+    torch.cuda.synchronize()
+    copy_gbs = 2 * src.numel() * 4 * 10 / (f0.elapsed_time(f1) / 1e3) / 1e9
+    del src, dst
+
+    out = {
+        "metric": "dequantizing product Y = X What^T from packed 3-bit codes, us per product",
+        "value": round(t_launch * 1e6, 3),
+        "unit": "us/product",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall / args.steps * 1e3, 4),
+        "higher_is_better": False,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "u32-packed 3-bit codes, f16 X, f32 accumulate",
+        "data": "synthetic",
+        "config": {"workload": f"fc_49152x12288: W 49152x12288 3-bit asymmetric, group 128, X {m}x12288 fp16, "
+                               f"{nlay} layers cycled",
+                   "d_row": d_row, "d_col": d_col, "bits": bits, "group_size": group, "m": m,
+                   "products_per_step": args.gemv_iters, "parallelism": "single-gpu"},
+        "roofline": {"bound": "hbm",
+                     "kernel": "gemv1_f16_kernel" if m == 1 else "dequant_gemv_f16_kernel",
+                     "achieved": round(ach, 1),
+                     "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(ach / PEAK_HBM_GBS, 4),
+                     "traffic": traffic, "algorithmic_bytes_per_launch": alg},
+        "fp16_weights_torch_matmul_us": round(t_f16 * 1e6, 3),
+        "speedup_vs_fp16_weights": round(t_f16 / t_launch, 3),
+        "plain_copy_gbs": round(copy_gbs, 1),
+    }
+    if not args.no_cpu_baseline:
+        log("bench: timing the fp64 oracle's product on a bounded sample (CPU)")
+        p, s, z = layers[0]
+        out["cpu_baseline"] = packed_gemv_cpu_baseline(
+            p[:8192].cpu().numpy().view(np.uint32), bits, s[:8192].cpu().numpy(),
+            z[:8192].cpu().numpy(), group, X.float().cpu().numpy(), d_col, d_row)
+        out["gpu_speedup_vs_cpu_oracle"] = round(out["cpu_baseline"]["value"] / (t_launch * 1e6), 1)
+    print(json.dumps(out), flush=True)
+
+
 def main():
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -107,6 +252,10 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         log(f"bench: copied {args.copy_calibration} bytes twice")
+        return
+
+    if args.packed_gemv:
+        packed_gemv(args)
         return
 
     import post_weight_quantization_02_amd as G

@@ -10,12 +10,16 @@
 // groups of positions stay contiguous; the product then gathers X in the same
 // order.
 //
-// Product (MI355X): HBM-bound on the packed words.  Each work-group stages the
-// m rows of X for a tile of columns in LDS (fp32, gathered through perm); each
-// wave owns kRows output rows and each lane whole 32-code chunks: it unpacks
-// the chunk's codes once per row, and per batch row adds
-// s * (sum c x - z * sum x) for each 16-code half (a half never spans two
-// groups, as group sizes are multiples of 16).  Lanes reduce by shuffles.
+// Product (MI355X): HBM-bound on the packed words.  Three kernels:
+//  - gemv1_f16_kernel: one row of fp16 X (the per-token product) whose width fits
+//    one LDS tile, groups of whole 32-code chunks; a persistent grid, codes turned
+//    into fp16 pairs and multiplied by v_dot2_f32_f16, loads one step ahead.
+//  - dequant_gemv_f16_kernel: the same pair arithmetic for 2..8 rows of fp16 X or
+//    wider rows, over column tiles of X staged in LDS.
+//  - dequant_matmul_kernel: the general case (fp32 X, or groups of 16 that split a
+//    chunk): codes unpacked to fp32, s * (sum c x - z * sum x) per 16-code half.
+// Each wave owns whole output rows and each lane whole chunks; lanes reduce by
+// shuffles, so every output is written once, with no atomics.
 #include "gptq_internal.h"
 
 namespace gptq {
@@ -160,6 +164,503 @@ __global__ __launch_bounds__(kThreads) void dequant_matmul_kernel(
   }
 }
 
+// ---------------------------------------------------------------------------
+// fp16 X, groups of whole chunks: codes as fp16 pairs and v_dot2_f32_f16.
+//
+// A pair takes two fields of one 32-bit word, one in each 16-bit half, at bit
+// offsets A and B (A, B <= 10 - bits).  OR-ing the masked word with an fp16
+// exponent of 25 - A (low half) and 25 - B (high half) gives the halves
+// 2^(10-A) + c_lo and 2^(10-B) + c_hi exactly, and one packed f16 subtraction
+// leaves c_lo and c_hi, so two codes cost one v_and_or_b32 and one v_pk_add_f16;
+// v_dot2_f32_f16 then multiplies them by the matching pair of X values (fp16 x
+// fp16 products are exact in fp32) and accumulates in fp32.  Each bit width has
+// its own order of the 16 pairs of a chunk (below); X is staged in LDS in that
+// order.
+// ---------------------------------------------------------------------------
+typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ uint32_t and_or(uint32_t v, uint32_t mask, uint32_t magic) {
+  uint32_t r;
+  asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(v), "s"(mask), "v"(magic));
+  return r;
+}
+
+template <int BITS, int A, int B>
+__device__ __forceinline__ h2 fpair(uint32_t v) {
+  static_assert(A + BITS <= 10 && B + BITS <= 10, "field must lie in the fp16 mantissa");
+  constexpr uint32_t m = (1u << BITS) - 1u;
+  constexpr uint32_t mask = (m << A) | ((m << B) << 16);
+  constexpr uint32_t magic = ((25u - A) << 10) | (((25u - B) << 10) << 16);
+  const h2 off = {(_Float16)(float)(1 << (10 - A)), (_Float16)(float)(1 << (10 - B))};
+  return __builtin_bit_cast(h2, and_or(v, mask, magic)) - off;
+}
+
+// chunk positions (lo, hi) of pair p, in the order unpack_pairs<BITS> returns them
+template <int BITS>
+__device__ __forceinline__ int2 pair_pos(int p) {
+  if constexpr (BITS == 4) {          // word k: (8k+j, 8k+4+j), j = 0..3
+    const int k = p >> 2, j = p & 3;
+    return make_int2(8 * k + j, 8 * k + 4 + j);
+  } else if constexpr (BITS == 2) {   // word k: (16k+j, 16k+8+j), j = 0..7
+    const int k = p >> 3, j = p & 7;
+    return make_int2(16 * k + j, 16 * k + 8 + j);
+  } else if constexpr (BITS == 8) {   // word k: (4k+j, 4k+2+j), j = 0..1
+    const int k = p >> 1, j = p & 1;
+    return make_int2(4 * k + j, 4 * k + 2 + j);
+  } else {                            // 3 bits: fields straddle words; see unpack_pairs<3>
+    const uint8_t lo[16] = {0, 1, 2, 3, 4, 22, 23, 24, 25, 11, 12, 13, 14, 15, 5, 10};
+    const uint8_t hi[16] = {16, 17, 18, 19, 20, 6, 7, 8, 9, 27, 28, 29, 30, 31, 21, 26};
+    return make_int2(lo[p], hi[p]);
+  }
+}
+
+template <int BITS>
+__device__ __forceinline__ void unpack_pairs(const uint32_t (&w)[BITS], h2 (&c)[16]) {
+  if constexpr (BITS == 4) {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const uint32_t s = w[k] >> 8;
+      c[4 * k + 0] = fpair<4, 0, 0>(w[k]);
+      c[4 * k + 1] = fpair<4, 4, 4>(w[k]);
+      c[4 * k + 2] = fpair<4, 0, 0>(s);
+      c[4 * k + 3] = fpair<4, 4, 4>(s);
+    }
+  } else if constexpr (BITS == 2) {
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      const uint32_t s = w[k] >> 10;
+      c[8 * k + 0] = fpair<2, 0, 0>(w[k]);
+      c[8 * k + 1] = fpair<2, 2, 2>(w[k]);
+      c[8 * k + 2] = fpair<2, 4, 4>(w[k]);
+      c[8 * k + 3] = fpair<2, 6, 6>(w[k]);
+      c[8 * k + 4] = fpair<2, 8, 8>(w[k]);
+      c[8 * k + 5] = fpair<2, 0, 0>(s);
+      c[8 * k + 6] = fpair<2, 2, 2>(s);
+      c[8 * k + 7] = fpair<2, 4, 4>(s);
+    }
+  } else if constexpr (BITS == 8) {
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      c[2 * k + 0] = fpair<8, 0, 0>(w[k]);
+      c[2 * k + 1] = fpair<8, 0, 0>(w[k] >> 8);
+    }
+  } else {
+    // A chunk is 96 bits: code e at stream bits 3e.  Halves of two words whose
+    // fields sit at equal offsets are merged with one byte permute; the two
+    // codes that straddle word boundaries pair with the two that straddle
+    // half-word boundaries.
+    const uint32_t w0 = w[0], w1 = w[1], w2 = w[2];
+    const uint32_t q1 = __builtin_amdgcn_perm(w1, w0, 0x07060100u);  // w0 bits 0-15 | w1 bits 16-31
+    const uint32_t q2 = __builtin_amdgcn_perm(w0, w2, 0x07060100u);  // w2 bits 0-15 | w0 bits 16-31
+    const uint32_t q3 = __builtin_amdgcn_perm(w2, w1, 0x07060100u);  // w1 bits 0-15 | w2 bits 16-31
+    c[0] = fpair<3, 0, 0>(q1);          // codes 0, 16
+    c[1] = fpair<3, 3, 3>(q1);          // 1, 17
+    c[2] = fpair<3, 6, 6>(q1);          // 2, 18
+    c[3] = fpair<3, 0, 0>(q1 >> 9);     // 3, 19
+    c[4] = fpair<3, 3, 3>(q1 >> 9);     // 4, 20
+    c[5] = fpair<3, 2, 2>(q2);          // 22, 6
+    c[6] = fpair<3, 5, 5>(q2);          // 23, 7
+    c[7] = fpair<3, 0, 0>(q2 >> 8);     // 24, 8
+    c[8] = fpair<3, 3, 3>(q2 >> 8);     // 25, 9
+    c[9] = fpair<3, 1, 1>(q3);          // 11, 27
+    c[10] = fpair<3, 4, 4>(q3);         // 12, 28
+    c[11] = fpair<3, 7, 7>(q3);         // 13, 29
+    c[12] = fpair<3, 0, 0>(q3 >> 10);   // 14, 30
+    c[13] = fpair<3, 3, 3>(q3 >> 10);   // 15, 31
+    // code 5 at stream bits 15-17, code 21 at 63-65
+    const uint32_t t = __builtin_amdgcn_alignbit(w2, w1, 31);
+    c[14] = fpair<3, 0, 1>(__builtin_amdgcn_alignbit(t, w0, 15));
+    // code 10 at stream bits 30-32, code 26 at 78-80
+    const uint32_t v = __builtin_amdgcn_alignbit(w1, w0, 30);
+    c[15] = fpair<3, 0, 6>(__builtin_amdgcn_perm(w2, v, 0x06050100u));
+  }
+}
+
+constexpr int kPairTileHalves = 16384;   // X staged per tile as fp16 pairs (32 KB)
+
+// Rows per wave: RG groups of R rows, R rows unpacked per chunk.  LDS: the X
+// tile as uint4 = 4 pairs, xp4[(b * 4 + q) * nchT + ch] holding pairs 4q .. 4q+3
+// of chunk ch (lane-consecutive 16-byte reads), and the fp32 sum of X over each
+// chunk for the zero term.
+template <int BITS, int M, int R, int RG>
+__global__ __launch_bounds__(kThreads) void dequant_gemv_f16_kernel(
+    const uint32_t* __restrict__ packed, int64_t ld_packed, const float* __restrict__ scales,
+    const int32_t* __restrict__ zeros, int64_t ngroups, int64_t G, const int32_t* __restrict__ perm,
+    int64_t d_row, int64_t d_col, const _Float16* __restrict__ X, int m, int64_t ld_x,
+    float* __restrict__ Y, int64_t ld_y) {
+  constexpr int CT = kPairTileHalves / M;   // columns per tile
+  constexpr int NCT = CT / 32;              // chunks per tile
+  __shared__ uint4 xp4[M * 4 * NCT];
+  __shared__ float xsum[M * NCT];
+  const int t = threadIdx.x, lane = t & 63;
+  const int w = __builtin_amdgcn_readfirstlane(t >> 6);   // wave index: uniform, so row bases are scalar
+  const int64_t rbase = ((int64_t)blockIdx.x * (kThreads / 64) + w) * (RG * R);
+  const int cpg = (int)(G >> 5);   // chunks per group
+  float y[RG * R][M];
+#pragma unroll
+  for (int i = 0; i < RG * R; ++i)
+#pragma unroll
+    for (int b = 0; b < M; ++b) y[i][b] = 0.f;
+  uint32_t* xp = reinterpret_cast<uint32_t*>(xp4);
+  for (int64_t c0 = 0; c0 < d_col; c0 += CT) {
+    const int64_t ncols = min<int64_t>(CT, d_col - c0);
+    const int nch = (int)((ncols + 31) / 32);
+    __syncthreads();
+    for (int i = t; i < M * nch * 16; i += kThreads) {
+      const int b = i / (nch * 16), rem = i % (nch * 16), ch = rem >> 4, p = rem & 15;
+      const int2 pp = pair_pos<BITS>(p);
+      const int64_t plo = c0 + ch * 32 + pp.x, phi = c0 + ch * 32 + pp.y;
+      _Float16 xl = (_Float16)0.f, xh = (_Float16)0.f;
+      if (b < m) {
+        if (plo < d_col) xl = X[(int64_t)b * ld_x + perm_idx(perm, plo, d_col)];
+        if (phi < d_col) xh = X[(int64_t)b * ld_x + perm_idx(perm, phi, d_col)];
+      }
+      const h2 v = {xl, xh};
+      xp[((b * 4 + (p >> 2)) * NCT + ch) * 4 + (p & 3)] = __builtin_bit_cast(uint32_t, v);
+    }
+    __syncthreads();
+    for (int i = t; i < M * nch; i += kThreads) {
+      const int b = i / nch, ch = i % nch;
+      float s = 0.f;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const uint4 v = xp4[(b * 4 + q) * NCT + ch];
+        const uint32_t u[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const h2 hv = __builtin_bit_cast(h2, u[e]);
+          s += (float)hv[0] + (float)hv[1];
+        }
+      }
+      xsum[b * NCT + ch] = s;
+    }
+    __syncthreads();
+    const int cg0 = (int)(c0 >> 5);
+    for (int ch = lane; ch < nch; ch += 64) {
+      const int cg = cg0 + ch;                              // chunk index in the row
+      const int gi = min(cg / cpg, (int)ngroups - 1);
+      float xs[M];
+#pragma unroll
+      for (int b = 0; b < M; ++b) xs[b] = xsum[b * NCT + ch];
+#pragma unroll
+      for (int g = 0; g < RG; ++g) {
+        uint32_t wd[R][BITS];
+        float sc[R], zc[R];
+#pragma unroll
+        for (int i = 0; i < R; ++i) {
+          // rows past the end read the last row; their sums are never written
+          const int64_t row = min<int64_t>(rbase + g * R + i, d_row - 1);
+          const uint32_t* pr = packed + row * ld_packed + (int64_t)cg * BITS;
+#pragma unroll
+          for (int k = 0; k < BITS; ++k) wd[i][k] = pr[k];
+          sc[i] = scales[row * ngroups + gi];
+          zc[i] = (float)zeros[row * ngroups + gi];
+        }
+#pragma unroll
+        for (int i = 0; i < R; ++i) {
+          h2 cp[16];
+          unpack_pairs<BITS>(wd[i], cp);
+#pragma unroll
+          for (int b = 0; b < M; ++b) {
+            float acc = 0.f;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+              const uint4 v = xp4[(b * 4 + q) * NCT + ch];
+              acc = __builtin_amdgcn_fdot2(cp[4 * q + 0], __builtin_bit_cast(h2, v.x), acc, false);
+              acc = __builtin_amdgcn_fdot2(cp[4 * q + 1], __builtin_bit_cast(h2, v.y), acc, false);
+              acc = __builtin_amdgcn_fdot2(cp[4 * q + 2], __builtin_bit_cast(h2, v.z), acc, false);
+              acc = __builtin_amdgcn_fdot2(cp[4 * q + 3], __builtin_bit_cast(h2, v.w), acc, false);
+            }
+            y[g * R + i][b] = fmaf(sc[i], fmaf(-zc[i], xs[b], acc), y[g * R + i][b]);
+          }
+        }
+      }
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < RG * R; ++i)
+#pragma unroll
+    for (int b = 0; b < M; ++b) {
+      float v = y[i][b];
+#pragma unroll
+      for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+      y[i][b] = v;
+    }
+  if (lane == 0) {
+#pragma unroll
+    for (int i = 0; i < RG * R; ++i)
+#pragma unroll
+      for (int b = 0; b < M; ++b)
+        if (b < m && rbase + i < d_row) Y[(int64_t)b * ld_y + rbase + i] = y[i][b];
+  }
+}
+
+// chunk position of half `hi` (0 = low, 1 = high) of pair p, in the order
+// unpack_pairs<BITS> returns the pairs (a compile-time constant once unrolled)
+template <int BITS>
+__device__ __forceinline__ constexpr int pair_code(int p, int hi) {
+  if (BITS == 4) return 8 * (p >> 2) + (p & 3) + 4 * hi;
+  if (BITS == 2) return 16 * (p >> 3) + (p & 7) + 8 * hi;
+  if (BITS == 8) return 4 * (p >> 1) + (p & 1) + 2 * hi;
+  const int lo3[16] = {0, 1, 2, 3, 4, 22, 23, 24, 25, 11, 12, 13, 14, 15, 5, 10};
+  const int hi3[16] = {16, 17, 18, 19, 20, 6, 7, 8, 9, 27, 28, 29, 30, 31, 21, 26};
+  return hi ? hi3[p] : lo3[p];
+}
+
+// the weight words are read once: loaded with the non-temporal hint (cache policy bit 1)
+constexpr int kStreamOnce = 2;
+
+template <int BITS>
+__device__ __forceinline__ void buffer_words(__amdgpu_buffer_rsrc_t r, int voff, int soff, uint32_t (&w)[BITS]) {
+  if constexpr (BITS == 2) {
+    const auto v = __builtin_amdgcn_raw_buffer_load_b64(r, voff, soff, kStreamOnce);
+    w[0] = v[0]; w[1] = v[1];
+  } else if constexpr (BITS == 3) {
+    const auto v = __builtin_amdgcn_raw_buffer_load_b96(r, voff, soff, kStreamOnce);
+    w[0] = v[0]; w[1] = v[1]; w[2] = v[2];
+  } else {
+#pragma unroll
+    for (int h = 0; h < BITS / 4; ++h) {
+      const auto v = __builtin_amdgcn_raw_buffer_load_b128(r, voff + 16 * h, soff, kStreamOnce);
+      w[4 * h] = v[0]; w[4 * h + 1] = v[1]; w[4 * h + 2] = v[2]; w[4 * h + 3] = v[3];
+    }
+  }
+}
+
+// One row of X whose pairs fit one LDS tile (d_col <= kPairTileHalves): a
+// persistent grid (as many work-groups as are resident at once) stages X once
+// per work-group, then each wave takes groups of R rows in a grid-stride loop.
+// A lane takes chunks lane, lane + 64, ...; the staged row is zero beyond d_col
+// up to a multiple of 64 chunks (nch64), so lanes past the end read a clamped
+// chunk and add nothing.  The words of the next (rows, chunk) step are loaded
+// before the current step is computed, and the first step's before X is staged.
+// Weights, scales and zeros come through buffer loads from a scalar base (the
+// step's first row) with one lane offset and a scalar offset per row, so the
+// loads cost no vector address arithmetic.  The group of chunk cg is
+// floor((2 cg + 1) * (0.5 / cpg)), exact in fp32 for cg < 2^15 (the distance to
+// the next integer, 1 / (2 cpg), exceeds the rounding error).
+// Dynamic LDS: nch64 * 4 uint4 of pairs, then nch64 floats of chunk sums.
+template <int BITS, int R>
+__global__ __launch_bounds__(kThreads) void gemv1_f16_kernel(
+    const uint32_t* __restrict__ packed, int64_t ld_packed, const float* __restrict__ scales,
+    const int32_t* __restrict__ zeros, int64_t ngroups, float half_inv_cpg, const int32_t* __restrict__ perm,
+    int64_t d_row, int64_t d_col, const _Float16* __restrict__ X, float* __restrict__ Y) {
+  extern __shared__ uint4 lds_dyn[];
+  const int t = threadIdx.x, lane = t & 63;
+  const int w = __builtin_amdgcn_readfirstlane(t >> 6);
+  const int nch = (int)((d_col + 31) / 32);
+  const int nch64 = (nch + 63) & ~63;
+  uint4* xp4 = lds_dyn;
+  float* xsum = reinterpret_cast<float*>(lds_dyn + 4 * nch64);
+  const int J = nch64 >> 6;                                   // chunk steps per row group
+  const int64_t ngrp = (d_row + R - 1) / R;
+  const int64_t nwaves = (int64_t)gridDim.x * (kThreads / 64);
+  int64_t q = (int64_t)blockIdx.x * (kThreads / 64) + w;
+  const int ldb = (int)(ld_packed * 4), ngb = (int)(ngroups * 4);   // row strides in bytes
+
+  // raw words only: converting a loaded value here would wait for the load
+  struct Step { uint32_t wd[R][BITS]; uint32_t sc[R], zc[R]; };
+  auto load = [&](int64_t qq, int jj, Step& st) {
+    const int cg = min(lane + 64 * jj, nch - 1);
+    const int gi = min((int)((float)(2 * cg + 1) * half_inv_cpg), (int)ngroups - 1);
+    const int64_t row0 = qq * R;
+    const int last = (int)min<int64_t>(R - 1, d_row - 1 - row0);   // rows past the end read the last row
+    const __amdgpu_buffer_rsrc_t rp =
+        __builtin_amdgcn_make_buffer_rsrc((void*)(packed + row0 * ld_packed), (short)0, 0x7FFFFFFF, 0x00020000);
+    const __amdgpu_buffer_rsrc_t rs =
+        __builtin_amdgcn_make_buffer_rsrc((void*)(scales + row0 * ngroups), (short)0, 0x7FFFFFFF, 0x00020000);
+    const __amdgpu_buffer_rsrc_t rz =
+        __builtin_amdgcn_make_buffer_rsrc((void*)(zeros + row0 * ngroups), (short)0, 0x7FFFFFFF, 0x00020000);
+#pragma unroll
+    for (int i = 0; i < R; ++i) {
+      const int ri = min(i, last);
+      buffer_words<BITS>(rp, cg * BITS * 4, ri * ldb, st.wd[i]);
+      st.sc[i] = __builtin_amdgcn_raw_buffer_load_b32(rs, gi * 4, ri * ngb, 0);
+      st.zc[i] = __builtin_amdgcn_raw_buffer_load_b32(rz, gi * 4, ri * ngb, 0);
+    }
+  };
+  Step cur, nxt;
+  int j = 0;
+  if (q < ngrp) load(q, j, cur);
+
+  // stage X by whole chunks: 32 values, their 16 pairs, and the chunk's sum
+  const bool vec = perm == nullptr && (reinterpret_cast<uintptr_t>(X) & 15) == 0;
+  const h2 ones = {(_Float16)1.f, (_Float16)1.f};
+  for (int ch = t; ch < nch64; ch += kThreads) {
+    const int64_t c0 = (int64_t)ch * 32;
+    _Float16 xv[32];
+    if (vec && c0 + 32 <= d_col) {
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const uint4 u = *reinterpret_cast<const uint4*>(X + c0 + 8 * v);
+        const uint32_t uu[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const h2 hv = __builtin_bit_cast(h2, uu[e]);
+          xv[8 * v + 2 * e] = hv[0];
+          xv[8 * v + 2 * e + 1] = hv[1];
+        }
+      }
+    } else {
+#pragma unroll
+      for (int e = 0; e < 32; ++e) xv[e] = c0 + e < d_col ? X[perm_idx(perm, c0 + e, d_col)] : (_Float16)0.f;
+    }
+    uint32_t pr[16];
+    float s = 0.f;
+#pragma unroll
+    for (int p = 0; p < 16; ++p) {
+      const h2 v = {xv[pair_code<BITS>(p, 0)], xv[pair_code<BITS>(p, 1)]};
+      pr[p] = __builtin_bit_cast(uint32_t, v);
+      s = __builtin_amdgcn_fdot2(v, ones, s, false);
+    }
+#pragma unroll
+    for (int qq = 0; qq < 4; ++qq) xp4[qq * nch64 + ch] = make_uint4(pr[4 * qq], pr[4 * qq + 1], pr[4 * qq + 2], pr[4 * qq + 3]);
+    xsum[ch] = s;
+  }
+  __syncthreads();
+  if (q >= ngrp) return;
+
+  float y[R];
+#pragma unroll
+  for (int i = 0; i < R; ++i) y[i] = 0.f;
+  // one (rows, chunk) step on st: the dot products, then at the last chunk the
+  // lane reduction and the store
+  auto compute = [&](const Step& st, int64_t qq, int jj) {
+    const int ch = lane + 64 * jj;
+    uint4 xv[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) xv[k] = xp4[k * nch64 + ch];
+    const float xs = xsum[ch];
+#pragma unroll
+    for (int i = 0; i < R; ++i) {
+      h2 cp[16];
+      unpack_pairs<BITS>(st.wd[i], cp);
+      float acc = 0.f;
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        acc = __builtin_amdgcn_fdot2(cp[4 * k + 0], __builtin_bit_cast(h2, xv[k].x), acc, false);
+        acc = __builtin_amdgcn_fdot2(cp[4 * k + 1], __builtin_bit_cast(h2, xv[k].y), acc, false);
+        acc = __builtin_amdgcn_fdot2(cp[4 * k + 2], __builtin_bit_cast(h2, xv[k].z), acc, false);
+        acc = __builtin_amdgcn_fdot2(cp[4 * k + 3], __builtin_bit_cast(h2, xv[k].w), acc, false);
+      }
+      const float sc = __builtin_bit_cast(float, st.sc[i]), zc = (float)(int32_t)st.zc[i];
+      y[i] = fmaf(sc, fmaf(-zc, xs, acc), y[i]);
+    }
+    if (jj == J - 1) {
+#pragma unroll
+      for (int i = 0; i < R; ++i) {
+        float v = y[i];
+#pragma unroll
+        for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+        if (lane == 0 && qq * R + i < d_row) Y[qq * R + i] = v;
+        y[i] = 0.f;
+      }
+    }
+  };
+  // two step buffers in turn: the loads of one are in flight while the other is
+  // computed, with no register copies between them.  The prefetch is issued on
+  // every step (the last one re-reads its own step) so that the wait before
+  // each compute counts exactly the newer loads.
+  while (true) {
+    int64_t qn = q;
+    int jn = j + 1;
+    if (jn == J) { jn = 0; qn += nwaves; }
+    bool more = qn < ngrp;
+    load(more ? qn : q, more ? jn : j, nxt);
+    compute(cur, q, j);
+    if (!more) break;
+    q = qn;
+    j = jn;
+    qn = q;
+    jn = j + 1;
+    if (jn == J) { jn = 0; qn += nwaves; }
+    more = qn < ngrp;
+    load(more ? qn : q, more ? jn : j, cur);
+    compute(nxt, q, j);
+    if (!more) break;
+    q = qn;
+    j = jn;
+  }
+}
+
+// rows unpacked together per chunk and the widest row-group count per wave
+template <int M>
+constexpr int gemv_rows() { return M <= 4 ? 4 : 2; }
+template <int M>
+constexpr int gemv_groups_max() { return M == 1 ? 4 : (M == 2 ? 2 : 1); }
+
+template <int BITS, int M, int RG>
+void gemv_f16_launch_rg(const uint32_t* packed, int64_t ld_packed, const float* scales, const int32_t* zeros,
+                        int64_t ngroups, int64_t G, const int32_t* perm, int64_t d_row, int64_t d_col,
+                        const _Float16* X, int m, int64_t ld_x, float* Y, int64_t ld_y, hipStream_t s) {
+  constexpr int R = gemv_rows<M>();
+  hipLaunchKernelGGL((dequant_gemv_f16_kernel<BITS, M, R, RG>),
+                     dim3((unsigned)cdiv(d_row, (kThreads / 64) * R * RG)), dim3(kThreads), 0, s, packed,
+                     ld_packed, scales, zeros, ngroups, G, perm, d_row, d_col, X, m, ld_x, Y, ld_y);
+}
+
+// the most rows per wave (up to RGM groups of R) that still gives at least 1024 work-groups
+template <int BITS, int M>
+void gemv_f16_launch_m(const uint32_t* packed, int64_t ld_packed, const float* scales, const int32_t* zeros,
+                       int64_t ngroups, int64_t G, const int32_t* perm, int64_t d_row, int64_t d_col,
+                       const _Float16* X, int m, int64_t ld_x, float* Y, int64_t ld_y, hipStream_t s) {
+  constexpr int R = gemv_rows<M>(), RGM = gemv_groups_max<M>();
+  int rg = RGM;
+  while (rg > 1 && cdiv(d_row, (kThreads / 64) * R * rg) < 1024) rg >>= 1;
+  if constexpr (RGM >= 4) {
+    if (rg == 4) {
+      gemv_f16_launch_rg<BITS, M, 4>(packed, ld_packed, scales, zeros, ngroups, G, perm, d_row, d_col, X, m, ld_x, Y, ld_y, s);
+      return;
+    }
+  }
+  if constexpr (RGM >= 2) {
+    if (rg == 2) {
+      gemv_f16_launch_rg<BITS, M, 2>(packed, ld_packed, scales, zeros, ngroups, G, perm, d_row, d_col, X, m, ld_x, Y, ld_y, s);
+      return;
+    }
+  }
+  gemv_f16_launch_rg<BITS, M, 1>(packed, ld_packed, scales, zeros, ngroups, G, perm, d_row, d_col, X, m, ld_x, Y, ld_y, s);
+}
+
+constexpr int kGemv1Rows = 4;
+
+// the persistent one-row kernel: as many work-groups as are resident at once
+// (occupancy from its registers and this launch's LDS), at most one per group
+// of rows per wave
+template <int BITS>
+hipError_t gemv1_f16_launch(const uint32_t* packed, int64_t ld_packed, const float* scales, const int32_t* zeros,
+                            int64_t ngroups, int64_t G, const int32_t* perm, int64_t d_row, int64_t d_col,
+                            const _Float16* X, float* Y, hipStream_t s) {
+  const auto kern = gemv1_f16_kernel<BITS, kGemv1Rows>;
+  const int64_t nch64 = cdiv(cdiv(d_col, 32), 64) * 64;
+  const size_t lds = (size_t)nch64 * (4 * sizeof(uint4) + sizeof(float));
+  int dev = 0, cus = 0, per_cu = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  if (e == hipSuccess) e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kern, kThreads, lds);
+  if (e != hipSuccess) return e;
+  const int64_t groups = cdiv(d_row, kGemv1Rows);
+  const int64_t wgs = std::max<int64_t>(1, std::min<int64_t>((int64_t)std::max(per_cu, 1) * cus,
+                                                              cdiv(groups, kThreads / 64)));
+  const float half_inv_cpg = 0.5f / (float)(G >> 5);
+  hipLaunchKernelGGL(kern, dim3((unsigned)wgs), dim3(kThreads), lds, s, packed, ld_packed, scales, zeros,
+                     ngroups, half_inv_cpg, perm, d_row, d_col, X, Y);
+  return hipGetLastError();
+}
+
+template <int BITS>
+hipError_t gemv_f16_launch(const uint32_t* packed, int64_t ld_packed, const float* scales, const int32_t* zeros,
+                           int64_t ngroups, int64_t G, const int32_t* perm, int64_t d_row, int64_t d_col,
+                           const _Float16* X, int m, int64_t ld_x, float* Y, int64_t ld_y, hipStream_t s) {
+  if (m == 1 && d_col <= kPairTileHalves)
+    return gemv1_f16_launch<BITS>(packed, ld_packed, scales, zeros, ngroups, G, perm, d_row, d_col, X, Y, s);
+  if (m <= 1) gemv_f16_launch_m<BITS, 1>(packed, ld_packed, scales, zeros, ngroups, G, perm, d_row, d_col, X, m, ld_x, Y, ld_y, s);
+  else if (m <= 2) gemv_f16_launch_m<BITS, 2>(packed, ld_packed, scales, zeros, ngroups, G, perm, d_row, d_col, X, m, ld_x, Y, ld_y, s);
+  else if (m <= 4) gemv_f16_launch_m<BITS, 4>(packed, ld_packed, scales, zeros, ngroups, G, perm, d_row, d_col, X, m, ld_x, Y, ld_y, s);
+  else gemv_f16_launch_m<BITS, 8>(packed, ld_packed, scales, zeros, ngroups, G, perm, d_row, d_col, X, m, ld_x, Y, ld_y, s);
+  return hipGetLastError();
+}
+
 template <int BITS, typename T>
 hipError_t dequant_launch_m(const uint32_t* packed, int64_t ld_packed, const float* scales,
                             const int32_t* zeros, int64_t ngroups, int64_t G, const int32_t* perm,
@@ -215,6 +716,16 @@ hipError_t dequant_matmul_launch(const uint32_t* packed, int64_t ld_packed, int 
                                  int64_t ld_y, hipStream_t s) {
   const int64_t G = group ? group : cdiv(d_col, 32) * 32;   // one group: every position maps to 0
   const int64_t ngroups = group ? cdiv(d_col, group) : 1;
+  if (x_dtype == 1 && G % 32 == 0) {   // every chunk inside one group: the fp16-pair kernel
+    const _Float16* Xh = (const _Float16*)X;
+    switch (bits) {
+      case 2: return gemv_f16_launch<2>(packed, ld_packed, scales, zeros, ngroups, G, perm, d_row, d_col, Xh, m, ld_x, Y, ld_y, s);
+      case 3: return gemv_f16_launch<3>(packed, ld_packed, scales, zeros, ngroups, G, perm, d_row, d_col, Xh, m, ld_x, Y, ld_y, s);
+      case 4: return gemv_f16_launch<4>(packed, ld_packed, scales, zeros, ngroups, G, perm, d_row, d_col, Xh, m, ld_x, Y, ld_y, s);
+      case 8: return gemv_f16_launch<8>(packed, ld_packed, scales, zeros, ngroups, G, perm, d_row, d_col, Xh, m, ld_x, Y, ld_y, s);
+      default: return hipErrorInvalidValue;
+    }
+  }
   if (x_dtype == 1)
     return dequant_launch_t<_Float16>(bits, packed, ld_packed, scales, zeros, ngroups, G, perm, d_row, d_col,
                                       (const _Float16*)X, m, ld_x, Y, ld_y, s);

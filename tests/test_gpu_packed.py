@@ -66,7 +66,19 @@ def _matmul_case(seed, d_row, d_col, bits, group, m, xdtype, ordered):
 
 MM_CASES = [
     # seed, d_row, d_col, bits, group, m, x dtype, ordered
+    # fp16 X with groups of whole 32-code chunks: the fp16-pair kernel
     (1, 300, 4096, 4, 128, 1, np.float16, False),
+    (11, 70001, 64, 4, 0, 1, np.float16, False),          # four row groups per wave
+    (12, 40000, 200, 3, 64, 1, np.float16, True),          # two row groups, ragged chunk
+    (13, 37, 20000, 3, 128, 1, np.float16, True),          # two column tiles, partial group
+    (14, 50, 9000, 2, 0, 2, np.float16, False),            # two column tiles at m = 2
+    (15, 21, 1000, 8, 32, 3, np.float16, False),
+    (16, 19, 5000, 2, 256, 7, np.float16, True),
+    (17, 1, 32, 3, 32, 4, np.float16, False),
+    (18, 5000, 3000, 2, 64, 1, np.float16, False),
+    (19, 999, 16384, 8, 128, 1, np.float16, True),         # one row of X filling the whole tile
+    (20, 4099, 16416, 4, 32, 1, np.float16, False),        # one chunk past the tile
+    # the general kernel: fp32 X, or groups that split a chunk
     (2, 17, 100, 3, 16, 3, np.float32, False),
     (3, 64, 12288, 3, 128, 8, np.float16, True),
     (4, 1, 32, 2, 0, 1, np.float32, False),
