@@ -217,7 +217,7 @@ def packed_gemv(args):
                    "d_row": d_row, "d_col": d_col, "bits": bits, "group_size": group, "m": m,
                    "products_per_step": args.gemv_iters, "parallelism": "single-gpu"},
         "roofline": {"bound": "hbm",
-                     "kernel": "gemv1_f16_kernel" if m == 1 else "dequant_gemv_f16_kernel",
+                     "kernel": "gemv1_f16_kernel" if m == 1 else "gemm_mfma_f16_kernel",
                      "achieved": round(ach, 1),
                      "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(ach / PEAK_HBM_GBS, 4),
                      "traffic": traffic, "algorithmic_bytes_per_launch": alg},

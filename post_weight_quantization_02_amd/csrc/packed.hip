@@ -14,8 +14,10 @@
 //  - gemv1_f16_kernel: one row of fp16 X (the per-token product) whose width fits
 //    one LDS tile, groups of whole 32-code chunks; a persistent grid, codes turned
 //    into fp16 pairs and multiplied by v_dot2_f32_f16, loads one step ahead.
-//  - dequant_gemv_f16_kernel: the same pair arithmetic for 2..8 rows of fp16 X or
-//    wider rows, over column tiles of X staged in LDS.
+//  - gemm_mfma_f16_kernel: 2..8 rows of fp16 X (or one wider row), one group per
+//    128 columns: the same pairs as the A operand of v_mfma_f32_16x16x32_f16.
+//  - dequant_gemv_f16_kernel: the pair arithmetic with v_dot2 for groups of 32 or 64,
+//    over column tiles of X staged in LDS.
 //  - dequant_matmul_kernel: the general case (fp32 X, or groups of 16 that split a
 //    chunk): codes unpacked to fp32, s * (sum c x - z * sum x) per 16-code half.
 // Each wave owns whole output rows and each lane whole chunks; lanes reduce by
@@ -583,6 +585,217 @@ __global__ __launch_bounds__(kThreads) void gemv1_f16_kernel(
   }
 }
 
+// ---------------------------------------------------------------------------
+// 2..16 rows of fp16 X: the product on the matrix cores.
+//
+// v_mfma_f32_16x16x32_f16 with A = 16 weight rows and B = up to 16 rows of X.
+// Lane l = (i = l % 16, kb = l / 16) holds eight k-slots of A's row i and the same
+// eight k-slots of B's column i; the k-slots of lane group kb are codes of chunk
+// 4s + kb in the pair order of unpack_pairs (A) and the X values of the same
+// columns (B, built from X in L2 with one byte permute per pair), so the four
+// lane groups cover 128 columns per step and four instructions per row block.
+// A fifth set with A = ones gives every column's sum of X over the step, for the
+// zero term; one group covers the whole step (group 0 or a multiple of 128), so
+// scale and zero are applied once per step to the fp32 accumulators.  A
+// work-group takes 32 rows (two 16-row blocks, B built once for both) and its four
+// waves split the row's steps; their partial sums meet in LDS and are added in a
+// fixed order.  The D layout puts rows 4 kb + r (r = 0..3) of batch row i in lane
+// l.  Loads run one step ahead as in gemv1_f16_kernel.  Rows past the end, batch
+// rows past m and chunks past the row compute on clamped data and are never
+// stored (X is zero past d_col).
+// ---------------------------------------------------------------------------
+typedef _Float16 h8 __attribute__((ext_vector_type(8)));
+typedef float f4v __attribute__((ext_vector_type(4)));
+
+template <int BITS, bool GATHER>
+__global__ __launch_bounds__(kThreads) void gemm_mfma_f16_kernel(
+    const uint32_t* __restrict__ packed, int64_t ld_packed, const float* __restrict__ scales,
+    const int32_t* __restrict__ zeros, int64_t ngroups, int64_t G, const int32_t* __restrict__ perm,
+    int64_t d_row, int64_t d_col, const _Float16* __restrict__ X, int m, int64_t ld_x,
+    float* __restrict__ Y, int64_t ld_y) {
+  __shared__ float red[kThreads / 64][8][64];               // partial sums of the four waves
+  const int t = threadIdx.x, lane = t & 63, li = lane & 15, kb = lane >> 4;
+  const int w = __builtin_amdgcn_readfirstlane(t >> 6);
+  const int dc = (int)d_col;                                  // widths and offsets fit 32 bits (checked at launch)
+  const int nch = (dc + 31) / 32;
+  const int NS = (nch + 3) / 4;                               // 128-column steps per row
+  const int NSW = (NS + 3) / 4;                               // steps per wave
+  const int s_lo = min(w * NSW, NS), s_hi = min(s_lo + NSW, NS);
+  const int64_t nbp = (d_row + 31) / 32;                      // pairs of 16-row blocks
+  const int jx = min(li, m - 1);                              // batch row whose X this lane loads
+  const int xoff = jx * (int)ld_x;
+  const int gstep = G >= d_col ? 0 : (int)(G / 128);          // steps per group (G a multiple of 128)
+  const int ldb = (int)(ld_packed * 4), ngb = (int)(ngroups * 4);
+  const h2 one2 = {(_Float16)1.f, (_Float16)1.f};
+  const h8 ones = {one2[0], one2[1], one2[0], one2[1], one2[0], one2[1], one2[0], one2[1]};
+  // X's exact extent: a 16-byte read past its end returns zeros
+  const __amdgpu_buffer_rsrc_t rx =
+      __builtin_amdgcn_make_buffer_rsrc((void*)X, (short)0, (int)(((int64_t)(m - 1) * ld_x + d_col) * 2), 0x00020000);
+
+  struct Step { uint32_t wd[2][BITS]; uint32_t xr[16]; uint32_t sc[2][4], zc[2][4]; };
+  for (int64_t bp = blockIdx.x; bp < nbp; bp += gridDim.x) {
+    const int64_t r0 = bp * 32;
+    const int last = (int)min<int64_t>(31, d_row - 1 - r0);   // rows past the end read the last row
+    const __amdgpu_buffer_rsrc_t rp =
+        __builtin_amdgcn_make_buffer_rsrc((void*)(packed + r0 * ld_packed), (short)0, 0x7FFFFFFF, 0x00020000);
+    const __amdgpu_buffer_rsrc_t rs =
+        __builtin_amdgcn_make_buffer_rsrc((void*)(scales + r0 * ngroups), (short)0, 0x7FFFFFFF, 0x00020000);
+    const __amdgpu_buffer_rsrc_t rz =
+        __builtin_amdgcn_make_buffer_rsrc((void*)(zeros + r0 * ngroups), (short)0, 0x7FFFFFFF, 0x00020000);
+    int vw[2], vs[2][4];                                      // this lane's row offsets, in bytes
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb) {
+      vw[rb] = min(16 * rb + li, last) * ldb;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) vs[rb][r] = min(16 * rb + 4 * kb + r, last) * ngb;
+    }
+    auto load = [&](int s, Step& st) {
+      const int chunk = 4 * s + kb;
+      const int cl = min(chunk, nch - 1);
+      const int g = gstep == 0 ? 0 : min(s / gstep, (int)ngroups - 1);
+#pragma unroll
+      for (int rb = 0; rb < 2; ++rb) {
+        buffer_words<BITS>(rp, vw[rb] + cl * BITS * 4, 0, st.wd[rb]);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          st.sc[rb][r] = __builtin_amdgcn_raw_buffer_load_b32(rs, vs[rb][r] + g * 4, 0, 0);
+          st.zc[rb][r] = __builtin_amdgcn_raw_buffer_load_b32(rz, vs[rb][r] + g * 4, 0, 0);
+        }
+      }
+      const int c0 = chunk * 32;
+      if constexpr (!GATHER) {
+        const int vo = (xoff + c0) * 2;
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          const auto u = __builtin_amdgcn_raw_buffer_load_b128(rx, vo + 16 * v, 0, 0);
+          st.xr[4 * v] = u[0]; st.xr[4 * v + 1] = u[1]; st.xr[4 * v + 2] = u[2]; st.xr[4 * v + 3] = u[3];
+        }
+      } else {
+        // element by element, through the quantization order if any; zero past d_col
+        const _Float16* xrow = X + xoff;
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const int p0 = c0 + 2 * e, p1 = p0 + 1;
+          const int q0 = perm ? min(max(perm[min(p0, dc - 1)], 0), dc - 1) : min(p0, dc - 1);
+          const int q1 = perm ? min(max(perm[min(p1, dc - 1)], 0), dc - 1) : min(p1, dc - 1);
+          const _Float16 a = p0 < dc ? xrow[q0] : (_Float16)0.f;
+          const _Float16 bb = p1 < dc ? xrow[q1] : (_Float16)0.f;
+          const h2 v = {a, bb};
+          st.xr[e] = __builtin_bit_cast(uint32_t, v);
+        }
+      }
+    };
+    f4v y[2];
+    y[0] = (f4v){0.f, 0.f, 0.f, 0.f};
+    y[1] = y[0];
+    auto compute = [&](const Step& st, int s) {
+      uint32_t xr[16];
+#pragma unroll
+      for (int e = 0; e < 16; ++e) xr[e] = st.xr[e];
+      if constexpr (!GATHER) {
+        // the row's last chunk: zero the values past d_col (they belong to the next row)
+        const int valid = dc - (4 * s + kb) * 32;
+        if (valid < 32) {
+#pragma unroll
+          for (int e = 0; e < 16; ++e)
+            xr[e] &= (2 * e + 1 < valid ? 0xFFFFFFFFu : 0u) | (2 * e < valid ? 0x0000FFFFu : 0u);
+        }
+      }
+      // B: the step's X values in pair order
+      uint32_t xp[16];
+#pragma unroll
+      for (int p = 0; p < 16; ++p) {
+        const int lo = pair_code<BITS>(p, 0), hi = pair_code<BITS>(p, 1);
+        const uint32_t sel = (uint32_t)(2 * (lo & 1)) | ((uint32_t)(2 * (lo & 1) + 1) << 8) |
+                             ((uint32_t)(4 + 2 * (hi & 1)) << 16) | ((uint32_t)(4 + 2 * (hi & 1) + 1) << 24);
+        xp[p] = __builtin_amdgcn_perm(xr[hi >> 1], xr[lo >> 1], sel);
+      }
+      h8 bq[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const h2 a0 = __builtin_bit_cast(h2, xp[4 * q]), a1 = __builtin_bit_cast(h2, xp[4 * q + 1]);
+        const h2 a2 = __builtin_bit_cast(h2, xp[4 * q + 2]), a3 = __builtin_bit_cast(h2, xp[4 * q + 3]);
+        bq[q] = (h8){a0[0], a0[1], a1[0], a1[1], a2[0], a2[1], a3[0], a3[1]};
+      }
+      f4v dx = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int q = 0; q < 4; ++q) dx = __builtin_amdgcn_mfma_f32_16x16x32_f16(ones, bq[q], dx, 0, 0, 0);
+#pragma unroll
+      for (int rb = 0; rb < 2; ++rb) {
+        h2 cp[16];
+        unpack_pairs<BITS>(st.wd[rb], cp);
+        f4v d = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const h8 aq = {cp[4 * q][0], cp[4 * q][1], cp[4 * q + 1][0], cp[4 * q + 1][1],
+                         cp[4 * q + 2][0], cp[4 * q + 2][1], cp[4 * q + 3][0], cp[4 * q + 3][1]};
+          d = __builtin_amdgcn_mfma_f32_16x16x32_f16(aq, bq[q], d, 0, 0, 0);
+        }
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const float sc = __builtin_bit_cast(float, st.sc[rb][r]), zc = (float)(int32_t)st.zc[rb][r];
+          y[rb][r] = fmaf(sc, fmaf(-zc, dx[r], d[r]), y[rb][r]);
+        }
+      }
+    };
+    // this wave's steps, two step buffers in turn (the prefetch is issued on every
+    // step, the last one re-reading its own step, so each wait counts exactly)
+    if (s_lo < s_hi) {
+      Step cur, nxt;
+      int s = s_lo;
+      load(s, cur);
+      while (true) {
+        bool more = s + 1 < s_hi;
+        load(more ? s + 1 : s, nxt);
+        compute(cur, s);
+        if (!more) break;
+        ++s;
+        more = s + 1 < s_hi;
+        load(more ? s + 1 : s, cur);
+        compute(nxt, s);
+        if (!more) break;
+        ++s;
+      }
+    }
+    // the four waves' partial sums, added in a fixed order
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) red[w][4 * rb + r][lane] = y[rb][r];
+    __syncthreads();
+    if (w == 0 && li < m) {
+#pragma unroll
+      for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const float v = ((red[0][4 * rb + r][lane] + red[1][4 * rb + r][lane]) + red[2][4 * rb + r][lane]) +
+                          red[3][4 * rb + r][lane];
+          const int64_t row = r0 + 16 * rb + 4 * kb + r;
+          if (row < d_row) Y[(int64_t)li * ld_y + row] = v;
+        }
+    }
+    __syncthreads();
+  }
+}
+
+template <int BITS>
+hipError_t gemm_mfma_f16_launch(const uint32_t* packed, int64_t ld_packed, const float* scales,
+                                const int32_t* zeros, int64_t ngroups, int64_t G, const int32_t* perm,
+                                int64_t d_row, int64_t d_col, const _Float16* X, int m, int64_t ld_x, float* Y,
+                                int64_t ld_y, hipStream_t s) {
+  const bool gather = perm != nullptr || (reinterpret_cast<uintptr_t>(X) & 15) != 0 || (ld_x & 7) != 0;
+  const auto kern = gather ? gemm_mfma_f16_kernel<BITS, true> : gemm_mfma_f16_kernel<BITS, false>;
+  int dev = 0, cus = 0, per_cu = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  if (e == hipSuccess) e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kern, kThreads, 0);
+  if (e != hipSuccess) return e;
+  const int64_t wgs = std::max<int64_t>(1, std::min<int64_t>((int64_t)std::max(per_cu, 1) * cus, cdiv(d_row, 32)));
+  hipLaunchKernelGGL(kern, dim3((unsigned)wgs), dim3(kThreads), 0, s, packed, ld_packed, scales, zeros, ngroups,
+                     G, perm, d_row, d_col, X, m, ld_x, Y, ld_y);
+  return hipGetLastError();
+}
+
 // rows unpacked together per chunk and the widest row-group count per wave
 template <int M>
 constexpr int gemv_rows() { return M <= 4 ? 4 : 2; }
@@ -654,6 +867,13 @@ hipError_t gemv_f16_launch(const uint32_t* packed, int64_t ld_packed, const floa
                            const _Float16* X, int m, int64_t ld_x, float* Y, int64_t ld_y, hipStream_t s) {
   if (m == 1 && d_col <= kPairTileHalves)
     return gemv1_f16_launch<BITS>(packed, ld_packed, scales, zeros, ngroups, G, perm, d_row, d_col, X, Y, s);
+  // the matrix-core kernel: one group per 128-column step, and 32-bit buffer offsets
+  const bool one_group_per_step = G % 128 == 0 || G >= d_col;
+  const bool offsets_fit = ((int64_t)(m - 1) * ld_x + d_col) * 2 < (int64_t(1) << 31) &&
+                           (32 * ld_packed + BITS) * 4 < (int64_t(1) << 31) && 32 * ngroups * 4 < (int64_t(1) << 31);
+  if (one_group_per_step && offsets_fit)
+    return gemm_mfma_f16_launch<BITS>(packed, ld_packed, scales, zeros, ngroups, G, perm, d_row, d_col, X, m, ld_x,
+                                      Y, ld_y, s);
   if (m <= 1) gemv_f16_launch_m<BITS, 1>(packed, ld_packed, scales, zeros, ngroups, G, perm, d_row, d_col, X, m, ld_x, Y, ld_y, s);
   else if (m <= 2) gemv_f16_launch_m<BITS, 2>(packed, ld_packed, scales, zeros, ngroups, G, perm, d_row, d_col, X, m, ld_x, Y, ld_y, s);
   else if (m <= 4) gemv_f16_launch_m<BITS, 4>(packed, ld_packed, scales, zeros, ngroups, G, perm, d_row, d_col, X, m, ld_x, Y, ld_y, s);

@@ -78,6 +78,13 @@ MM_CASES = [
     (18, 5000, 3000, 2, 64, 1, np.float16, False),
     (19, 999, 16384, 8, 128, 1, np.float16, True),         # one row of X filling the whole tile
     (20, 4099, 16416, 4, 32, 1, np.float16, False),        # one chunk past the tile
+    # 2..8 rows of fp16 X with one group per 128 columns: the matrix-core kernel
+    (21, 1000, 4096, 4, 128, 8, np.float16, False),
+    (22, 300, 2048, 8, 128, 4, np.float16, False),
+    (23, 20000, 256, 3, 128, 2, np.float16, False),        # many row blocks per wave
+    (24, 77, 4099, 4, 0, 6, np.float16, False),            # odd width: X read element by element
+    (25, 45, 3000, 3, 256, 5, np.float16, True),           # act-order gather
+    (26, 33, 40, 2, 64, 2, np.float16, False),             # one group wider than the row
     # the general kernel: fp32 X, or groups that split a chunk
     (2, 17, 100, 3, 16, 3, np.float32, False),
     (3, 64, 12288, 3, 128, 8, np.float16, True),
