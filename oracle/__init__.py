@@ -7,3 +7,4 @@ Every function is pinned by CPU tests; none is "parity unpinned".
 from .gptq_oracle import *  # noqa: F401,F403
 from .gptq_oracle import (GPTQResult, LayerSolution, NotPositiveDefinite,  # noqa: F401
                           ReplayMismatch)
+from . import model_pipeline  # noqa: F401,E402

@@ -267,3 +267,62 @@ def tiny_case(seed: int, d_row: int, d_col: int, n_rows: int, corr: float = 0.8,
     w = 0.02 * rng.standard_normal((d_row, d_col))
     x = _ar1_rows(rng.standard_normal((n_rows, d_col)), corr)
     return w.astype(dtype), x.astype(dtype)
+
+
+# ---------------------------------------------------------------------------
+# synthetic GPT-style model (random weights) for the model-level procedure
+# ---------------------------------------------------------------------------
+# The wiki page's description of the whole-model procedure (blocks one at a time,
+# each quantized block's outputs feeding the next) needs a model; the nanoGPT
+# post's model is a GPT-2-style stack.  Only the seeded parameters and the block-0
+# inputs live here: the fp64 oracle and the GPU-side torch module each implement
+# the block's forward pass on their own.
+
+GPT_WORKLOAD = 6
+GPT_LINEARS = ("attn", "attn_proj", "fc", "fc_proj")   # [out x in]: 3d x d, d x d, 4d x d, d x 4d
+
+
+@dataclasses.dataclass(frozen=True)
+class GPTSpec:
+    """A pre-LayerNorm GPT-2-style stack: x += attn_proj(attention(attn(ln1(x))));
+    x += fc_proj(gelu(fc(ln2(x)))), causal attention with n_head heads."""
+    n_block: int = 6
+    d: int = 384
+    n_head: int = 6
+    seq: int = 256
+    n_seq: int = 64          # sequences per calibration batch
+    n_batch: int = 10
+    w_std: float = 0.02
+    bits: int = 4
+    group_size: int = 0
+    block_size: int = 128
+    percdamp: float = 0.01
+
+    @property
+    def tokens(self) -> int:
+        return self.n_seq * self.seq * self.n_batch
+
+
+def gpt_block_params(spec: GPTSpec, block: int) -> dict:
+    """fp32 parameters of one block: linear weights w_std * N(0, 1), biases
+    0.02 * N(0, 1), LayerNorm gains 1 + 0.1 * N(0, 1) and shifts 0.02 * N(0, 1)."""
+    rng = _rng(GPT_WORKLOAD, block, T_W)
+    d = spec.d
+    shapes = {"attn": (3 * d, d), "attn_proj": (d, d), "fc": (4 * d, d), "fc_proj": (d, 4 * d)}
+    p = {}
+    for ln in ("ln1", "ln2"):
+        p[ln + "_w"] = 1.0 + 0.1 * rng.standard_normal(d)
+        p[ln + "_b"] = 0.02 * rng.standard_normal(d)
+    for name in GPT_LINEARS:
+        p[name + "_w"] = spec.w_std * rng.standard_normal(shapes[name])
+        p[name + "_b"] = 0.02 * rng.standard_normal(shapes[name][0])
+    return {k: v.astype(np.float32) for k, v in p.items()}
+
+
+def gpt_embeddings(spec: GPTSpec, batch: int) -> np.ndarray:
+    """Block-0 inputs of one calibration batch, fp32 [n_seq x seq x d]: the
+    LayerNorm-like recipe with 2% Student-t(3) outlier channels."""
+    layer = LayerSpec(GPT_WORKLOAD, 10_000, "emb", spec.d, spec.d, spec.n_seq * spec.seq, "f32", "f32",
+                      0.0, spec.bits, 0, x_kind="lnorm")
+    x = make_x_chunk(layer, batch, rows=spec.n_seq * spec.seq)
+    return x.reshape(spec.n_seq, spec.seq, spec.d)
