@@ -48,6 +48,11 @@ def parse():
                          "49152 x 12288 3-bit group-128 layer (one token) instead of the solver")
     ap.add_argument("--gemv-m", type=int, default=1, help="rows of X for --packed-gemv (1..8)")
     ap.add_argument("--gemv-iters", type=int, default=200, help="products per step for --packed-gemv")
+    ap.add_argument("--pipeline", action="store_true",
+                    help="time the whole-model procedure on a 6-block d=384 GPT-style stack (24 layers, "
+                         "163840 calibration tokens) instead of the single layer")
+    ap.add_argument("--independent", action="store_true",
+                    help="with --pipeline: every block sees the unquantized model's activations")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="run two plain device-to-device copies of BYTES bytes and exit (the reference "
                          "kernel for scaling the FETCH_SIZE / WRITE_SIZE counters)")
@@ -235,6 +240,153 @@ def packed_gemv(args):
     print(json.dumps(out), flush=True)
 
 
+def pipeline_cpu_baseline(spec, act_order):
+    """The fp64 oracle's procedure on one block: one calibration batch through the
+    forward pass (scaled to 2 passes x all batches x all blocks) and the block's
+    four layer solves on that batch's H (scaled to all blocks)."""
+    import numpy as np
+    import oracle as O
+    import workloads as wl
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = len(os.sched_getaffinity(0))
+    MP = O.model_pipeline
+    p = {k: v.astype(np.float64) for k, v in wl.gpt_block_params(spec, 0).items()}
+    x = wl.gpt_embeddings(spec, 0).astype(np.float64)
+    cap = {}
+    t0 = time.perf_counter()
+    MP.block_forward(p, x, spec.n_head, capture=cap)
+    t_fwd = time.perf_counter() - t0
+    t0 = time.perf_counter()
+    for name in MP.LINEARS:
+        H = O.hessian(cap[name]) * spec.n_batch
+        if act_order:
+            perm = O.act_order_perm(H)
+            Hl, _ = O.damp(H[np.ix_(perm, perm)], spec.percdamp)
+            O.gptq_quantize_act_order(p[name + "_w"], O.inv_hessian_factor(Hl), perm, spec.bits, spec.group_size,
+                                      spec.block_size)
+        else:
+            Hl, _ = O.damp(H, spec.percdamp)
+            O.gptq_quantize(p[name + "_w"], O.inv_hessian_factor(Hl), spec.bits, spec.group_size, spec.block_size)
+    t_solve = time.perf_counter() - t0
+    total = t_fwd * 2 * spec.n_batch * spec.n_block + t_solve * spec.n_block
+    return {"value": round(total, 2), "unit": "s/model", "cores": int(threads), "kind": "oracle",
+            "sample": (f"block 0: one batch of {spec.n_seq}x{spec.seq} tokens through the fp64 forward "
+                       f"(x{2 * spec.n_batch * spec.n_block}: two passes, {spec.n_batch} batches, "
+                       f"{spec.n_block} blocks) and its 4 layer solves (x{spec.n_block}); scaled to the model"),
+            "stages_s": {"forward_per_batch_block": t_fwd, "solves_per_block": t_solve}}
+
+
+def pipeline_bench(args):
+    """The whole-model procedure: 6 GPT-style blocks (d 384, 6 heads), 10 calibration
+    batches of 64 x 256 tokens, 4-bit per-row grid, block 128, 1% damping."""
+    import torch
+    import post_weight_quantization_02_amd as G  # noqa: F401
+    from post_weight_quantization_02_amd import pipeline as P
+    import workloads as wl
+    from workloads import torch_gpt
+
+    spec = wl.GPTSpec()
+    dev = torch.device("cuda:0")
+    blocks = torch_gpt.build_model(spec, device=dev)
+    orig = [{n: m.weight.detach().clone() for n, m in P.linear_layers(b)} for b in blocks]
+    xs = [torch.from_numpy(wl.gpt_embeddings(spec, i)).to(dev) for i in range(spec.n_batch)]
+    torch.cuda.synchronize()
+    sequential = not args.independent
+
+    def restore():
+        with torch.no_grad():
+            for b, o in zip(blocks, orig):
+                for n, m in P.linear_layers(b):
+                    m.weight.copy_(o[n])
+
+    def step():
+        return P.quantize_model(blocks, xs, spec.bits, spec.group_size, spec.block_size, spec.percdamp,
+                                act_order=args.act_order, sequential=sequential)
+
+    for _ in range(args.warmup):
+        restore()
+        step()
+    torch.cuda.synchronize()
+    times, errs = [], None
+    for _ in range(args.steps):
+        restore()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        res, _ = step()
+        torch.cuda.synchronize()
+        times.append(time.perf_counter() - t0)
+        errs = {f"h{i}.{n}": float(L.err.item()) for i, r in enumerate(res) for n, L in r.layers.items()}
+    per_step = sum(times) / len(times)
+    # one forward pass of the unquantized model over all batches, for the stage split
+    restore()
+    with torch.no_grad():
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for b in blocks:
+            ys = [b(x) for x in xs]
+        torch.cuda.synchronize()
+        t_fwd = time.perf_counter() - t0
+    passes = 2 if sequential else 1
+    # the quantizer's dominant kernel in this procedure: the fp32 syrk of
+    # gptq_hessian_accumulate at the model's shapes (one calibration batch of rows,
+    # widths d and 4d), timed with events on the stream it runs on
+    rows = spec.n_seq * spec.seq
+    t_h = {}
+    for width in (spec.d, 4 * spec.d):
+        Xh = torch.randn(rows, width, device=dev)
+        Hh = torch.zeros(width, width, device=dev)
+        for _ in range(3):
+            G.gptq_hessian_accumulate(Hh, Xh)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(20):
+            G.gptq_hessian_accumulate(Hh, Xh)
+        e1.record()
+        torch.cuda.synchronize()
+        t_h[width] = e0.elapsed_time(e1) / 1e3 / 20
+    f = lambda w: rows * w * (w + 1)  # noqa: E731  (upper triangle, 2 flop per multiply-add)
+    per_batch_block_flops = 3 * f(spec.d) + f(4 * spec.d)
+    per_batch_block_time = 3 * t_h[spec.d] + t_h[4 * spec.d]
+    ach = per_batch_block_flops / per_batch_block_time / 1e12
+    roof = {"bound": "mfma", "kernel": "gptq_hessian_accumulate: syrk_f32_kernel + split reduce (fp32 X)",
+            "achieved": round(ach, 2), "peak": PEAK_F32_MFMA_TFLOPS, "unit": "TFLOP/s",
+            "frac": round(ach / PEAK_F32_MFMA_TFLOPS, 4), "traffic": None,
+            "per_call_us": {str(k): round(v * 1e6, 2) for k, v in t_h.items()}}
+    out = {
+        "metric": "whole-model GPTQ, s per model (6-block d=384 GPT-style stack, 24 layers, 163840 tokens)",
+        "value": round(per_step, 5),
+        "unit": "s/model",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(per_step * 1e3, 3),
+        "higher_is_better": False,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32 model forward / f32-mfma syrk / f64 Cholesky / f32 loop",
+        "data": "synthetic",
+        "config": {"workload": (f"gpt6x384: {spec.n_block} blocks, d {spec.d}, {spec.n_head} heads, "
+                                f"{spec.n_batch} batches x {spec.n_seq} seqs x {spec.seq} tokens, "
+                                f"{spec.bits}-bit per-row, block {spec.block_size}, 1% damping, "
+                                + ("sequential" if sequential else "independent")
+                                + (", act-order" if args.act_order else "")),
+                   "sequential": sequential, "act_order": bool(args.act_order), "parallelism": "single-gpu"},
+        "stages": {"model_forward_all_blocks_ms": round(t_fwd * 1e3, 3), "forward_passes_per_block": passes,
+                   "quantizer_and_hooks_ms_estimate": round((per_step - passes * t_fwd) * 1e3, 3)},
+        "roofline": roof,
+        "layer_errors": errs,
+    }
+    if not args.no_cpu_baseline:
+        log("bench: timing the fp64 oracle's procedure on a bounded sample (CPU)")
+        cb = pipeline_cpu_baseline(spec, args.act_order)
+        out["cpu_baseline"] = cb
+        out["gpu_speedup_vs_cpu_oracle"] = round(cb["value"] / per_step, 1)
+    print(json.dumps(out), flush=True)
+
+
 def main():
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -256,6 +408,9 @@ def main():
 
     if args.packed_gemv:
         packed_gemv(args)
+        return
+    if args.pipeline:
+        pipeline_bench(args)
         return
 
     import post_weight_quantization_02_amd as G

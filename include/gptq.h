@@ -237,6 +237,24 @@ gptq_status gptq_dequant_matmul(const uint32_t* packed, int64_t ld_packed, int32
                                 int32_t x_dtype, int64_t m, int64_t ld_x, float* Y, int64_t ld_y,
                                 void* stream);
 
+/*
+ * Dequantized weights -- What as the model uses it between quantized layers
+ * (itwiki "GPTQ", algorithm section: the loop's output is What = scale * (q - zero)
+ * on the grid; the model-level procedure feeds the quantized block's outputs on).
+ *
+ * gptq_dequantize: out [device] [d_row x d_col] (out_dtype GPTQ_F32 or GPTQ_F16,
+ *   leading dimension ld_out >= d_col) = scales[r][g] * (codes[r][j] - zeros[r][g]),
+ *   computed in fp32 and rounded once to out_dtype.  codes [device] uint8
+ *   [d_row x ld_codes]; scales / zeros [device] [d_row x n_groups] as written by
+ *   gptq_quantize_layer(_perm), n_groups = ceil(d_col / group_size) (1 when
+ *   group_size == 0).  g: g_idx[j] when g_idx ([device] int32 [d_col], the
+ *   act-order column-to-group map; entries clamped to [0, n_groups)) is given,
+ *   else j / group_size, else 0.  No workspace.
+ */
+gptq_status gptq_dequantize(const uint8_t* codes, int64_t d_row, int64_t d_col, int64_t ld_codes,
+                            const float* scales, const int32_t* zeros, int64_t group_size, const int32_t* g_idx,
+                            void* out, int32_t out_dtype, int64_t ld_out, void* stream);
+
 /* [host] static description of a status code; never NULL. */
 const char* gptq_status_string(int32_t status);
 /* [host] library version string, e.g. "gptq-gfx950 0.1.0". */

@@ -24,7 +24,7 @@ __all__ = [
     "gptq_prepare_hinv", "gptq_prepare_hinv_workspace_size",
     "gptq_quantize_layer", "gptq_quantize_layer_workspace_size",
     "gptq_act_order_perm", "gptq_prepare_hinv_perm", "gptq_quantize_layer_perm",
-    "gptq_packed_words_per_row", "gptq_pack_codes", "gptq_dequant_matmul",
+    "gptq_packed_words_per_row", "gptq_pack_codes", "gptq_dequant_matmul", "gptq_dequantize",
     "gptq_status_string", "gptq_version", "quantize_layer",
 ]
 
@@ -90,6 +90,8 @@ def library() -> ctypes.CDLL:
     lib.gptq_dequant_matmul.argtypes = [vp, i64, i32, vp, vp, i64, vp, i64, i64, vp, i32, i64, i64, vp,
                                         i64, vp]
     lib.gptq_dequant_matmul.restype = i32
+    lib.gptq_dequantize.argtypes = [vp, i64, i64, i64, vp, vp, i64, vp, vp, i32, i64, vp]
+    lib.gptq_dequantize.restype = i32
     lib.gptq_status_string.argtypes = [i32]
     lib.gptq_status_string.restype = ctypes.c_char_p
     lib.gptq_version.argtypes = []
@@ -290,6 +292,23 @@ def gptq_pack_codes(codes, bits: int, perm=None, packed=None, stream=None):
                                    _ptr(perm), packed.data_ptr(), packed.stride(0), _stream(stream))
     _check(st, "gptq_pack_codes")
     return packed
+
+
+def gptq_dequantize(codes, scales, zeros, group_size: int, g_idx=None, out=None, out_dtype=None,
+                    stream=None):
+    """What [d_row x d_col] = scales * (codes - zeros) per group (through g_idx if
+    given), fp32 unless out / out_dtype say fp16."""
+    torch = _torch()
+    _rowmajor(codes, "codes")
+    d_row, d_col = codes.shape
+    if out is None:
+        out = torch.empty(d_row, d_col, dtype=out_dtype or torch.float32, device=codes.device)
+    _rowmajor(out, "out")
+    st = library().gptq_dequantize(codes.data_ptr(), d_row, d_col, codes.stride(0), scales.data_ptr(),
+                                   zeros.data_ptr(), int(group_size), _ptr(g_idx), out.data_ptr(),
+                                   _dtype_code(out), out.stride(0), _stream(stream))
+    _check(st, "gptq_dequantize")
+    return out
 
 
 def gptq_dequant_matmul(packed, bits: int, scales, zeros, group_size: int, X, d_col: int,

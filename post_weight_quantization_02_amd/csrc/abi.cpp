@@ -155,6 +155,19 @@ gptq_status gptq_pack_codes(const uint8_t* codes, int64_t d_row, int64_t d_col, 
                                     (hipStream_t)stream));
 }
 
+gptq_status gptq_dequantize(const uint8_t* codes, int64_t d_row, int64_t d_col, int64_t ld_codes,
+                            const float* scales, const int32_t* zeros, int64_t group_size, const int32_t* g_idx,
+                            void* out, int32_t out_dtype, int64_t ld_out, void* stream) {
+  if (d_row <= 0 || d_col <= 0) return GPTQ_ERR_BAD_SIZE;
+  if (d_row > kMaxDim || d_col > kMaxDim) return GPTQ_ERR_TOO_LARGE;
+  if (codes == nullptr || scales == nullptr || zeros == nullptr || out == nullptr) return GPTQ_ERR_NULL_POINTER;
+  if (out_dtype != GPTQ_F32 && out_dtype != GPTQ_F16) return GPTQ_ERR_BAD_DTYPE;
+  if (group_size < 0) return GPTQ_ERR_BAD_GROUP;
+  if (ld_codes < d_col || ld_out < d_col) return GPTQ_ERR_BAD_LEADING_DIM;
+  return from_hip(gptq::dequantize_launch(codes, d_row, d_col, ld_codes, scales, zeros, group_size, g_idx, out,
+                                          out_dtype == GPTQ_F16 ? 1 : 0, ld_out, (hipStream_t)stream));
+}
+
 gptq_status gptq_dequant_matmul(const uint32_t* packed, int64_t ld_packed, int32_t bits,
                                 const float* scales, const int32_t* zeros, int64_t group_size,
                                 const int32_t* perm, int64_t d_row, int64_t d_col, const void* X,

@@ -60,6 +60,9 @@ hipError_t act_order_launch(const float* H, int64_t d, int32_t* perm, hipStream_
 int64_t packed_words_per_row(int64_t d_col, int bits);
 hipError_t pack_launch(const uint8_t* codes, int64_t d_row, int64_t d_col, int64_t ld_codes, int bits,
                        const int32_t* perm, uint32_t* packed, int64_t ld_packed, hipStream_t s);
+hipError_t dequantize_launch(const uint8_t* codes, int64_t d_row, int64_t d_col, int64_t ld_codes,
+                             const float* scales, const int32_t* zeros, int64_t group, const int32_t* g_idx,
+                             void* out, int out_dtype, int64_t ld_out, hipStream_t s);
 hipError_t dequant_matmul_launch(const uint32_t* packed, int64_t ld_packed, int bits, const float* scales,
                                  const int32_t* zeros, int64_t group, const int32_t* perm, int64_t d_row,
                                  int64_t d_col, const void* X, int x_dtype, int m, int64_t ld_x, float* Y,

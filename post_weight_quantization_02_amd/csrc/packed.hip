@@ -916,6 +916,40 @@ hipError_t dequant_launch_t(int bits, const uint32_t* packed, int64_t ld_packed,
 
 int64_t packed_words_per_row(int64_t d_col, int bits) { return cdiv(d_col, 32) * bits; }
 
+namespace {
+// What = scale * (code - zero), one thread per weight; the group of column j is
+// g_idx[j] (clamped) when given, else j / group (0 for one group per row)
+template <typename T>
+__global__ __launch_bounds__(kThreads) void dequantize_kernel(const uint8_t* __restrict__ codes, int64_t d_row,
+                                                              int64_t d_col, int64_t ld_codes,
+                                                              const float* __restrict__ scales,
+                                                              const int32_t* __restrict__ zeros, int64_t group,
+                                                              int64_t ngroups, const int32_t* __restrict__ g_idx,
+                                                              T* __restrict__ out, int64_t ld_out) {
+  const int64_t id = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+  if (id >= d_row * d_col) return;
+  const int64_t r = id / d_col, j = id % d_col;
+  const int64_t g = g_idx ? min<int64_t>(max<int32_t>(g_idx[j], 0), ngroups - 1) : (group ? j / group : 0);
+  const float s = scales[r * ngroups + g];
+  const float z = (float)zeros[r * ngroups + g];
+  out[r * ld_out + j] = (T)(s * ((float)codes[r * ld_codes + j] - z));
+}
+}  // namespace
+
+hipError_t dequantize_launch(const uint8_t* codes, int64_t d_row, int64_t d_col, int64_t ld_codes,
+                             const float* scales, const int32_t* zeros, int64_t group, const int32_t* g_idx,
+                             void* out, int out_dtype, int64_t ld_out, hipStream_t s) {
+  const int64_t ngroups = group ? cdiv(d_col, group) : 1;
+  const dim3 grid((unsigned)cdiv(d_row * d_col, kThreads)), blk(kThreads);
+  if (out_dtype == 1)
+    hipLaunchKernelGGL(dequantize_kernel<_Float16>, grid, blk, 0, s, codes, d_row, d_col, ld_codes, scales, zeros,
+                       group, ngroups, g_idx, (_Float16*)out, ld_out);
+  else
+    hipLaunchKernelGGL(dequantize_kernel<float>, grid, blk, 0, s, codes, d_row, d_col, ld_codes, scales, zeros,
+                       group, ngroups, g_idx, (float*)out, ld_out);
+  return hipGetLastError();
+}
+
 hipError_t pack_launch(const uint8_t* codes, int64_t d_row, int64_t d_col, int64_t ld_codes, int bits,
                        const int32_t* perm, uint32_t* packed, int64_t ld_packed, hipStream_t s) {
   const int64_t nchunk = cdiv(d_col, 32);

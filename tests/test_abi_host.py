@@ -171,3 +171,24 @@ def test_packed_validation():
     assert d(*a) == _status("GPTQ_ERR_BAD_LEADING_DIM")  # ld_y < d_row
     a = list(ok); a[3] = None
     assert d(*a) == _status("GPTQ_ERR_NULL_POINTER")
+
+
+def test_dequantize_validation():
+    f = G.library().gptq_dequantize
+    ok = [FAKE, 4, 64, 64, FAKE, FAKE, 16, None, FAKE, 0, 64, None]
+    a = list(ok); a[1] = 0
+    assert f(*a) == _status("GPTQ_ERR_BAD_SIZE")
+    a = list(ok); a[0] = None
+    assert f(*a) == _status("GPTQ_ERR_NULL_POINTER")
+    a = list(ok); a[8] = None
+    assert f(*a) == _status("GPTQ_ERR_NULL_POINTER")
+    a = list(ok); a[9] = 5
+    assert f(*a) == _status("GPTQ_ERR_BAD_DTYPE")
+    a = list(ok); a[6] = -1
+    assert f(*a) == _status("GPTQ_ERR_BAD_GROUP")
+    a = list(ok); a[3] = 63
+    assert f(*a) == _status("GPTQ_ERR_BAD_LEADING_DIM")
+    a = list(ok); a[10] = 10
+    assert f(*a) == _status("GPTQ_ERR_BAD_LEADING_DIM")
+    a = list(ok); a[2] = (1 << 20) + 1; a[3] = a[2]; a[10] = a[2]
+    assert f(*a) == _status("GPTQ_ERR_TOO_LARGE")

@@ -122,3 +122,26 @@ def test_quantize_pack_matmul_end_to_end(act_order):
     mag = np.abs(sc[:, gidx]) * (np.abs(codes) + np.abs(zr[:, gidx]))
     bound = 2.0 * 1024 * U32 * (np.abs(Xq.astype(np.float64)) @ mag.T)
     assert np.all(np.abs(Y.cpu().numpy() - Yo) <= bound)
+
+
+@pytest.mark.parametrize("group,use_gidx,out", [(0, False, "f32"), (32, False, "f16"), (16, True, "f32"),
+                                                (48, False, "f16")])
+def test_dequantize_parity(group, use_gidx, out):
+    """What = fp32(scale * (code - zero)) (then rounded to fp16), bitwise, through
+    the group map when given; written with a leading dimension."""
+    rng = np.random.default_rng(group + 7)
+    d_row, d_col = 37, 200
+    ng = -(-d_col // group) if group else 1
+    codes = rng.integers(0, 16, (d_row, d_col)).astype(np.uint8)
+    scales = rng.uniform(1e-3, 1e-1, (d_row, ng)).astype(np.float32)
+    zeros = rng.integers(-3, 19, (d_row, ng)).astype(np.int32)
+    gi = rng.integers(0, ng, d_col).astype(np.int32) if use_gidx else np.arange(d_col) // (group or 10 ** 9)
+    dt = torch.float16 if out == "f16" else torch.float32
+    buf = torch.full((d_row, d_col + 5), 7.0, dtype=dt, device="cuda")
+    G.gptq_dequantize(dev(codes), dev(scales), dev(zeros), group, dev(gi) if use_gidx else None,
+                      out=buf[:, :d_col])
+    torch.cuda.synchronize()
+    ref = (scales[:, gi].astype(np.float64) * (codes.astype(np.float64) - zeros[:, gi])).astype(np.float32)
+    got = buf.cpu().numpy()
+    np.testing.assert_array_equal(got[:, :d_col], ref.astype(np.float16) if out == "f16" else ref)
+    assert np.all(got[:, d_col:] == 7.0)
