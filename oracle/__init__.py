@@ -8,3 +8,4 @@ from .gptq_oracle import *  # noqa: F401,F403
 from .gptq_oracle import (GPTQResult, LayerSolution, NotPositiveDefinite,  # noqa: F401
                           ReplayMismatch)
 from . import model_pipeline  # noqa: F401,E402
+from . import gptq2d  # noqa: F401,E402
