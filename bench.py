@@ -53,6 +53,8 @@ def parse():
                          "163840 calibration tokens) instead of the single layer")
     ap.add_argument("--independent", action="store_true",
                     help="with --pipeline: every block sees the unquantized model's activations")
+    ap.add_argument("--gptq2d", action="store_true",
+                    help="time two-sided adaptive rounding of a 4096 x 4096 fp16 matrix instead of the layer")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="run two plain device-to-device copies of BYTES bytes and exit (the reference "
                          "kernel for scaling the FETCH_SIZE / WRITE_SIZE counters)")
@@ -387,6 +389,107 @@ def pipeline_bench(args):
     print(json.dumps(out), flush=True)
 
 
+PEAK_F32_VALU_TFLOPS = 157.3    # 256 CUs x 4 SIMDs x 2.4 GHz x 64 flop per cycle (fp32 vector)
+
+
+def gptq2d_cpu_baseline(bits):
+    """The fp64 oracle's sweep on a 256 x 256 problem of the same recipe, scaled by
+    m n (m + n) to 4096 x 4096."""
+    import numpy as np
+    import oracle as O
+    rng = np.random.default_rng(5)
+    k = 256
+    X = (0.015 * rng.standard_normal((k, k))).astype(np.float16).astype(np.float64)
+    Z = rng.standard_normal((4 * k, k))
+    Q = 2 * Z.T @ Z
+    Z = rng.standard_normal((4 * k, k))
+    P = 2 * Z.T @ Z
+    UQ = O.inv_hessian_factor(O.damp(Q, 0.01)[0])
+    UP = O.inv_hessian_factor(O.damp(P, 0.01)[0])
+    t0 = time.perf_counter()
+    O.gptq2d.gptq2d(X, UQ, UP, bits)
+    t = (time.perf_counter() - t0) * (4096 * 4096 * 8192) / (k * k * 2 * k)
+    return {"value": round(t, 1), "unit": "s/matrix", "cores": 1, "kind": "oracle",
+            "sample": "the sweep on a 256 x 256 problem of the same recipe, scaled by m n (m + n) to 4096 x 4096"}
+
+
+def gptq2d_bench(args):
+    """Two-sided rounding of a 4096 x 4096 fp16 matrix (the attn_4096 weight recipe)
+    with A^T A and B B^T = 2 Z^T Z of two seeded 16384-row low-rank streams, 1%
+    damping, 4 bits; the timed call is gptq2d_quantize (the factors are inputs)."""
+    import torch
+    import post_weight_quantization_02_amd as G
+    import workloads as wl
+
+    m = n = 4096
+    bits = 4
+    dev = torch.device("cuda:0")
+    spec = wl.workload_layers(3)[0]
+    X = torch.from_numpy(wl.make_weight(spec)).to(dev)
+    grams = []
+    for layer in (201, 202):
+        zs = wl.LayerSpec(3, layer, "side", 8, m, 16384, "f32", "f16", 0.0, 4, 0, x_kind="lowrank")
+        Hs = torch.zeros(m, m, device=dev)
+        G.gptq_hessian_accumulate(Hs, torch.from_numpy(wl.make_x_chunk(zs, 0)).to(dev))
+        grams.append(Hs)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    UQ, _, iq = G.gptq_prepare_hinv(grams[0], 0.01)
+    UP, _, ip = G.gptq_prepare_hinv(grams[1], 0.01)
+    e1.record()
+    torch.cuda.synchronize()
+    if int(iq.item()) or int(ip.item()):
+        raise SystemExit("side factor failed")
+    t_factors = e0.elapsed_time(e1) / 1e3
+    codes = torch.empty(m, n, dtype=torch.uint8, device=dev)
+    scale = torch.empty(1, device=dev)
+    zero = torch.empty(1, dtype=torch.int32, device=dev)
+    err = torch.empty(1, dtype=torch.float64, device=dev)
+    ws = torch.empty(G.gptq2d_quantize_workspace_size(m, n), dtype=torch.uint8, device=dev)
+    for _ in range(args.warmup):
+        G.gptq2d_quantize(X, UQ, UP, bits, codes, scale, zero, err, ws)
+    torch.cuda.synchronize()
+    e0.record()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        G.gptq2d_quantize(X, UQ, UP, bits, codes, scale, zero, err, ws)
+    e1.record()
+    torch.cuda.synchronize()
+    wall = (time.perf_counter() - t0) / args.steps
+    t = e0.elapsed_time(e1) / 1e3 / args.steps
+    flops = m * n * (m + n + 2)          # every entry's dot product and row update, 2 flop per multiply-add
+    ach = flops / t / 1e12
+    out = {
+        "metric": "two-sided adaptive rounding (GPTQ-2D), s per 4096 x 4096 matrix",
+        "value": round(t, 6),
+        "unit": "s/matrix",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall * 1e3, 4),
+        "higher_is_better": False,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16 X, f32 sweep, f64 error sums",
+        "data": "synthetic",
+        "config": {"workload": "2d_4096: X 4096x4096 fp16 (N(0, 0.015^2)), A^T A and B B^T from two 16384-row "
+                               "rank-64 fp16 streams, 1% damping, 4-bit, one grid per matrix",
+                   "m": m, "n": n, "bits": bits, "parallelism": "single-gpu"},
+        "stages": {"side_factors_ms": round(t_factors * 1e3, 3), "sweep_launches": m // 32 + n // 32 - 1,
+                   "err": float(err.item())},
+        "roofline": {"bound": "alu", "kernel": "the sweep: corr2d_kernel + tile2d_kernel + feed2d_kernel per 32-tile "
+                                               "anti-diagonal",
+                     "achieved": round(ach, 3), "peak": PEAK_F32_VALU_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(ach / PEAK_F32_VALU_TFLOPS, 4), "traffic": None},
+    }
+    if not args.no_cpu_baseline:
+        log("bench: timing the fp64 oracle's sweep on a bounded sample (CPU)")
+        cb = gptq2d_cpu_baseline(bits)
+        out["cpu_baseline"] = cb
+        out["gpu_speedup_vs_cpu_oracle"] = round(cb["value"] / t, 1)
+    print(json.dumps(out), flush=True)
+
+
 def main():
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -411,6 +514,9 @@ def main():
         return
     if args.pipeline:
         pipeline_bench(args)
+        return
+    if args.gptq2d:
+        gptq2d_bench(args)
         return
 
     import post_weight_quantization_02_amd as G

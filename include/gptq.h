@@ -255,6 +255,29 @@ gptq_status gptq_dequantize(const uint8_t* codes, int64_t d_row, int64_t d_col, 
                             const float* scales, const int32_t* zeros, int64_t group_size, const int32_t* g_idx,
                             void* out, int32_t out_dtype, int64_t ld_out, void* stream);
 
+/*
+ * Two-sided adaptive rounding (blog.secrett2633.cloud, "[논문리뷰] GPTQ-2D:
+ * Cubic-Time Two-Sided Adaptive Rounding", sections 1-3): round X [m x n] on one
+ * asymmetric k-bit grid so as to minimise ||A (Z - X) B||_F^2, entry by entry with
+ * error feedback, swept by anti-diagonals.
+ *
+ * gptq2d_quantize: X [device] [m x n] (x_dtype GPTQ_F32 or GPTQ_F16, leading
+ *   dimension ldx >= n); U_Q [device] fp32 [m x m] and U_P [device] fp32 [n x n]:
+ *   upper factors with U_Q^T U_Q = (A^T A)^-1 and U_P^T U_P = (B B^T)^-1 (for
+ *   example gptq_prepare_hinv of A^T A and of B B^T; only the upper triangles are
+ *   read); bits in [2, 8].  Writes codes [device] uint8 [m x ld_codes] (ld_codes >=
+ *   n), scale [device] one float and zero [device] one int32 (the grid: scale =
+ *   max(max X - min X, 1e-8) / (2^bits - 1), zero = round(-min X / scale); What =
+ *   scale * (code - zero)) and out_err [device] one double: sum of the squared
+ *   scaled errors, which is ||A (What - X) B||_F^2 for the A^T A and B B^T the
+ *   factors come from.  Workspace: gptq2d_quantize_workspace_size(m, n) bytes
+ *   (M, m x n fp32, and per-tile partial sums); m + n - 1 launches of 32 x 32 tiles.
+ */
+size_t gptq2d_quantize_workspace_size(int64_t m, int64_t n);
+gptq_status gptq2d_quantize(const void* X, int32_t x_dtype, int64_t m, int64_t n, int64_t ldx, const float* U_Q,
+                            const float* U_P, int32_t bits, uint8_t* codes, int64_t ld_codes, float* scale,
+                            int32_t* zero, double* out_err, void* ws, size_t ws_bytes, void* stream);
+
 /* [host] static description of a status code; never NULL. */
 const char* gptq_status_string(int32_t status);
 /* [host] library version string, e.g. "gptq-gfx950 0.1.0". */

@@ -25,6 +25,7 @@ __all__ = [
     "gptq_quantize_layer", "gptq_quantize_layer_workspace_size",
     "gptq_act_order_perm", "gptq_prepare_hinv_perm", "gptq_quantize_layer_perm",
     "gptq_packed_words_per_row", "gptq_pack_codes", "gptq_dequant_matmul", "gptq_dequantize",
+    "gptq2d_quantize", "gptq2d_quantize_workspace_size",
     "gptq_status_string", "gptq_version", "quantize_layer",
 ]
 
@@ -90,6 +91,10 @@ def library() -> ctypes.CDLL:
     lib.gptq_dequant_matmul.argtypes = [vp, i64, i32, vp, vp, i64, vp, i64, i64, vp, i32, i64, i64, vp,
                                         i64, vp]
     lib.gptq_dequant_matmul.restype = i32
+    lib.gptq2d_quantize_workspace_size.argtypes = [i64, i64]
+    lib.gptq2d_quantize_workspace_size.restype = sz
+    lib.gptq2d_quantize.argtypes = [vp, i32, i64, i64, i64, vp, vp, i32, vp, i64, vp, vp, vp, vp, sz, vp]
+    lib.gptq2d_quantize.restype = i32
     lib.gptq_dequantize.argtypes = [vp, i64, i64, i64, vp, vp, i64, vp, vp, i32, i64, vp]
     lib.gptq_dequantize.restype = i32
     lib.gptq_status_string.argtypes = [i32]
@@ -292,6 +297,32 @@ def gptq_pack_codes(codes, bits: int, perm=None, packed=None, stream=None):
                                    _ptr(perm), packed.data_ptr(), packed.stride(0), _stream(stream))
     _check(st, "gptq_pack_codes")
     return packed
+
+
+def gptq2d_quantize_workspace_size(m: int, n: int) -> int:
+    return int(library().gptq2d_quantize_workspace_size(m, n))
+
+
+def gptq2d_quantize(X, U_Q, U_P, bits: int, codes=None, scale=None, zero=None, out_err=None, ws=None,
+                    stream=None):
+    """Two-sided adaptive rounding of X [m x n] (fp16/fp32) with the upper factors
+    U_Q [m x m] and U_P [n x n].  Returns (codes uint8, scale fp32 [1], zero int32 [1],
+    err fp64 [1])."""
+    torch = _torch()
+    _rowmajor(X, "X")
+    m, n = X.shape
+    dev = X.device
+    codes = codes if codes is not None else torch.empty(m, n, dtype=torch.uint8, device=dev)
+    scale = scale if scale is not None else torch.empty(1, dtype=torch.float32, device=dev)
+    zero = zero if zero is not None else torch.empty(1, dtype=torch.int32, device=dev)
+    out_err = out_err if out_err is not None else torch.empty(1, dtype=torch.float64, device=dev)
+    ws = _workspace(gptq2d_quantize_workspace_size(m, n), dev, ws)
+    st = library().gptq2d_quantize(X.data_ptr(), _dtype_code(X), m, n, X.stride(0), U_Q.data_ptr(),
+                                   U_P.data_ptr(), int(bits), codes.data_ptr(), codes.stride(0), scale.data_ptr(),
+                                   zero.data_ptr(), out_err.data_ptr(), ws.data_ptr(), ws.numel(),
+                                   _stream(stream))
+    _check(st, "gptq2d_quantize")
+    return codes, scale, zero, out_err
 
 
 def gptq_dequantize(codes, scales, zeros, group_size: int, g_idx=None, out=None, out_dtype=None,

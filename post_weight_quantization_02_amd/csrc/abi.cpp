@@ -155,6 +155,28 @@ gptq_status gptq_pack_codes(const uint8_t* codes, int64_t d_row, int64_t d_col, 
                                     (hipStream_t)stream));
 }
 
+size_t gptq2d_quantize_workspace_size(int64_t m, int64_t n) {
+  if (m <= 0 || n <= 0 || m > kMaxDim || n > kMaxDim) return 0;
+  return gptq::plan2d(m, n).ws_bytes;
+}
+
+gptq_status gptq2d_quantize(const void* X, int32_t x_dtype, int64_t m, int64_t n, int64_t ldx, const float* U_Q,
+                            const float* U_P, int32_t bits, uint8_t* codes, int64_t ld_codes, float* scale,
+                            int32_t* zero, double* out_err, void* ws, size_t ws_bytes, void* stream) {
+  if (m <= 0 || n <= 0) return GPTQ_ERR_BAD_SIZE;
+  if (m > kMaxDim || n > kMaxDim) return GPTQ_ERR_TOO_LARGE;
+  if (X == nullptr || U_Q == nullptr || U_P == nullptr || codes == nullptr || scale == nullptr ||
+      zero == nullptr || out_err == nullptr)
+    return GPTQ_ERR_NULL_POINTER;
+  if (x_dtype != GPTQ_F32 && x_dtype != GPTQ_F16) return GPTQ_ERR_BAD_DTYPE;
+  if (bits < 2 || bits > 8) return GPTQ_ERR_BAD_BITS;
+  if (ldx < n || ld_codes < n) return GPTQ_ERR_BAD_LEADING_DIM;
+  const gptq::Plan2D p = gptq::plan2d(m, n);
+  if (ws == nullptr || ws_bytes < p.ws_bytes) return GPTQ_ERR_WORKSPACE;
+  return from_hip(gptq::quantize2d_launch(p, X, x_dtype == GPTQ_F16 ? 1 : 0, ldx, U_Q, U_P, bits, codes, ld_codes,
+                                          scale, zero, out_err, ws, (hipStream_t)stream));
+}
+
 gptq_status gptq_dequantize(const uint8_t* codes, int64_t d_row, int64_t d_col, int64_t ld_codes,
                             const float* scales, const int32_t* zeros, int64_t group_size, const int32_t* g_idx,
                             void* out, int32_t out_dtype, int64_t ld_out, void* stream) {

@@ -68,6 +68,17 @@ hipError_t dequant_matmul_launch(const uint32_t* packed, int64_t ld_packed, int 
                                  int64_t d_col, const void* X, int x_dtype, int m, int64_t ld_x, float* Y,
                                  int64_t ld_y, hipStream_t s);
 
+// ---------------------------------------------------------------- two-sided rounding
+struct Plan2D {
+  int64_t m, n, Mb, Nb;   // matrix and 32-tile counts
+  int64_t nchunk_a;       // correction chunks per tile (8 tile-rows each)
+  size_t off_m, off_e, off_cpart, off_err, off_part, off_grid, ws_bytes;
+};
+Plan2D plan2d(int64_t m, int64_t n);
+hipError_t quantize2d_launch(const Plan2D& p, const void* X, int x_dtype, int64_t ldx, const float* UQ,
+                             const float* UP, int bits, uint8_t* codes, int64_t ldc, float* scale, int32_t* zero,
+                             double* out_err, void* ws, hipStream_t s);
+
 // ---------------------------------------------------------------- quantize
 struct QuantPlan {
   int64_t d_row, d_col, B, nblk;

@@ -19,7 +19,7 @@ pytestmark = pytest.mark.skipif(not os.path.exists(G.lib_path()),
 def _declared():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(gptq_[a-z_]+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(gptq(?:2d)?_[a-z_]+)\s*\(", text)))
 
 
 def _status(name):
@@ -191,4 +191,28 @@ def test_dequantize_validation():
     a = list(ok); a[10] = 10
     assert f(*a) == _status("GPTQ_ERR_BAD_LEADING_DIM")
     a = list(ok); a[2] = (1 << 20) + 1; a[3] = a[2]; a[10] = a[2]
+    assert f(*a) == _status("GPTQ_ERR_TOO_LARGE")
+
+
+def test_gptq2d_validation():
+    assert "gptq2d_quantize" in _declared()
+    f = G.library().gptq2d_quantize
+    need = G.gptq2d_quantize_workspace_size(64, 48)
+    assert need > 64 * 48 * 4 and G.gptq2d_quantize_workspace_size(0, 48) == 0
+    ok = [FAKE, 0, 64, 48, 48, FAKE, FAKE, 4, FAKE, 48, FAKE, FAKE, FAKE, FAKE, need, None]
+    a = list(ok); a[2] = 0
+    assert f(*a) == _status("GPTQ_ERR_BAD_SIZE")
+    a = list(ok); a[5] = None
+    assert f(*a) == _status("GPTQ_ERR_NULL_POINTER")
+    a = list(ok); a[1] = 3
+    assert f(*a) == _status("GPTQ_ERR_BAD_DTYPE")
+    a = list(ok); a[7] = 9
+    assert f(*a) == _status("GPTQ_ERR_BAD_BITS")
+    a = list(ok); a[4] = 47
+    assert f(*a) == _status("GPTQ_ERR_BAD_LEADING_DIM")
+    a = list(ok); a[9] = 40
+    assert f(*a) == _status("GPTQ_ERR_BAD_LEADING_DIM")
+    a = list(ok); a[14] = need - 1
+    assert f(*a) == _status("GPTQ_ERR_WORKSPACE")
+    a = list(ok); a[3] = (1 << 20) + 1; a[4] = a[3]; a[9] = a[3]
     assert f(*a) == _status("GPTQ_ERR_TOO_LARGE")
