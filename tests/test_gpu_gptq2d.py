@@ -87,3 +87,41 @@ def test_gptq2d_end_to_end_with_the_library_factors_and_determinism():
     s, z = Q2.tensor_grid(X.astype(np.float64), bits)
     rtn = O.dequant(O.quant_codes(X.astype(np.float64), s, z, (1 << bits) - 1), s, z)
     assert mg < Q2.two_sided_metric(X, rtn, A, B)
+
+
+def test_gptq2d_full_size_properties():
+    """The benchmarked size (4096 x 4096 fp16, sides from 16384-row rank-64 streams,
+    1% damping, 4 bits), where the oracle cannot redo the sweep: the reported sum of
+    squared scaled errors equals tr(D^T Q D P) of the GPU's own What (D = What - X,
+    Q and P the damped side matrices, fp64 on the host) within 1e-3, every code is on
+    the grid, the metric is below round-to-nearest's, and two runs are identical."""
+    import workloads as wl
+    m = n = 4096
+    spec = wl.workload_layers(3)[0]
+    X = wl.make_weight(spec)
+    grams = []
+    for layer in (201, 202):
+        zs = wl.LayerSpec(3, layer, "side", 8, m, 16384, "f32", "f16", 0.0, 4, 0, x_kind="lowrank")
+        Hs = torch.zeros(m, m, device="cuda")
+        G.gptq_hessian_accumulate(Hs, dev(wl.make_x_chunk(zs, 0)))
+        grams.append(Hs)
+    UQ, lq, iq = G.gptq_prepare_hinv(grams[0], 0.01)
+    UP, lp, ip = G.gptq_prepare_hinv(grams[1], 0.01)
+    outs = [G.gptq2d_quantize(dev(X), UQ, UP, 4) for _ in range(2)]
+    torch.cuda.synchronize()
+    assert int(iq.item()) == 0 and int(ip.item()) == 0
+    for a, b in zip(*outs):
+        assert torch.equal(a, b)
+    codes, scale, zero, err = outs[0]
+    c = codes.cpu().numpy()
+    assert int(c.max()) <= 15
+    s, z = float(scale.item()), int(zero.item())
+    Xd = X.astype(np.float64)
+    D = s * (c.astype(np.float64) - z) - Xd
+    Q = grams[0].cpu().numpy().astype(np.float64) + float(lq.item()) * np.eye(m)
+    P = grams[1].cpu().numpy().astype(np.float64) + float(lp.item()) * np.eye(n)
+    metric = float(np.sum((Q @ D) * (D @ P)))
+    assert abs(float(err.item()) - metric) <= 1e-3 * metric, (float(err.item()), metric)
+    s_o, z_o = Q2.tensor_grid(Xd, 4)
+    Dr = O.dequant(O.quant_codes(Xd, s_o, z_o, 15), s_o, z_o) - Xd
+    assert metric < float(np.sum((Q @ Dr) * (Dr @ P)))

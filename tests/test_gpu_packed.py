@@ -145,3 +145,34 @@ def test_dequantize_parity(group, use_gidx, out):
     got = buf.cpu().numpy()
     np.testing.assert_array_equal(got[:, :d_col], ref.astype(np.float16) if out == "f16" else ref)
     assert np.all(got[:, d_col:] == 7.0)
+
+
+@pytest.mark.parametrize("m", [1, 8])
+def test_dequant_matmul_full_size_sampled_rows(m):
+    """The benchmarked shape (49152 x 12288, 3-bit, group 128, fp16 X) in the
+    launch configuration the benchmark times: 128 sampled output rows against the
+    oracle's product of those rows (m = 1: the one-row kernel; m = 8: the
+    matrix-core kernel)."""
+    d_row, d_col, bits, group = 49152, 12288, 3, 128
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(77 + m)
+    codes = torch.randint(0, 1 << bits, (d_row, d_col), dtype=torch.uint8, device="cuda", generator=gen)
+    packed = G.gptq_pack_codes(codes, bits)
+    ng = d_col // group
+    scales = torch.rand(d_row, ng, device="cuda", generator=gen) * 0.01 + 1e-3
+    zeros = torch.randint(0, 1 << bits, (d_row, ng), dtype=torch.int32, device="cuda", generator=gen)
+    X = torch.randn(m, d_col, device="cuda", generator=gen).to(torch.float16)
+    Y = G.gptq_dequant_matmul(packed, bits, scales, zeros, group, X, d_col)
+    torch.cuda.synchronize()
+    rows = np.sort(np.random.default_rng(m).choice(d_row, 128, replace=False))
+    rt = torch.from_numpy(rows).cuda()
+    pk = packed[rt].cpu().numpy().view(np.uint32)
+    sc, zr = scales[rt].cpu().numpy(), zeros[rt].cpu().numpy()
+    Xn = X.cpu().numpy()
+    Yo = O.dequant_matmul(pk, bits, sc, zr, group, Xn, d_col)
+    c = O.unpack_codes(pk, bits, d_col).astype(np.float64)
+    gi = np.arange(d_col) // group
+    mag = np.abs(sc.astype(np.float64)[:, gi]) * (np.abs(c) + np.abs(zr.astype(np.float64)[:, gi]))
+    bound = 2.0 * d_col * U32 * (np.abs(Xn.astype(np.float64)) @ mag.T)
+    err = np.abs(Y.cpu().numpy()[:, rows].astype(np.float64) - Yo)
+    assert np.all(err <= bound), float(np.max(err / bound))

@@ -123,3 +123,40 @@ def test_pipeline_end_to_end_against_the_oracle():
         for name in MP.LINEARS:
             e_g, e_o = float(res[b].layers[name].err.item()), out[b].layers[name].err
             assert abs(e_g - e_o) <= 0.02 * e_o, (b, name, e_g, e_o)
+
+
+def test_pipeline_full_size_sampled():
+    """The benchmarked model (6 blocks, d 384, 10 x 64 x 256 tokens, 4-bit per row,
+    block 128) in the configuration the benchmark times, checked where the oracle
+    can redo a stage in seconds: the attn layers' H of blocks 0 and 5 (their input
+    rows are the layer norm of the block's inputs), four sampled layers' weights
+    and errors against the oracle's solve of the GPU's H, and block 0's outputs on
+    one batch with the GPU's What."""
+    spec = wl.GPTSpec()
+    blocks = torch_gpt.build_model(spec)
+    xs = [torch.from_numpy(wl.gpt_embeddings(spec, i)).cuda() for i in range(spec.n_batch)]
+    res, _ = P.quantize_model(blocks, xs, spec.bits, spec.group_size, spec.block_size, spec.percdamp,
+                              keep_inputs=True, keep_hessians=True)
+    torch.cuda.synchronize()
+    for b in (0, 5):
+        p0 = wl.gpt_block_params(spec, b)
+        rows = [MP.layer_norm(x.cpu().numpy().astype(np.float64).reshape(-1, spec.d), p0["ln1_w"].astype(np.float64),
+                              p0["ln1_b"].astype(np.float64)) for x in res[b].inputs]
+        assert relf(res[b].layers["attn"].H.cpu().numpy(), O.hessian(rows)) <= 1e-5
+    for b, name in ((0, "attn"), (0, "fc_proj"), (5, "attn_proj"), (5, "fc")):
+        L = res[b].layers[name]
+        W0 = wl.gpt_block_params(spec, b)[name + "_w"].astype(np.float64)
+        Hg = L.H.cpu().numpy().astype(np.float64)
+        Hl, _ = O.damp(Hg, spec.percdamp)
+        sol = O.gptq_quantize(W0, O.inv_hessian_factor(Hl), spec.bits, 0, spec.block_size)
+        e_o = O.output_error(W0, sol.w_hat, Hg)
+        assert abs(float(L.err.item()) - e_o) <= 0.01 * e_o, (b, name)
+        sg, zg, cg = L.scales.cpu().numpy(), L.zeros.cpu().numpy(), L.codes.cpu().numpy()
+        what = (sg.astype(np.float64) * (cg.astype(np.float64) - zg)).astype(np.float32)
+        m = dict(P.linear_layers(blocks[b]))[name]
+        np.testing.assert_array_equal(m.weight.detach().cpu().numpy(), what)
+    q = {k: v.astype(np.float64) for k, v in wl.gpt_block_params(spec, 0).items()}
+    for name, m in P.linear_layers(blocks[0]):
+        q[name + "_w"] = m.weight.detach().cpu().numpy().astype(np.float64)
+    x0 = res[0].inputs[0].cpu().numpy().astype(np.float64)
+    assert relf(res[1].inputs[0].cpu().numpy(), MP.block_forward(q, x0, spec.n_head)) <= 1e-5
