@@ -9,8 +9,7 @@
 // then one LDS word per lane with 32 consecutive lanes on consecutive words.
 // 128x128 output tile per work-group (4 waves, 64x64 each), K in two 64-deep
 // phases (67 KB LDS, two work-groups per CU); the C tile is read into
-// registers at the start of the last K phase (its latency hides under that
-// phase's MFMAs) and written once.  Tiles are mapped so that each XCD runs a contiguous range.
+// registers at the start (its traffic hides under the MFMAs) and written once.  Tiles are mapped so that each XCD runs a contiguous range.
 #include "gptq_internal.h"
 
 namespace gptq {
@@ -194,20 +193,20 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
       __builtin_amdgcn_raw_ptr_buffer_load_lds(ur, (void GPTQ_LDS*)(LU + (8 * w + 2 * j) * kT), 16, voU[j], soU, 0, 0);
     }
   };
-  // C quadrant of this wave, coalesced: rows lane / 16 + 4 i, columns 4 (lane % 16) .. + 3
+  // C quadrant of this wave, coalesced: rows lane / 16 + 4 i, columns 4 (lane % 16) .. + 3.
+  // Exactly 16 loads per wave, always issued (the waits below count them): a lane
+  // outside M x N reads an in-bounds vector instead, whose value is never stored.
   const int qr0 = m0 + wm * 64 + (lane >> 4), qc = n0 + wn * 64 + (lane & 15) * 4;
+  const int qcl = std::min(qc, (N - 4) & ~3);
   f32x4 cq[16];
   auto cload = [&]() {
+    asm volatile("" ::: "memory");  // keep the C loads after the sub-phase loads
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
-      const int row = qr0 + 4 * i;
-      if (row < M && qc + 3 < N) {
-        cq[i] = *(const f32x4*)(C + (int64_t)row * ldc + qc);
-      } else {
-#pragma unroll
-        for (int e = 0; e < 4; ++e) cq[i][e] = (row < M && qc + e < N) ? C[(int64_t)row * ldc + qc + e] : 0.f;
-      }
+      const int row = std::min(qr0 + 4 * i, M - 1);
+      cq[i] = *(const f32x4*)(C + (int64_t)row * ldc + qcl);
     }
+    asm volatile("" ::: "memory");
   };
 
   f32x16 acc[2][2];
@@ -238,24 +237,27 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
   };
 
   // sub-phase s lives in buffer s % 2; the loads of s + 1 run under the MFMAs of
-  // s; C is read under the MFMAs of the last sub-phase
+  // s.  C is read right after the first two sub-phases' loads, so its HBM
+  // traffic spreads over all the tile's MFMAs.  Each wait for sub-phase s allows
+  // exactly the loads issued after it to stay in flight (8 per sub-phase, 16 for
+  // C), so it never waits for C or a later sub-phase.
   dma(E0, U0, 0);
   if constexpr (NSUB > 1) {
     dma(E1, U1, 1);
-    asm volatile("s_waitcnt vmcnt(8)\n\ts_barrier" ::: "memory");
-  } else {
-    asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
     cload();
+    asm volatile("s_waitcnt vmcnt(24)\n\ts_barrier" ::: "memory");
+  } else {
+    cload();
+    asm volatile("s_waitcnt vmcnt(16)\n\ts_barrier" ::: "memory");
   }
   compute(E0, U0, 0);
   if constexpr (NSUB > 1) {
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
     if constexpr (NSUB > 2) {
       dma(E0, U0, 2);
-      asm volatile("s_waitcnt vmcnt(8)\n\ts_barrier" ::: "memory");
+      asm volatile("s_waitcnt vmcnt(24)\n\ts_barrier" ::: "memory");
     } else {
-      asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
-      cload();
+      asm volatile("s_waitcnt vmcnt(16)\n\ts_barrier" ::: "memory");
     }
     compute(E1, U1, 1);
   }
@@ -266,13 +268,11 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
       asm volatile("s_waitcnt vmcnt(8)\n\ts_barrier" ::: "memory");
     } else {
       asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
-      cload();
     }
     compute(E0, U0, 2);
   }
   if constexpr (NSUB > 3) {
     asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
-    cload();
     compute(E1, U1, 3);
   }
   // epilogue: every wave is done with the operand buffers after this barrier
@@ -314,7 +314,7 @@ hipError_t trail_update_launch(float* C, int64_t ldc, int M, int N, int K, const
   const bool vec = (lde % 4 == 0) && (ldu % 4 == 0) && (((uintptr_t)Et & 15) == 0) &&
                    (((uintptr_t)Ub & 15) == 0);
   // buffer loads need 32-bit byte extents and 16-byte rows
-  const bool dma = vec && (ldc % 4 == 0) && (((uintptr_t)C & 15) == 0) && K <= 4 * kKS &&
+  const bool dma = vec && (ldc % 4 == 0) && (((uintptr_t)C & 15) == 0) && K <= 4 * kKS && N >= 4 &&
                    (int64_t)K * std::max(lde, ldu) * 4 < (int64_t(1) << 31);
   if (dma) {
     const dim3 g((unsigned)(tm * tn)), b(kThreads);
