@@ -186,17 +186,19 @@ __device__ __forceinline__ void static_for(F&& f) {
 // Hence T M^-T D^-1/2 = m_T D^1/2: the Cholesky tile of T, and for T = I the
 // transpose of D^-1/2 M^-1, the inverse of the diagonal Cholesky factor.
 //
-// Pivots go in panels of 8 columns.  Wave 0 factors a panel with one row per
-// lane in registers (pivot-row values by readlane: a_jc = a_cj sits in lane c),
-// then stores
+// Pivots go in panels of 8 columns.  Wave 0 eliminates the diagonal block Dm
+// alone, one row per lane in registers (pivot-row values by readlane:
+// a_jc = a_cj sits in lane c), and stores
 //   W  = pivot-time column values a_ij (i >= j) in the lower part of S0,
-//   M^T in the upper part of S0 (row j, columns i > j),
-//   m_T in place of T's panel columns, and d_j in dv.
-// The rank-8 update of everything right of the panel runs on fp64 MFMA in
-// 16x16 tiles.  Wave 0 takes the tiles of the next 16 columns and goes on to
-// factor the next panel at once; waves 1-3 take the remaining tiles; one
-// barrier per panel.  Tiles never overlap between the two groups, and neither
-// group reads what the other writes within a panel step.
+//   M^T in the upper part of S0 (row j, columns i > j), d_j in dv, 1/d_j in rdv.
+// The rank-8 update of Dm right of the panel runs on fp64 MFMA in 16x16 tiles:
+// wave 0 takes the next 16 columns and goes on to the next panel at once.
+// The stacked rows T follow one panel behind, off wave 0's path: each of waves
+// 1-3 owns fixed 16-row blocks of T (wave 1 two, waves 2 and 3 one each), turns
+// their panel columns into multipliers m_T by forward substitution with the
+// panel's W and 1/d, and applies the rank-8 update to its own rows; waves 2 and
+// 3 also take the Dm tiles right of the next 16 columns.  One barrier per panel;
+// within a panel step no wave reads what another writes.
 // ---------------------------------------------------------------------------
 enum : int { kTileDm = 0, kTileT = 1, kTileNone = -1 };
 struct TileDesc {
@@ -249,16 +251,14 @@ __device__ __forceinline__ void rank8_tiles(double* S0, double* S1, int lane, De
   }
 }
 
-// wave 0: factor panel P (columns 8P .. 8P+7) of the stacked rows
+// wave 0: eliminate panel P (columns 8P .. 8P+7) of Dm, one row per lane
 template <int P>
-__device__ __forceinline__ void ldl_panel(double* S0, double* S1, double* dv, int lane) {
+__device__ __forceinline__ void ldl_dm_panel(double* S0, double* dv, double* rdv, int lane) {
   constexpr int J0 = 8 * P;
-  double v[8], vt[8], mu[8];
+  double v[8], mu[8];
 #pragma unroll
   for (int c = 0; c < 8; ++c) v[c] = S0[lane * kP + J0 + c];
-#pragma unroll
-  for (int c = 0; c < 8; ++c) vt[c] = S1[lane * kP + J0 + c];
-  double dsel = 0.0;
+  double dsel = 0.0, rsel = 0.0;
 #pragma unroll
   for (int jj = 0; jj < 8; ++jj) {
     const double dj = readlane_f64(v[jj], J0 + jj);
@@ -267,23 +267,43 @@ __device__ __forceinline__ void ldl_panel(double* S0, double* S1, double* dv, in
     for (int j2 = jj + 1; j2 < 8; ++j2) s[j2] = readlane_f64(v[jj], J0 + j2);  // a_{j, j2}
     const double rd = rcp_f64(dj);
     mu[jj] = (lane > J0 + jj) ? v[jj] * rd : 0.0;
-    vt[jj] *= rd;
 #pragma unroll
-    for (int j2 = jj + 1; j2 < 8; ++j2) {
-      v[j2] = fma(-mu[jj], s[j2], v[j2]);
-      vt[j2] = fma(-vt[jj], s[j2], vt[j2]);
-    }
+    for (int j2 = jj + 1; j2 < 8; ++j2) v[j2] = fma(-mu[jj], s[j2], v[j2]);
     dsel = (lane == jj) ? dj : dsel;
+    rsel = (lane == jj) ? rd : rsel;
   }
-  if (lane < 8) dv[J0 + lane] = dsel;
+  if (lane < 8) {
+    dv[J0 + lane] = dsel;
+    rdv[J0 + lane] = rsel;
+  }
 #pragma unroll
   for (int c = 0; c < 8; ++c)
     if (lane >= J0 + c) S0[lane * kP + J0 + c] = v[c];
 #pragma unroll
   for (int c = 0; c < 8; ++c)
     if (lane > J0 + c) S0[(J0 + c) * kP + lane] = mu[c];
+}
+
+// rows row0 .. row0 + nrows - 1 of T (one per lane): the same eliminations of
+// panel P, t_j <- t_j / d_j, then t_j2 -= t_j a_{j, j2} (a_{j, j2} = W[j2][j]),
+// leaving the multipliers m_T in the panel columns
+template <int P>
+__device__ __forceinline__ void t_panel(const double* S0, double* S1, const double* rdv, int lane, int row0,
+                                        int nrows) {
+  constexpr int J0 = 8 * P;
+  if (lane >= nrows) return;
+  double* r = S1 + (row0 + lane) * kP + J0;
+  double tv[8];
 #pragma unroll
-  for (int c = 0; c < 8; ++c) S1[lane * kP + J0 + c] = vt[c];
+  for (int c = 0; c < 8; ++c) tv[c] = r[c];
+#pragma unroll
+  for (int jj = 0; jj < 8; ++jj) {
+    tv[jj] *= rdv[J0 + jj];
+#pragma unroll
+    for (int j2 = jj + 1; j2 < 8; ++j2) tv[j2] = fma(-tv[jj], S0[(J0 + j2) * kP + J0 + jj], tv[j2]);
+  }
+#pragma unroll
+  for (int c = 0; c < 8; ++c) r[c] = tv[c];
 }
 
 // triangular index (a, b), 1 <= b <= a, in order (1,1) (2,1) (2,2) (3,1) ...
@@ -292,35 +312,38 @@ __device__ __forceinline__ void tri_ab(int i, int& a, int& b) {
   b = i - (a - 1) * a / 2 + 1;
 }
 
-__device__ __forceinline__ void ldl_stacked(double* S0, double* S1, double* dv, int t) {
+__device__ __forceinline__ void ldl_stacked(double* S0, double* S1, double* dv, double* rdv, int t) {
   const int lane = t & 63, w = t >> 6;
-  if (w == 0) ldl_panel<0>(S0, S1, dv, lane);
+  if (w == 0) ldl_dm_panel<0>(S0, dv, rdv, lane);
   __syncthreads();
-  static_for<0, kNB / 8 - 1>([&](auto PP) {
+  static_for<0, kNB / 8>([&](auto PP) {
     constexpr int P = decltype(PP)::value;
     constexpr int J0 = 8 * P, T0 = J0 + 8;
-    constexpr int nT = (kNB - T0 + 15) / 16;                    // 16-wide column blocks right of the panel
-    constexpr int nDm = nT * (nT - 1) / 2, nTr = 4 * (nT - 1);  // tiles outside column block 0
-    constexpr int nRest = nDm + nTr;
+    constexpr int nT = (kNB - T0 + 15) / 16;  // 16-wide column blocks right of the panel
+    constexpr int nDm = nT * (nT - 1) / 2;    // Dm tiles outside column block 0
     if (w == 0) {
-      // column block 0 (holds the next panel): Dm (a, 0) and T (q, 0)
-      rank8_tiles<J0, nT + 4>(S0, S1, lane, [&](int u) {
-        return (u < nT) ? TileDesc{kTileDm, T0 + 16 * u, T0} : TileDesc{kTileT, 16 * (u - nT), T0};
-      });
-      ldl_panel<P + 1>(S0, S1, dv, lane);
-    } else if constexpr (nRest > 0) {
-      const int wv = w - 1;
-      rank8_tiles<J0, (nRest + 2) / 3>(S0, S1, lane, [&](int u) {
-        const int i = wv + 3 * u;
-        if (i >= nRest) return TileDesc{kTileNone, 0, 0};
-        if (i < nDm) {
+      if constexpr (nT > 0) {
+        rank8_tiles<J0, nT>(S0, S1, lane, [&](int u) { return TileDesc{kTileDm, T0 + 16 * u, T0}; });
+        ldl_dm_panel<P + 1>(S0, dv, rdv, lane);
+      }
+    } else if (w == 1) {
+      t_panel<P>(S0, S1, rdv, lane, 0, 32);
+      if constexpr (nT > 0)
+        rank8_tiles<J0, 2 * nT>(S0, S1, lane, [&](int u) {
+          return TileDesc{kTileT, 16 * (u / nT), T0 + 16 * (u % nT)};
+        });
+    } else {
+      const int q = w;  // T rows 16 q .. 16 q + 15 (q = 2, 3)
+      t_panel<P>(S0, S1, rdv, lane, 16 * q, 16);
+      if constexpr (nT > 0)
+        rank8_tiles<J0, nT + (nDm + 1) / 2>(S0, S1, lane, [&](int u) {
+          if (u < nT) return TileDesc{kTileT, 16 * q, T0 + 16 * u};
+          const int i = 2 * (u - nT) + (q - 2);
+          if (i >= nDm) return TileDesc{kTileNone, 0, 0};
           int a, b;
           tri_ab(i, a, b);
           return TileDesc{kTileDm, T0 + 16 * a, T0 + 16 * b};
-        }
-        const int q = (i - nDm) / (nT - 1), b = 1 + (i - nDm) % (nT - 1);
-        return TileDesc{kTileT, 16 * q, T0 + 16 * b};
-      });
+        });
     }
     __syncthreads();
   });
@@ -328,7 +351,7 @@ __device__ __forceinline__ void ldl_stacked(double* S0, double* S1, double* dv, 
 
 struct PanelSmem {
   double S0[kNB * kP], S1[kNB * kP];
-  double dv[kNB], sq[kNB], rsq[kNB];
+  double dv[kNB], rdv[kNB], sq[kNB], rsq[kNB];
   int fail;
 };
 
@@ -385,7 +408,7 @@ __device__ __forceinline__ void task_panel(const StepArgs a, int b, PanelSmem& s
       }
   if (t == 0) sm.fail = kNB;
   __syncthreads();
-  ldl_stacked(sm.S0, sm.S1, sm.dv, t);
+  ldl_stacked(sm.S0, sm.S1, sm.dv, sm.rdv, t);
   if (t < kNB) {
     const double dj = sm.dv[t];
     if (!(dj > 0.0)) atomicMin(&sm.fail, t);
