@@ -55,6 +55,8 @@ def parse():
                     help="with --pipeline: every block sees the unquantized model's activations")
     ap.add_argument("--gptq2d", action="store_true",
                     help="time two-sided adaptive rounding of a 4096 x 4096 fp16 matrix instead of the layer")
+    ap.add_argument("--loop-ffn", action="store_true",
+                    help="time the lazy-batch loop alone at the 175B-class FFN shape (49152 x 12288)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="run two plain device-to-device copies of BYTES bytes and exit (the reference "
                          "kernel for scaling the FETCH_SIZE / WRITE_SIZE counters)")
@@ -490,6 +492,83 @@ def gptq2d_bench(args):
     print(json.dumps(out), flush=True)
 
 
+def loop_ffn_bench(args):
+    """The lazy-batch loop alone at the 175B-class FFN shape: W_fc 49152 x 12288 fp16,
+    3-bit, group 128, B = 128.  U comes from H = 2 X^T X of the first 16384-row
+    chunk of the layer's calibration stream with 1% damping (the factor at this d is
+    timed separately as a stage); the timed call is gptq_quantize_layer."""
+    import torch
+    import post_weight_quantization_02_amd as G
+    import workloads as wl
+
+    spec = wl.workload_layers(5)[0]
+    dr, d = spec.d_row, spec.d_col
+    dev = torch.device("cuda:0")
+    W = torch.from_numpy(wl.make_weight(spec)).to(dev)
+    H = torch.zeros(d, d, device=dev)
+    G.gptq_hessian_accumulate(H, torch.from_numpy(wl.make_x_chunk(spec, 0)).to(dev))
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    U, lam, info = G.gptq_prepare_hinv(H, spec.percdamp)
+    e1.record()
+    torch.cuda.synchronize()
+    if int(info.item()) != 0:
+        raise SystemExit(f"factor failed: info={int(info.item())}")
+    t_factor = e0.elapsed_time(e1) / 1e3
+    ng = d // spec.group_size
+    codes = torch.empty(dr, d, dtype=torch.uint8, device=dev)
+    scales = torch.empty(dr, ng, device=dev)
+    zeros = torch.empty(dr, ng, dtype=torch.int32, device=dev)
+    err = torch.empty(1, dtype=torch.float64, device=dev)
+    ws = torch.empty(G.gptq_quantize_layer_workspace_size(dr, d, spec.block_size), dtype=torch.uint8,
+                     device=dev)
+
+    def step():
+        G.gptq_quantize_layer(W, U, lam, spec.bits, spec.group_size, spec.block_size, codes, scales, zeros,
+                              err, ws=ws)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    e0.record()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    e1.record()
+    torch.cuda.synchronize()
+    wall = (time.perf_counter() - t0) / args.steps
+    t = e0.elapsed_time(e1) / 1e3 / args.steps
+    flops_gemm = dr * d * (d - spec.block_size)     # sum over blocks of 2 * d_row * B * (d - i2)
+    ach = flops_gemm / t / 1e12
+    log(f"bench: lazy-batch loop {t * 1e3:.2f} ms at {dr}x{d}; factor {t_factor * 1e3:.2f} ms")
+    out = {
+        "metric": "lazy-batch loop s/layer (175B-class FFN W_fc 49152x12288, 3-bit g128)",
+        "value": round(t, 6),
+        "unit": "s/layer",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall * 1e3, 4),
+        "higher_is_better": False,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32 loop (fp32 MFMA out-of-block correction)",
+        "data": "synthetic",
+        "config": {"workload": "w_fc: W 49152x12288 fp16 N(0, 0.01^2); H from one 16384-row chunk of the "
+                               "k^-1 power-law stream, 1% damping; 3-bit asymmetric, group 128, block 128",
+                   "d_row": dr, "d_col": d, "bits": spec.bits, "group_size": spec.group_size,
+                   "block_size": spec.block_size, "parallelism": "single-gpu"},
+        "stages": {"factor_ms": round(t_factor * 1e3, 3), "err": float(err.item()),
+                   "trailing_gemm_tflop": round(flops_gemm / 1e12, 3)},
+        # the whole loop's time stands in for the correction's own: a lower bound on its rate
+        "roofline": {"bound": "mfma", "kernel": "trail_dma_kernel (whole-loop time, a lower bound on its rate)",
+                     "achieved": round(ach, 2), "peak": 157.3, "unit": "TFLOP/s",
+                     "frac": round(ach / 157.3, 4), "traffic": None},
+        "cpu_baseline": None,
+    }
+    print(json.dumps(out), flush=True)
+
+
 def main():
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -517,6 +596,9 @@ def main():
         return
     if args.gptq2d:
         gptq2d_bench(args)
+        return
+    if args.loop_ffn:
+        loop_ffn_bench(args)
         return
 
     import post_weight_quantization_02_amd as G
