@@ -18,8 +18,10 @@
 // Kernels: damp (lambda, info = 0) -> reversed fp64 copy with lambda on the
 // diagonal -> one launch per 64-column block (blocked right-looking Cholesky
 // with look-ahead; each diagonal block's inverse comes out of its
-// factorization) -> recursive-doubling triangular inverse, two batched fp32
-// MFMA products per level -> reversed write of U.
+// factorization); past 96 blocks the trailing updates of each step are confined
+// to its group of eight blocks (512 columns), with one rank-512 update of the
+// rest of the matrix after each group -> recursive-doubling triangular inverse,
+// two batched fp32 MFMA products per level -> reversed write of U.
 #include "gptq_internal.h"
 
 namespace gptq {
@@ -91,7 +93,10 @@ __global__ __launch_bounds__(kThreads) void rev_copy_kernel(const float* __restr
 //      (each P work-group redundantly), and solve its own tile:
 //      L[r][c] = T Lcc^-T.  The r == c work-group writes Lcc^-1 as the
 //      diagonal block of L^-1 (Lcc itself is never needed again).
-//   UC (tiles (i, j), i >= j >= k+2): A[i][j] -= L[i][k] L[j][k]^T (fp64 MFMA)
+//   UC (tiles (i, j), i >= j >= k+2, j < jend): A[i][j] -= L[i][k] L[j][k]^T
+//      (fp64 MFMA); jend is the end of the step's column group, whose steps
+//      reach the block columns past it in one rank-512 update instead.  The
+//      first launch of a group (skip_step) finds step k already applied.
 // ---------------------------------------------------------------------------
 struct StepArgs {
   double* A;
@@ -99,6 +104,8 @@ struct StepArgs {
   int32_t* info;
   int d, nblk, k;
   int np, nuc;
+  int jend;       // update tiles only in block columns < jend
+  int skip_step;  // step k already applied (by the column group's rank-512 update)
 };
 
 // C[m][n] (this wave's 32x32 quadrant) += sum_k SA[m][k] SB[n][k], fp64 MFMA
@@ -134,22 +141,31 @@ __device__ __forceinline__ void zero_acc(f64x4 (&acc)[2][2]) {
     for (int y = 0; y < 2; ++y) acc[x][y] = f64x4{0.0, 0.0, 0.0, 0.0};
 }
 
-// load a 64x64 fp64 tile (rows R0.., cols C0..) into LDS [row][col], zeros outside d.
-// All global loads are issued before any LDS store (one memory round trip).
-__device__ __forceinline__ void load_tile_f64(double* S, const double* __restrict__ A, int64_t d,
-                                              int64_t R0, int64_t C0, int t) {
-  double v[16];
+// a 64x64 fp64 tile (rows R0.., cols C0..) into registers, zeros outside d
+__device__ __forceinline__ void load_tile_regs(double (&v)[16], const double* __restrict__ A, int64_t d,
+                                               int64_t R0, int64_t C0, int t) {
 #pragma unroll
   for (int u = 0; u < 16; ++u) {
     const int idx = t + u * kThreads;
     const int r = idx >> 6, c = idx & 63;
     v[u] = (R0 + r < d && C0 + c < d) ? A[(R0 + r) * d + C0 + c] : 0.0;
   }
+}
+__device__ __forceinline__ void store_tile_lds(double* S, const double (&v)[16], int t) {
 #pragma unroll
   for (int u = 0; u < 16; ++u) {
     const int idx = t + u * kThreads;
     S[(idx >> 6) * kP + (idx & 63)] = v[u];
   }
+}
+
+// load a 64x64 fp64 tile into LDS [row][col], zeros outside d.
+// All global loads are issued before any LDS store (one memory round trip).
+__device__ __forceinline__ void load_tile_f64(double* S, const double* __restrict__ A, int64_t d,
+                                              int64_t R0, int64_t C0, int t) {
+  double v[16];
+  load_tile_regs(v, A, d, R0, C0, t);
+  store_tile_lds(S, v, t);
 }
 
 // 1/x: the hardware estimate (relative error below 2^-22) refined by one
@@ -386,7 +402,7 @@ __device__ __forceinline__ void task_panel(const StepArgs a, int b, PanelSmem& s
   f64x4 accD[2][2], accT[2][2];
   zero_acc(accD);
   zero_acc(accT);
-  if (a.k >= 0) {
+  if (a.k >= 0 && !a.skip_step) {
     load_tile_f64(sm.S0, a.A, d, C0, K0, t);            // L[c1][k]
     if (!own) load_tile_f64(sm.S1, a.A, d, R0, K0, t);  // L[r][k]
     __syncthreads();
@@ -439,11 +455,14 @@ __device__ __forceinline__ void task_panel(const StepArgs a, int b, PanelSmem& s
 __device__ __forceinline__ void task_update_chol(const StepArgs a, int b, PanelSmem& sm) {
   const int t = threadIdx.x, lane = t & 63, w = t >> 6, wm = w & 1, wn = w >> 1;
   const int64_t d = a.d;
-  int i = (int)((sqrt(8.0 * (double)b + 1.0) - 1.0) * 0.5);
-  while ((i + 1) * (i + 2) / 2 <= b) ++i;
-  while (i * (i + 1) / 2 > b) --i;
-  const int j = b - i * (i + 1) / 2;
-  const int base = a.k + 2;
+  // tiles (i, j), j = 0 .. jend - base - 1, i = j .. nblk - base - 1, column by column
+  const int base = a.k + 2, m = a.nblk - base;
+  int j = 0;
+  while (b >= m - j) {
+    b -= m - j;
+    ++j;
+  }
+  const int i = j + b;
   const int64_t R0 = (int64_t)(base + i) * kNB, C0 = (int64_t)(base + j) * kNB,
                 K0 = (int64_t)a.k * kNB;
   load_tile_f64(sm.S0, a.A, d, R0, K0, t);
@@ -482,6 +501,60 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
   }
   b -= a.np;
   if (b < a.nuc) task_update_chol(a, b, sm);
+}
+
+// ---------------------------------------------------------------------------
+// The steps of one column group (blocks jb .. je-1) applied at once to the block
+// columns past it: A[i][j] -= sum_s L[i][s] L[j][s]^T, je <= j <= i (fp64 MFMA,
+// K = 64 (je - jb)).  One 64x64 tile per work-group, C read and written once;
+// the next step's two L tiles load into registers under the current products.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) void chol_group_update_kernel(
+    double* __restrict__ A, int d, int jb, int je) {
+  __shared__ double S0[kNB * kP], S1[kNB * kP];
+  const int t = threadIdx.x, lane = t & 63, w = t >> 6, wm = w & 1, wn = w >> 1;
+  const int b = blockIdx.x;
+  int i = (int)((sqrt(8.0 * (double)b + 1.0) - 1.0) * 0.5);
+  while ((i + 1) * (i + 2) / 2 <= b) ++i;
+  while (i * (i + 1) / 2 > b) --i;
+  const int j = b - i * (i + 1) / 2;
+  const int64_t dd = d;
+  const int64_t R0 = (int64_t)(je + i) * kNB, C0 = (int64_t)(je + j) * kNB;
+  double va[16], vb[16];
+  load_tile_regs(va, A, dd, R0, (int64_t)jb * kNB, t);
+  load_tile_regs(vb, A, dd, C0, (int64_t)jb * kNB, t);
+  double c[16];
+#pragma unroll
+  for (int fm = 0; fm < 2; ++fm)
+#pragma unroll
+    for (int fn = 0; fn < 2; ++fn)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int64_t row = R0 + nt_row(lane, wm, fm, q), col = C0 + nt_col(lane, wn, fn);
+        c[(fm * 2 + fn) * 4 + q] = (row < dd && col <= row) ? A[row * dd + col] : 0.0;
+      }
+  f64x4 acc[2][2];
+  zero_acc(acc);
+  for (int s = jb; s < je; ++s) {
+    store_tile_lds(S0, va, t);
+    store_tile_lds(S1, vb, t);
+    __syncthreads();
+    if (s + 1 < je) {
+      load_tile_regs(va, A, dd, R0, (int64_t)(s + 1) * kNB, t);
+      load_tile_regs(vb, A, dd, C0, (int64_t)(s + 1) * kNB, t);
+    }
+    mma_nt_f64(S0, S1, acc, lane, wm, wn);
+    __syncthreads();
+  }
+#pragma unroll
+  for (int fm = 0; fm < 2; ++fm)
+#pragma unroll
+    for (int fn = 0; fn < 2; ++fn)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int64_t row = R0 + nt_row(lane, wm, fm, q), col = C0 + nt_col(lane, wn, fn);
+        if (row < dd && col <= row) A[row * dd + col] = c[(fm * 2 + fn) * 4 + q] - acc[fm][fn][q];
+      }
 }
 
 // ---------------------------------------------------------------------------
@@ -730,19 +803,38 @@ hipError_t factor_launch(const FactorPlan& p, const float* H, const int32_t* per
   hipLaunchKernelGGL(rev_copy_kernel, dim3(nt, nt), dim3(kThreads), 0, s, H, d, lam, perm, A);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   const int nblk = (int)p.nblk;
-  for (int k = -1; k < nblk - 1; ++k) {
-    StepArgs a{};
-    a.A = A;
-    a.Linv = Linv;
-    a.info = info;
-    a.d = (int)d;
-    a.nblk = nblk;
-    a.k = k;
-    a.np = nblk - (k + 1);
-    const int m = nblk - k - 2;
-    a.nuc = (k >= 0 && m > 0) ? m * (m + 1) / 2 : 0;
-    hipLaunchKernelGGL(chol_step_kernel, dim3((unsigned)(a.np + a.nuc)), dim3(kThreads), 0, s, a);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
+  // 64-column blocks per column group.  Up to 96 blocks one group spans the
+  // matrix (every step updates the whole trailing triangle under the panel
+  // chain); past that the trailing updates outgrow the chain and groups of 8
+  // blocks (512 columns) with one rank-512 update each are faster (measured:
+  // equal at d = 6144, 9% faster at 8192, 20% at 12288, 5-10% slower at
+  // 2048-4096).
+  const int kGroup = nblk > 96 ? 8 : nblk;
+  for (int jb = 0; jb < nblk; jb += kGroup) {
+    const int je = std::min(jb + kGroup, nblk);
+    for (int k = jb - 1; k < je - 1; ++k) {
+      StepArgs a{};
+      a.A = A;
+      a.Linv = Linv;
+      a.info = info;
+      a.d = (int)d;
+      a.nblk = nblk;
+      a.k = k;
+      a.np = nblk - (k + 1);
+      a.jend = je;
+      a.skip_step = (jb > 0 && k == jb - 1) ? 1 : 0;
+      const int m = nblk - (k + 2);  // block rows past column k+1
+      const int w = je - (k + 2);    // block columns of the group past column k+1
+      a.nuc = (k >= 0 && !a.skip_step && w > 0) ? w * m - w * (w - 1) / 2 : 0;
+      hipLaunchKernelGGL(chol_step_kernel, dim3((unsigned)(a.np + a.nuc)), dim3(kThreads), 0, s, a);
+      if ((e = hipGetLastError()) != hipSuccess) return e;
+    }
+    if (je < nblk) {
+      const int m = nblk - je;
+      hipLaunchKernelGGL(chol_group_update_kernel, dim3((unsigned)(m * (m + 1) / 2)), dim3(kThreads), 0, s, A,
+                         (int)d, jb, je);
+      if ((e = hipGetLastError()) != hipSuccess) return e;
+    }
   }
   const bool vec = (d % 4) == 0;
   for (int64_t sb = 1; sb < p.nblk; sb *= 2) {

@@ -104,6 +104,9 @@ F_CASES = [
     ("tiny_2", lambda: O.hessian([case_x("ar1", 10, 2, np.float32, 14)])),
     ("tiny_1", lambda: O.hessian([case_x("ar1", 10, 1, np.float32, 15)])),
     ("powerlaw_1536", lambda: O.hessian([case_x("powerlaw", 6144, 1536, np.float16, 16)])),
+    # 97 blocks of 64, the last 56 wide: past 96 blocks the factor runs in column
+    # groups of 512 with one rank-512 update per group
+    ("lowrank_6200_grouped", lambda: O.hessian([case_x("lowrank", 4096, 6200, np.float16, 17)])),
 ]
 
 
