@@ -10,7 +10,7 @@
 // groups of positions stay contiguous; the product then gathers X in the same
 // order.
 //
-// Product (MI355X): HBM-bound on the packed words.  Three kernels:
+// Product (MI355X): HBM-bound on the packed words.  Four kernels:
 //  - gemv1_f16_kernel: one row of fp16 X (the per-token product) whose width fits
 //    one LDS tile, groups of whole 32-code chunks; a persistent grid, codes turned
 //    into fp16 pairs and multiplied by v_dot2_f32_f16, loads one step ahead.
