@@ -57,6 +57,8 @@ def parse():
                     help="time two-sided adaptive rounding of a 4096 x 4096 fp16 matrix instead of the layer")
     ap.add_argument("--loop-ffn", action="store_true",
                     help="time the lazy-batch loop alone at the 175B-class FFN shape (49152 x 12288)")
+    ap.add_argument("--configs", action="store_true",
+                    help="seconds per layer for every layer shape of the five configurations")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="run two plain device-to-device copies of BYTES bytes and exit (the reference "
                          "kernel for scaling the FETCH_SIZE / WRITE_SIZE counters)")
@@ -569,6 +571,88 @@ def loop_ffn_bench(args):
     print(json.dumps(out), flush=True)
 
 
+def configs_bench(args):
+    """Seconds per layer for every layer of the five configurations, at their full
+    weight shapes and calibration row counts, through the three library calls on
+    resident inputs.  Timing-only inputs: X and W are seeded Gaussian tensors of the
+    configurations' shapes and dtypes drawn on the GPU (the host cannot synthesise
+    the 25.8 GB power-law stream of the widest layer in a benchmark's time); the
+    recipe inputs are checked for parity at these shapes by the GPU tests."""
+    import torch
+    import post_weight_quantization_02_amd as G
+    import workloads as wl
+
+    dev = torch.device("cuda:0")
+    out = {}
+    for cfg in (1, 2, 3, 4, 5):
+        layers = wl.workload_layers(cfg)
+        if cfg == 2:
+            layers = layers[:4]          # the six blocks repeat the same four shapes
+        for spec in layers:
+            gen = torch.Generator(device=dev)
+            gen.manual_seed(1000 * cfg + spec.layer)
+            xdt = torch.float16 if spec.x_dtype == "f16" else torch.float32
+            wdt = torch.float16 if spec.w_dtype == "f16" else torch.float32
+            X = torch.randn(spec.n_rows, spec.d_col, device=dev, generator=gen).to(xdt)
+            W = (spec.w_std * torch.randn(spec.d_row, spec.d_col, device=dev, generator=gen)).to(wdt)
+            d, dr = spec.d_col, spec.d_row
+            H = torch.zeros(d, d, device=dev)
+            ws_h = torch.empty(G.gptq_hessian_accumulate_workspace_size(d, spec.n_rows, G.GPTQ_F16 if spec.x_dtype == "f16" else G.GPTQ_F32),
+                               dtype=torch.uint8, device=dev)
+            ws_f = torch.empty(G.gptq_prepare_hinv_workspace_size(d), dtype=torch.uint8, device=dev)
+            ws_q = torch.empty(G.gptq_quantize_layer_workspace_size(dr, d, spec.block_size), dtype=torch.uint8,
+                               device=dev)
+            U = torch.empty(d, d, device=dev)
+            lam = torch.empty(1, device=dev)
+            info = torch.empty(1, dtype=torch.int32, device=dev)
+            ng = -(-d // spec.group_size) if spec.group_size else 1
+            codes = torch.empty(dr, d, dtype=torch.uint8, device=dev)
+            scales = torch.empty(dr, ng, device=dev)
+            zeros = torch.empty(dr, ng, dtype=torch.int32, device=dev)
+            err = torch.empty(1, dtype=torch.float64, device=dev)
+            ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+
+            def step(rec):
+                H.zero_()
+                if rec:
+                    ev[0].record()
+                G.gptq_hessian_accumulate(H, X, ws=ws_h)
+                if rec:
+                    ev[1].record()
+                G.gptq_prepare_hinv(H, spec.percdamp, U, lam, info, ws=ws_f)
+                if rec:
+                    ev[2].record()
+                G.gptq_quantize_layer(W, U, lam, spec.bits, spec.group_size, spec.block_size, codes, scales,
+                                      zeros, err, ws=ws_q)
+                if rec:
+                    ev[3].record()
+
+            step(False)
+            torch.cuda.synchronize()
+            reps = max(1, min(args.steps, 3))
+            st = [0.0, 0.0, 0.0]
+            for _ in range(reps):
+                step(True)
+                torch.cuda.synchronize()
+                for k in range(3):
+                    st[k] += ev[k].elapsed_time(ev[k + 1]) / 1e3 / reps
+            if int(info.item()) != 0:
+                raise SystemExit(f"{spec.name}: factor failed (info={int(info.item())})")
+            key = f"config{cfg}:{spec.name}"
+            out[key] = {"d_row": dr, "d_col": d, "n_rows": spec.n_rows, "bits": spec.bits,
+                        "group_size": spec.group_size, "s_per_layer": round(sum(st), 6),
+                        "hessian_ms": round(st[0] * 1e3, 3), "factor_ms": round(st[1] * 1e3, 3),
+                        "quantize_ms": round(st[2] * 1e3, 3)}
+            log(f"bench: {key} {sum(st) * 1e3:.2f} ms (H {st[0] * 1e3:.2f}, factor {st[1] * 1e3:.2f}, "
+                f"loop {st[2] * 1e3:.2f})")
+            del X, W, H, ws_h, ws_f, ws_q, U, codes, scales, zeros
+            torch.cuda.empty_cache()
+    print(json.dumps({"metric": "GPTQ s/layer per configuration (timing-only Gaussian inputs of the "
+                                "configurations' shapes, drawn on the GPU)",
+                      "unit": "s/layer", "n_gpus": 1, "higher_is_better": False, "data": "synthetic",
+                      "layers": out}), flush=True)
+
+
 def main():
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -599,6 +683,9 @@ def main():
         return
     if args.loop_ffn:
         loop_ffn_bench(args)
+        return
+    if args.configs:
+        configs_bench(args)
         return
 
     import post_weight_quantization_02_amd as G
