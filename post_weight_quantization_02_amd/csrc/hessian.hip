@@ -161,13 +161,15 @@ __global__ __launch_bounds__(kThreads) void syrk_f16_kernel(
   const int nfull = full_cols ? nrows / kKS16 : 0;
   const int nq = nfull >> 2;  // pipelined stages come in fours
   if (nq > 0) {
-    // buffer loads with a uniform base and per-stage offset; the launch keeps the
-    // split's byte span below 2^31
-    const uint64_t xb = (uint64_t)(uintptr_t)Xs;
-    const uint64_t xu = ((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(xb >> 32)) << 32) |
-                        (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)xb);
-    const __amdgpu_buffer_rsrc_t rsrc =
-        __builtin_amdgcn_make_buffer_rsrc((void*)(uintptr_t)xu, (short)0, 0x7FFFFFFF, 0x00020000);
+    // buffer loads with a uniform base that moves with each group of four stages
+    // and a per-stage offset inside the group, so the 32-bit offsets span at most
+    // five stages of rows at any row width (the launch checks that bound)
+    auto rsrc_at = [&](int st) {
+      const uint64_t xb = (uint64_t)(uintptr_t)(Xs + (int64_t)(st & ~3) * kKS16 * ldx);
+      const uint64_t xu = ((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(xb >> 32)) << 32) |
+                          (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)xb);
+      return __builtin_amdgcn_make_buffer_rsrc((void*)(uintptr_t)xu, (short)0, 0x7FFFFFFF, 0x00020000);
+    };
     const uint32_t ldb = (uint32_t)ldx * 2u;
     // load j (0..3) of this wave fills rows 8 w + 2 j, + 1 of the operand; lane l
     // brings chunk l % 32 of row 8 w + 2 j + l / 32 (its logical chunk unswizzled)
@@ -181,7 +183,9 @@ __global__ __launch_bounds__(kThreads) void syrk_f16_kernel(
     }
     const int last = 4 * nq - 1;
     auto dma = [&](_Float16* L, int st) {
-      const int so = __builtin_amdgcn_readfirstlane((int)((uint32_t)(min(st, last) * kKS16) * ldb));
+      const int sc = min(st, last);
+      const __amdgpu_buffer_rsrc_t rsrc = rsrc_at(sc);
+      const int so = __builtin_amdgcn_readfirstlane((int)((uint32_t)((sc & 3) * kKS16) * ldb));
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (void GPTQ_LDS*)(L + (8 * w + 2 * j) * kBT16), 16,
@@ -506,8 +510,6 @@ HessianPlan hessian_plan(int64_t d, int64_t n, int dtype) {
   }
   int64_t rps = cdiv(n, ns);
   rps = cdiv(rps, ks) * ks;
-  const int64_t rps_max = std::max<int64_t>(ks, ((int64_t(1) << 31) / std::max<int64_t>(d, 1)) / ks * ks);
-  rps = std::min(rps, rps_max);
   p.rows_per_split = rps;
   p.nsplit = cdiv(n, rps);
   p.ws_bytes = (size_t)p.nsplit * (size_t)p.ntiles * (size_t)p.bt * (size_t)p.bt * sizeof(float);
@@ -521,8 +523,8 @@ hipError_t hessian_launch(const HessianPlan& p, float* H, int64_t d, const void*
   float* part = (float*)ws;
   const int64_t grid = p.ntiles * p.nsplit;
   if (p.dtype == 1) {
-    // the fast path addresses a split with 32-bit byte offsets
-    const bool fits = (p.rows_per_split + kKS16) * ldx * 2 < (int64_t(1) << 31);
+    // the fast path addresses five stages of rows with 32-bit byte offsets
+    const bool fits = (int64_t)(5 * kKS16) * ldx * 2 + 2 * d < (int64_t(1) << 31);
     const bool vec = fits && (d % 8 == 0) && (ldx % 8 == 0) && (((uintptr_t)X & 15) == 0);
     if (vec)
       hipLaunchKernelGGL(syrk_f16_kernel<true>, dim3((unsigned)grid), dim3(kThreads), 0, s,
