@@ -445,10 +445,16 @@ __device__ __forceinline__ void task_panel(const StepArgs a, int b, PanelSmem& s
     if (t == 0 && sm.fail < nbe && *a.info == 0) *a.info = (int32_t)(d - (C0 + sm.fail));
     return;
   }
-  // L[r][c1] = m_T D^1/2
+  // L[r][c1] = m_T D^1/2, and its fp32 rounding at the same place of L^-1's
+  // buffer: the block is read there by the one triangular-inverse product that
+  // needs it, before the product after it overwrites the block with L^-1's
   for (int idx = t; idx < kNB * kNB; idx += kThreads) {
     const int i = idx >> 6, c = idx & 63;
-    if (R0 + i < d && c < nbe) a.A[(R0 + i) * d + C0 + c] = sm.S1[i * kP + c] * sm.sq[c];
+    if (R0 + i < d && c < nbe) {
+      const double v = sm.S1[i * kP + c] * sm.sq[c];
+      a.A[(R0 + i) * d + C0 + c] = v;
+      a.Linv[(R0 + i) * d + C0 + c] = (float)v;
+    }
   }
 }
 
@@ -564,7 +570,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
 // Level sb (sb = 1, 2, 4, ... blocks) pairs A = blocks [2 p sb, 2 p sb + sb)
 // with C = the next sb blocks (clipped at the end of the matrix).  With A^-1
 // and C^-1 from the levels below it runs two batched products:
-//   mode 0:  T = B A^-1   (B = L[C][A], the fp64 factor rounded to fp32; A^-1
+//   mode 0:  T = B A^-1   (B = L[C][A], the fp64 factor rounded to fp32, which
+//                          the Cholesky left at the same place of L^-1's buffer; A^-1
 //                          is lower triangular, so output block column j sums
 //                          k = j .. sb-1)
 //   mode 1:  X = -C^-1 T  (C^-1 lower: output block row i sums k = 0 .. i)
@@ -573,7 +580,6 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
 // and is skipped -- so masking rows and columns >= d of C is enough.
 // ---------------------------------------------------------------------------
 struct TriArgs {
-  const double* L;  // fp64 factor, ld d (off-diagonal blocks)
   float* Linv;      // ld d
   float* Tw;        // scratch: pair p at p (64 sb)^2, ld 64 sb
   int64_t d;
@@ -607,17 +613,17 @@ __global__ __launch_bounds__(kThreads) void tri_gemm_kernel(TriArgs a) {
   float ra[16], rb[16];
   auto gload = [&](int kb) {
     if (MODE == 0) {
-      // A operand: L[C0+bi][A0+kb] (fp64; its columns lie in the A range, < d)
-      const double* src = a.L + arow * d + (int64_t)(A0 + kb) * kNB + sc;
+      // A operand: L[C0+bi][A0+kb] rounded to fp32, from L^-1's buffer (its
+      // columns lie in the A range, < d)
+      const float* src = a.Linv + arow * d + (int64_t)(A0 + kb) * kNB + sc;
 #pragma unroll
-      for (int e = 0; e < 16; e += 2) {
-        if (VEC) {
-          const double2 v = (arow < d) ? *(const double2*)(src + e) : double2{0.0, 0.0};
-          ra[e] = (float)v.x;
-          ra[e + 1] = (float)v.y;
+      for (int e = 0; e < 16; e += 4) {
+        if (VEC && arow < d) {
+          const f32x4 v = *(const f32x4*)(src + e);
+          ra[e] = v[0]; ra[e + 1] = v[1]; ra[e + 2] = v[2]; ra[e + 3] = v[3];
         } else {
-          ra[e] = (arow < d) ? (float)src[e] : 0.f;
-          ra[e + 1] = (arow < d) ? (float)src[e + 1] : 0.f;
+#pragma unroll
+          for (int u = 0; u < 4; ++u) ra[e + u] = (arow < d) ? src[e + u] : 0.f;
         }
       }
       // B operand: L^-1[A0+kb][A0+bj] (inside the A range)
@@ -838,7 +844,7 @@ hipError_t factor_launch(const FactorPlan& p, const float* H, const int32_t* per
   }
   const bool vec = (d % 4) == 0;
   for (int64_t sb = 1; sb < p.nblk; sb *= 2) {
-    TriArgs t{A, Linv, Tw, d, nblk, (int)sb, (int)tri_pairs(p.nblk, sb)};
+    TriArgs t{Linv, Tw, d, nblk, (int)sb, (int)tri_pairs(p.nblk, sb)};
     const dim3 grid((unsigned)(t.npairs * sb * sb));
     if (vec) {
       hipLaunchKernelGGL((tri_gemm_kernel<0, true>), grid, dim3(kThreads), 0, s, t);
