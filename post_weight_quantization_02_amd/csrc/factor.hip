@@ -512,12 +512,17 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
 // ---------------------------------------------------------------------------
 // The steps of one column group (blocks jb .. je-1) applied at once to the block
 // columns past it: A[i][j] -= sum_s L[i][s] L[j][s]^T, je <= j <= i (fp64 MFMA,
-// K = 64 (je - jb)).  One 64x64 tile per work-group, C read and written once;
-// the next step's two L tiles load into registers under the current products.
+// K = 64 (je - jb)).  One 64x64 tile per work-group, C read and written once
+// after the products; K staged 32 columns at a time (34 KB of LDS and few
+// registers, so four work-groups share a CU), the next stage loading into
+// registers under the current products.
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) void chol_group_update_kernel(
+constexpr int kGK = 32;       // K columns per stage
+constexpr int kGP = kGK + 1;  // LDS pitch (doubles) of the [row][k] stages
+
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) void chol_group_update_kernel(
     double* __restrict__ A, int d, int jb, int je) {
-  __shared__ double S0[kNB * kP], S1[kNB * kP];
+  __shared__ double S0[kNB * kGP], S1[kNB * kGP];
   const int t = threadIdx.x, lane = t & 63, w = t >> 6, wm = w & 1, wn = w >> 1;
   const int b = blockIdx.x;
   int i = (int)((sqrt(8.0 * (double)b + 1.0) - 1.0) * 0.5);
@@ -526,9 +531,51 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
   const int j = b - i * (i + 1) / 2;
   const int64_t dd = d;
   const int64_t R0 = (int64_t)(je + i) * kNB, C0 = (int64_t)(je + j) * kNB;
-  double va[16], vb[16];
-  load_tile_regs(va, A, dd, R0, (int64_t)jb * kNB, t);
-  load_tile_regs(vb, A, dd, C0, (int64_t)jb * kNB, t);
+  // staging: thread t covers row t / 4 of a [64][32] stage, columns 8 (t % 4) .. + 7
+  const int sr = t >> 2, sc = 8 * (t & 3);
+  double va[8], vb[8];
+  auto gload = [&](double (&v)[8], int64_t row0, int64_t k0) {
+    const int64_t row = row0 + sr;
+    const bool ok = row < dd;
+    const double* src = A + (ok ? row : 0) * dd + k0 + sc;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) v[e] = ok ? src[e] : 0.0;
+  };
+  const int64_t K0 = (int64_t)jb * kNB;
+  gload(va, R0, K0);
+  gload(vb, C0, K0);
+  f64x4 acc[2][2];
+  zero_acc(acc);
+  const int nst = (je - jb) * (kNB / kGK);
+  for (int st = 0; st < nst; ++st) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      S0[sr * kGP + sc + e] = va[e];
+      S1[sr * kGP + sc + e] = vb[e];
+    }
+    __syncthreads();
+    if (st + 1 < nst) {
+      gload(va, R0, K0 + (int64_t)(st + 1) * kGK);
+      gload(vb, C0, K0 + (int64_t)(st + 1) * kGK);
+    }
+#pragma unroll
+    for (int k4 = 0; k4 < kGK / 4; ++k4) {
+      const int k = 4 * k4 + (lane >> 4);
+      double a[2], bb[2];
+#pragma unroll
+      for (int f = 0; f < 2; ++f) {
+        a[f] = S0[(wm * 32 + f * 16 + (lane & 15)) * kGP + k];
+        bb[f] = S1[(wn * 32 + f * 16 + (lane & 15)) * kGP + k];
+      }
+#pragma unroll
+      for (int fm = 0; fm < 2; ++fm)
+#pragma unroll
+        for (int fn = 0; fn < 2; ++fn)
+          acc[fm][fn] = __builtin_amdgcn_mfma_f64_16x16x4f64(a[fm], bb[fn], acc[fm][fn], 0, 0, 0);
+    }
+    __syncthreads();
+  }
+  // C after the products (few registers live across the K loop)
   double c[16];
 #pragma unroll
   for (int fm = 0; fm < 2; ++fm)
@@ -537,21 +584,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         const int64_t row = R0 + nt_row(lane, wm, fm, q), col = C0 + nt_col(lane, wn, fn);
-        c[(fm * 2 + fn) * 4 + q] = (row < dd && col <= row) ? A[row * dd + col] : 0.0;
+        c[(fm * 2 + fn) * 4 + q] = A[std::min(row, dd - 1) * dd + std::min(col, dd - 1)];
       }
-  f64x4 acc[2][2];
-  zero_acc(acc);
-  for (int s = jb; s < je; ++s) {
-    store_tile_lds(S0, va, t);
-    store_tile_lds(S1, vb, t);
-    __syncthreads();
-    if (s + 1 < je) {
-      load_tile_regs(va, A, dd, R0, (int64_t)(s + 1) * kNB, t);
-      load_tile_regs(vb, A, dd, C0, (int64_t)(s + 1) * kNB, t);
-    }
-    mma_nt_f64(S0, S1, acc, lane, wm, wn);
-    __syncthreads();
-  }
 #pragma unroll
   for (int fm = 0; fm < 2; ++fm)
 #pragma unroll
