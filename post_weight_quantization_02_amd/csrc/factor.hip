@@ -620,13 +620,14 @@ struct TriArgs {
   int nblk, sb, npairs;
 };
 
-constexpr int kTPa = kNB + 1;   // LDS pitch of the [m][k] operand tile
-constexpr int kTPb = kNB + 32;  // LDS pitch of the [k][n] operand tile (the two k rows of one read use disjoint banks)
+constexpr int kTK = kNB / 2;    // K per stage (half a block: small LDS, many work-groups per CU)
+constexpr int kTPa = kTK + 1;   // LDS pitch of the [m][k] operand stage
+constexpr int kTPb = kNB + 32;  // LDS pitch of the [k][n] operand stage (the two k rows of one read use disjoint banks)
 
 template <int MODE, bool VEC>
 __global__ __launch_bounds__(kThreads) void tri_gemm_kernel(TriArgs a) {
   __shared__ float SA[kNB * kTPa];
-  __shared__ __attribute__((aligned(16))) float SB[kNB * kTPb];
+  __shared__ __attribute__((aligned(16))) float SB[kTK * kTPb];
   const int sb = a.sb, np = a.npairs;
   // longest K ranges first: mode 0 by block column, mode 1 by block row (descending)
   const int outer = blockIdx.x / (np * sb), rem = blockIdx.x % (np * sb);
@@ -641,75 +642,58 @@ __global__ __launch_bounds__(kThreads) void tri_gemm_kernel(TriArgs a) {
   float* Tp = a.Tw + (int64_t)p * ldt * ldt;
   const int kb0 = (MODE == 0) ? bj : 0, kb1 = (MODE == 0) ? sb : bi + 1;
   const int t = threadIdx.x, lane = t & 63, w = t >> 6, wm = w & 1, wn = w >> 1;
-  // staging: thread t covers tile row t / 4, 16 columns from (t % 4) * 16
-  const int sr = t >> 2, sc = (t & 3) * 16;
-  const int64_t arow = (int64_t)(C0 + bi) * kNB + sr;
-  float ra[16], rb[16];
-  auto gload = [&](int kb) {
-    if (MODE == 0) {
-      // A operand: L[C0+bi][A0+kb] rounded to fp32, from L^-1's buffer (its
-      // columns lie in the A range, < d)
-      const float* src = a.Linv + arow * d + (int64_t)(A0 + kb) * kNB + sc;
+  // K in stages of half a block: the A stage is [64 m][32 k] (thread t: row t / 4,
+  // 8 k from 8 (t % 4)), the B stage [32 k][64 n] (thread t: k-row t / 8, 8 n from 8 (t % 8))
+  const int ar = t >> 2, ac = 8 * (t & 3), br = t >> 3, bc = 8 * (t & 7);
+  const int64_t arow = (int64_t)(C0 + bi) * kNB + ar;
+  float ra[8], rb[8];
+  auto gload = [&](int st) {
+    const int kb = kb0 + (st >> 1), kh = (st & 1) * kTK;
+    // A: mode 0 L[C0+bi][A0+kb] rounded to fp32 (in L^-1's buffer; columns inside
+    // the A range, < d), mode 1 L^-1[C0+bi][C0+kb] (columns may pass d in the last block)
+    const int64_t acol = (int64_t)((MODE == 0 ? A0 : C0) + kb) * kNB + kh + ac;
+    const float* src = a.Linv + (arow < d ? arow : 0) * d + acol;
 #pragma unroll
-      for (int e = 0; e < 16; e += 4) {
-        if (VEC && arow < d) {
-          const f32x4 v = *(const f32x4*)(src + e);
-          ra[e] = v[0]; ra[e + 1] = v[1]; ra[e + 2] = v[2]; ra[e + 3] = v[3];
-        } else {
+    for (int e = 0; e < 8; e += 4) {
+      if (VEC && arow < d && (MODE == 0 || acol + e + 3 < d)) {
+        const f32x4 v = *(const f32x4*)(src + e);
+        ra[e] = v[0]; ra[e + 1] = v[1]; ra[e + 2] = v[2]; ra[e + 3] = v[3];
+      } else {
 #pragma unroll
-          for (int u = 0; u < 4; ++u) ra[e + u] = (arow < d) ? src[e + u] : 0.f;
-        }
+        for (int u = 0; u < 4; ++u) ra[e + u] = (arow < d && acol + e + u < d) ? src[e + u] : 0.f;
       }
-      // B operand: L^-1[A0+kb][A0+bj] (inside the A range)
-      const float* bsrc = a.Linv + ((int64_t)(A0 + kb) * kNB + sr) * d + (int64_t)(A0 + bj) * kNB + sc;
+    }
+    // B: mode 0 L^-1[A0+kb][A0+bj] (inside the A range), mode 1 T[kb][bj] of this pair
+    const float* bsrc = (MODE == 0)
+                            ? a.Linv + ((int64_t)(A0 + kb) * kNB + kh + br) * d + (int64_t)(A0 + bj) * kNB + bc
+                            : Tp + ((int64_t)kb * kNB + kh + br) * ldt + (int64_t)bj * kNB + bc;
 #pragma unroll
-      for (int e = 0; e < 16; e += 4) {
-        if (VEC) {
-          const f32x4 v = *(const f32x4*)(bsrc + e);
-          rb[e] = v[0]; rb[e + 1] = v[1]; rb[e + 2] = v[2]; rb[e + 3] = v[3];
-        } else {
-#pragma unroll
-          for (int u = 0; u < 4; ++u) rb[e + u] = bsrc[e + u];
-        }
-      }
-    } else {
-      // A operand: L^-1[C0+bi][C0+kb] (rows and columns may pass d in the last block)
-      const int64_t col = (int64_t)(C0 + kb) * kNB + sc;
-      const float* src = a.Linv + arow * d + col;
-#pragma unroll
-      for (int e = 0; e < 16; e += 4) {
-        if (VEC && arow < d && col + e + 3 < d) {
-          const f32x4 v = *(const f32x4*)(src + e);
-          ra[e] = v[0]; ra[e + 1] = v[1]; ra[e + 2] = v[2]; ra[e + 3] = v[3];
-        } else {
-#pragma unroll
-          for (int u = 0; u < 4; ++u) ra[e + u] = (arow < d && col + e + u < d) ? src[e + u] : 0.f;
-        }
-      }
-      // B operand: T[kb][bj] of this pair (always inside the scratch)
-      const float* bsrc = Tp + ((int64_t)kb * kNB + sr) * ldt + (int64_t)bj * kNB + sc;
-#pragma unroll
-      for (int e = 0; e < 16; e += 4) {
+    for (int e = 0; e < 8; e += 4) {
+      if (VEC) {
         const f32x4 v = *(const f32x4*)(bsrc + e);
         rb[e] = v[0]; rb[e + 1] = v[1]; rb[e + 2] = v[2]; rb[e + 3] = v[3];
+      } else {
+#pragma unroll
+        for (int u = 0; u < 4; ++u) rb[e + u] = bsrc[e + u];
       }
     }
   };
   f32x16 acc;
 #pragma unroll
   for (int r = 0; r < 16; ++r) acc[r] = 0.f;
-  gload(kb0);
-  for (int kb = kb0; kb < kb1; ++kb) {
+  const int nst = 2 * (kb1 - kb0);
+  gload(0);
+  for (int st = 0; st < nst; ++st) {
     __syncthreads();
 #pragma unroll
-    for (int e = 0; e < 16; ++e) SA[sr * kTPa + sc + e] = ra[e];
+    for (int e = 0; e < 8; ++e) SA[ar * kTPa + ac + e] = ra[e];
 #pragma unroll
-    for (int e = 0; e < 16; e += 4)
-      *(f32x4*)&SB[sr * kTPb + sc + e] = f32x4{rb[e], rb[e + 1], rb[e + 2], rb[e + 3]};
+    for (int e = 0; e < 8; e += 4)
+      *(f32x4*)&SB[br * kTPb + bc + e] = f32x4{rb[e], rb[e + 1], rb[e + 2], rb[e + 3]};
     __syncthreads();
-    if (kb + 1 < kb1) gload(kb + 1);
+    if (st + 1 < nst) gload(st + 1);
 #pragma unroll 8
-    for (int kk = 0; kk < kNB / 2; ++kk) {
+    for (int kk = 0; kk < kTK / 2; ++kk) {
       const int k = 2 * kk + (lane >> 5);
       const float av = SA[(wm * 32 + (lane & 31)) * kTPa + k];
       const float bv = SB[k * kTPb + wn * 32 + (lane & 31)];
