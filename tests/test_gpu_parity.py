@@ -82,6 +82,35 @@ def test_hessian_strided_rows_and_empty_chunk():
     assert relf(H.cpu().numpy(), O.hessian([x])) <= 1e-5
 
 
+def test_hessian_split_over_2gib():
+    """One row split whose X rows span more than 2 GiB (32768 rows x 33280 fp16
+    columns, 2.2 GB in one call): the pipelined loads address it in groups of
+    four stages.  X is drawn on the GPU; 256 sampled entries are checked against
+    fp64 dot products of the same columns (fp16 products are exact), and H is
+    exactly symmetric."""
+    n, d = 32768, 33280
+    assert n * d * 2 > 2 ** 31
+    g = torch.Generator(device="cuda")
+    g.manual_seed(77)
+    X = torch.randn(n, d, device="cuda", generator=g).half()
+    H = torch.zeros(d, d, device="cuda")
+    G.gptq_hessian_accumulate(H, X)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(77)
+    pi = np.concatenate([np.arange(0, d, d // 32)[:32], rng.integers(0, d, 224)])
+    pj = np.concatenate([np.arange(0, d, d // 32)[:32], rng.integers(0, d, 224)])
+    cols = np.unique(np.concatenate([pi, pj]))
+    pos = {c: k for k, c in enumerate(cols)}
+    xs = X[:, torch.from_numpy(cols).cuda()].cpu().numpy().astype(np.float64)
+    ref = 2.0 * np.einsum("ri,ri->i", xs[:, [pos[c] for c in pi]], xs[:, [pos[c] for c in pj]])
+    got = H[torch.from_numpy(pi).cuda(), torch.from_numpy(pj).cuda()].cpu().numpy().astype(np.float64)
+    assert np.linalg.norm(got - ref) / np.linalg.norm(ref) <= 1e-5
+    Hs = H[:: d // 64, :: d // 64]
+    assert torch.equal(Hs, Hs.t())
+    del X, H
+    torch.cuda.empty_cache()
+
+
 # ------------------------------------------------------------------ factor
 def _factor_case(Ho, percdamp=0.01):
     H32 = Ho.astype(np.float32)
