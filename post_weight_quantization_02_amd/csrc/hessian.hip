@@ -41,7 +41,7 @@ __device__ __forceinline__ void tile_of(int64_t t, int& ti, int& tj) {
 // so with the tile count a multiple of 8, XCD x takes tiles
 // ord[x * ntiles / 8 .. (x + 1) * ntiles / 8) of every split: the plan groups
 // tiles that share column blocks there, so each XCD's L2 serves few blocks.
-__device__ __forceinline__ void wg_map(int64_t ntiles, int64_t nsplit, const TileOrder& ord,
+__device__ __forceinline__ void wg_map(int64_t ntiles, const TileOrder& ord,
                                        int64_t& tile, int64_t& split) {
   const int64_t bid = blockIdx.x;
   if ((ntiles & 7) == 0) {
@@ -106,7 +106,7 @@ __global__ __launch_bounds__(kThreads) void syrk_f16_kernel(
   __shared__ __attribute__((aligned(16))) _Float16 L2[kStageHalfs];
   __shared__ __attribute__((aligned(16))) _Float16 L3[kStageHalfs];
   int64_t tile, split;
-  wg_map(ntiles, nsplit, ord, tile, split);
+  wg_map(ntiles, ord, tile, split);
   int ti, tj;
   tile_of(tile, ti, tj);
   const int I0 = ti * kBT16, J0 = tj * kBT16;
@@ -283,7 +283,7 @@ __global__ __launch_bounds__(kThreads) void syrk_f32_kernel(
     int64_t rps, float* __restrict__ part, const TileOrder ord) {
   __shared__ __attribute__((aligned(16))) float lds[2][kKS32 * kP32];
   int64_t tile, split;
-  wg_map(ntiles, nsplit, ord, tile, split);
+  wg_map(ntiles, ord, tile, split);
   int ti, tj;
   tile_of(tile, ti, tj);
   const bool diag = (ti == tj);
