@@ -1,7 +1,8 @@
 // Out-of-block correction of the lazy batch on fp32 matrix cores:
 //   W[:, i+B:] -= E U[i:i+B, i+B:]
 // (itwiki "GPTQ", three-changes table, change 2, and the last line of
-// Algorithm 1).  K = B <= 128, M = d_row, N = the columns after the block.
+// Algorithm 1).  K = B <= 128 (or two blocks' rows, up to 256, when the caller
+// pairs blocks), M = d_row, N = the columns after the block.
 //
 // E arrives transposed (Et [B x d_row], written that way by the panel kernel)
 // so that both operands stage with 16-byte loads along the M or N direction
@@ -140,13 +141,21 @@ __global__ __launch_bounds__(kThreads) void trail_kernel(float* __restrict__ C, 
 // ---------------------------------------------------------------------------
 // Aligned operands (the usual case): the same 128x128 tile, with Et and U rows
 // streamed by buffer loads straight into LDS (their row-major [k][m] / [k][n]
-// layout is already what the 32x32x2 MFMA reads), K in sub-phases of 32 rows
-// double-buffered, and the C tile read under the last sub-phase's MFMAs in a
-// coalesced per-wave layout.  Each wave finishes its own 64x64 quadrant through a
+// layout is already what the 32x32x2 MFMA reads), K in up to eight sub-phases of
+// 32 rows double-buffered, and the C tile read under the first sub-phase's
+// MFMAs in a coalesced per-wave layout.  Each wave finishes its own 64x64 quadrant through a
 // private LDS array: accumulators in, row-major out, C - acc, store.
 // Rows past K and columns past N read zeros or neighbouring data that only
 // reaches discarded outputs; the buffer extents keep every read inside Et and U.
 constexpr int kKS = 32;
+
+template <int I, int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (I < N) {
+    f(std::integral_constant<int, I>{});
+    static_for<I + 1, N>(f);
+  }
+}
 
 template <int NSUB>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) void trail_dma_kernel(float* __restrict__ C, int64_t ldc,
@@ -251,30 +260,24 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
     asm volatile("s_waitcnt vmcnt(16)\n\ts_barrier" ::: "memory");
   }
   compute(E0, U0, 0);
-  if constexpr (NSUB > 1) {
-    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-    if constexpr (NSUB > 2) {
-      dma(E0, U0, 2);
-      asm volatile("s_waitcnt vmcnt(24)\n\ts_barrier" ::: "memory");
+  // sub-phase S: once every wave is past S - 1 (whose buffer S + 1 reuses), the
+  // loads of S + 1 go out; the wait for S then lets exactly C (if S == 1) and
+  // S + 1 stay in flight
+  static_for<1, NSUB>([&](auto SS) {
+    constexpr int S = decltype(SS)::value;
+    if constexpr (S + 1 < NSUB) {
+      asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+      if constexpr ((S + 1) % 2 == 0) dma(E0, U0, S + 1);
+      else dma(E1, U1, S + 1);
+      if constexpr (S == 1) asm volatile("s_waitcnt vmcnt(24)\n\ts_barrier" ::: "memory");
+      else asm volatile("s_waitcnt vmcnt(8)\n\ts_barrier" ::: "memory");
     } else {
-      asm volatile("s_waitcnt vmcnt(16)\n\ts_barrier" ::: "memory");
+      if constexpr (S == 1) asm volatile("s_waitcnt vmcnt(16)\n\ts_barrier" ::: "memory");
+      else asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
     }
-    compute(E1, U1, 1);
-  }
-  if constexpr (NSUB > 2) {
-    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-    if constexpr (NSUB > 3) {
-      dma(E1, U1, 3);
-      asm volatile("s_waitcnt vmcnt(8)\n\ts_barrier" ::: "memory");
-    } else {
-      asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
-    }
-    compute(E0, U0, 2);
-  }
-  if constexpr (NSUB > 3) {
-    asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
-    compute(E1, U1, 3);
-  }
+    if constexpr (S % 2 == 0) compute(E0, U0, S);
+    else compute(E1, U1, S);
+  });
   // epilogue: every wave is done with the operand buffers after this barrier
   asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
   float* Q = (w == 0) ? E0 : (w == 1) ? U0 : (w == 2) ? E1 : U1;  // 64x64 private quadrant
@@ -314,7 +317,7 @@ hipError_t trail_update_launch(float* C, int64_t ldc, int M, int N, int K, const
   const bool vec = (lde % 4 == 0) && (ldu % 4 == 0) && (((uintptr_t)Et & 15) == 0) &&
                    (((uintptr_t)Ub & 15) == 0);
   // buffer loads need 32-bit byte extents and 16-byte rows
-  const bool dma = vec && (ldc % 4 == 0) && (((uintptr_t)C & 15) == 0) && K <= 4 * kKS && N >= 4 &&
+  const bool dma = vec && (ldc % 4 == 0) && (((uintptr_t)C & 15) == 0) && K <= 8 * kKS && N >= 4 &&
                    (int64_t)K * std::max(lde, ldu) * 4 < (int64_t(1) << 31);
   if (dma) {
     const dim3 g((unsigned)(tm * tn)), b(kThreads);
@@ -322,14 +325,24 @@ hipError_t trail_update_launch(float* C, int64_t ldc, int M, int N, int K, const
       case 1: hipLaunchKernelGGL(trail_dma_kernel<1>, g, b, 0, s, C, ldc, M, N, K, Et, lde, Ub, ldu, tm, tn); break;
       case 2: hipLaunchKernelGGL(trail_dma_kernel<2>, g, b, 0, s, C, ldc, M, N, K, Et, lde, Ub, ldu, tm, tn); break;
       case 3: hipLaunchKernelGGL(trail_dma_kernel<3>, g, b, 0, s, C, ldc, M, N, K, Et, lde, Ub, ldu, tm, tn); break;
-      default: hipLaunchKernelGGL(trail_dma_kernel<4>, g, b, 0, s, C, ldc, M, N, K, Et, lde, Ub, ldu, tm, tn); break;
+      case 4: hipLaunchKernelGGL(trail_dma_kernel<4>, g, b, 0, s, C, ldc, M, N, K, Et, lde, Ub, ldu, tm, tn); break;
+      case 5: hipLaunchKernelGGL(trail_dma_kernel<5>, g, b, 0, s, C, ldc, M, N, K, Et, lde, Ub, ldu, tm, tn); break;
+      case 6: hipLaunchKernelGGL(trail_dma_kernel<6>, g, b, 0, s, C, ldc, M, N, K, Et, lde, Ub, ldu, tm, tn); break;
+      case 7: hipLaunchKernelGGL(trail_dma_kernel<7>, g, b, 0, s, C, ldc, M, N, K, Et, lde, Ub, ldu, tm, tn); break;
+      default: hipLaunchKernelGGL(trail_dma_kernel<8>, g, b, 0, s, C, ldc, M, N, K, Et, lde, Ub, ldu, tm, tn); break;
     }
-  } else if (vec)
-    hipLaunchKernelGGL(trail_kernel<true>, dim3((unsigned)(tm * tn)), dim3(kThreads), 0, s, C, ldc,
-                       M, N, K, Et, lde, Ub, ldu, tm, tn);
-  else
-    hipLaunchKernelGGL(trail_kernel<false>, dim3((unsigned)(tm * tn)), dim3(kThreads), 0, s, C, ldc,
-                       M, N, K, Et, lde, Ub, ldu, tm, tn);
+  } else {
+    // the register-staged kernel takes K <= 2 kKP per launch
+    for (int k0 = 0; k0 < K; k0 += 2 * kKP) {
+      const int kc = std::min(2 * kKP, K - k0);
+      if (vec)
+        hipLaunchKernelGGL(trail_kernel<true>, dim3((unsigned)(tm * tn)), dim3(kThreads), 0, s, C, ldc,
+                           M, N, kc, Et + (int64_t)k0 * lde, lde, Ub + (int64_t)k0 * ldu, ldu, tm, tn);
+      else
+        hipLaunchKernelGGL(trail_kernel<false>, dim3((unsigned)(tm * tn)), dim3(kThreads), 0, s, C, ldc,
+                           M, N, kc, Et + (int64_t)k0 * lde, lde, Ub + (int64_t)k0 * ldu, ldu, tm, tn);
+    }
+  }
   return hipGetLastError();
 }
 

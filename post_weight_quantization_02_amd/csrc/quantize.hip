@@ -425,11 +425,12 @@ QuantPlan quant_plan(int64_t d_row, int64_t d_col, int64_t B) {
   p.B = B;
   p.nblk = cdiv(d_col, B);
   p.panel_wgs = cdiv(d_row, 16);
+  p.big = d_row * d_col >= (int64_t(1) << 28);
   size_t off = 0;
   p.off_w = off;
   off = align_up(off + (size_t)d_row * d_col * sizeof(float), 256);
-  p.off_e = off;
-  off = align_up(off + (size_t)d_row * B * sizeof(float), 256);
+  p.off_e = off;  // E of one block, or of two consecutive blocks when they are paired
+  off = align_up(off + (size_t)d_row * B * (p.big ? 2 : 1) * sizeof(float), 256);
   p.off_part = off;
   off = align_up(off + (size_t)p.panel_wgs * sizeof(double), 256);
   p.off_err = off;
@@ -464,8 +465,18 @@ hipError_t quant_launch(const QuantPlan& p, const void* W0, int w_dtype, int64_t
     hipLaunchKernelGGL(prep_kernel<float>, dim3((unsigned)d_row), dim3(kThreads), 0, s,
                        (const float*)W0, ldw, d_col, perm, W, group == 0, maxq, scales, zeros);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  for (int64_t i1 = 0; i1 < d_col; i1 += B) {
+  // On large layers the out-of-block update runs once per pair of blocks: after
+  // an even block only the next block's columns are brought up to date (a thin
+  // update), and after the odd block the rest of W takes both blocks' errors in
+  // one product of depth 2B, W[:, i2:] -= [E_even; E_odd] U[i0:i2, i2:], which
+  // reads and writes W there half as often.  The updates are linear in E, so the
+  // result is the same up to rounding order.  A grid of groups wider than B is
+  // fitted to fully updated columns, so such groups must start on even blocks.
+  const bool pair = p.big && (group == 0 || group <= B || group % (2 * B) == 0);
+  for (int64_t i1 = 0, blk = 0; i1 < d_col; i1 += B, ++blk) {
     const int width = (int)std::min<int64_t>(B, d_col - i1);
+    const bool odd = pair && (blk & 1);
+    float* Eb = odd ? E + B * d_row : E;
     if (group > B && i1 % group == 0) {
       const int64_t gw = std::min<int64_t>(group, d_col - i1);
       hipLaunchKernelGGL(group_grid_kernel, dim3((unsigned)cdiv(d_row, 4)), dim3(kThreads), 0, s, W,
@@ -478,19 +489,26 @@ hipError_t quant_launch(const QuantPlan& p, const void* W0, int w_dtype, int64_t
     const int ng = (int)ngroups;
     switch (B) {
       case 16: e = launch_panel<1>(gin, full, pg, s, W, (int)d_row, (int)d_col, (int)i1, width, U,
-                                   maxq, gwide, ng, cpos, scales, zeros, E, part_e); break;
+                                   maxq, gwide, ng, cpos, scales, zeros, Eb, part_e); break;
       case 32: e = launch_panel<2>(gin, full, pg, s, W, (int)d_row, (int)d_col, (int)i1, width, U,
-                                   maxq, gwide, ng, cpos, scales, zeros, E, part_e); break;
+                                   maxq, gwide, ng, cpos, scales, zeros, Eb, part_e); break;
       case 64: e = launch_panel<4>(gin, full, pg, s, W, (int)d_row, (int)d_col, (int)i1, width, U,
-                                   maxq, gwide, ng, cpos, scales, zeros, E, part_e); break;
+                                   maxq, gwide, ng, cpos, scales, zeros, Eb, part_e); break;
       default: e = launch_panel<8>(gin, full, pg, s, W, (int)d_row, (int)d_col, (int)i1, width, U,
-                                   maxq, gwide, ng, cpos, scales, zeros, E, part_e); break;
+                                   maxq, gwide, ng, cpos, scales, zeros, Eb, part_e); break;
     }
     if (e != hipSuccess) return e;
     const int64_t i2 = i1 + width;
     if (i2 < d_col) {
-      e = trail_update_launch(W + i2, d_col, (int)d_row, (int)(d_col - i2), width, E, d_row,
-                              U + i1 * d_col + i2, d_col, s);
+      if (!pair)
+        e = trail_update_launch(W + i2, d_col, (int)d_row, (int)(d_col - i2), width, E, d_row,
+                                U + i1 * d_col + i2, d_col, s);
+      else if (!odd)
+        e = trail_update_launch(W + i2, d_col, (int)d_row, (int)std::min<int64_t>(B, d_col - i2), width, E,
+                                d_row, U + i1 * d_col + i2, d_col, s);
+      else
+        e = trail_update_launch(W + i2, d_col, (int)d_row, (int)(d_col - i2), (int)B + width, E, d_row,
+                                U + (i1 - B) * d_col + i2, d_col, s);
       if (e != hipSuccess) return e;
     }
   }
