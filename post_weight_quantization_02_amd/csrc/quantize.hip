@@ -130,12 +130,15 @@ __global__ __launch_bounds__(kThreads) void group_grid_kernel(const float* __res
 // parameters group_grid_kernel wrote at the block start).  FULL: width == B.
 // Both are compile-time so the fully unrolled column loop carries the group
 // code only at the group starts.
+// Eprev: NULL, or (blocks paired in the out-of-block correction) the previous
+// block's E, whose share W[:, i1:i1+width] -= E_prev U[i1-B:i1, i1:i1+width] the
+// work-group applies to its own rows before the column loop.
 template <int CPL, int GIN, bool FULL>
 __global__ __launch_bounds__(kThreads) void panel_kernel(
     float* __restrict__ W, int d_row, int d_col, int i1, int width,
     const float* __restrict__ U, int maxq, int gwide, int ngroups,
     uint8_t* __restrict__ codes, float* __restrict__ scales, int32_t* __restrict__ zeros,
-    float* __restrict__ E, double* __restrict__ part_e) {
+    float* __restrict__ E, double* __restrict__ part_e, const float* __restrict__ Eprev) {
   constexpr int B = 16 * CPL;
   static_assert(GIN == 0 || (GIN % 16 == 0 && B % GIN == 0), "group inside block");
   __shared__ __attribute__((aligned(16))) float Us[B * B];
@@ -212,6 +215,73 @@ __global__ __launch_bounds__(kThreads) void panel_kernel(
     w[r] = (FULL || col < width) ? W[rowc * d_col + i1 + col] : 0.f;
     cr[r] = 0.f;
     er[r] = 0.f;
+  }
+  if (Eprev) {
+    // E_prev is stored [k][row].  U rows are 16-byte aligned here (the caller
+    // pairs blocks only then).
+    if constexpr (FULL && CPL == 8) {
+      // Each wave computes its 4 rows x 128 columns with lane l owning columns
+      // 2l, 2l + 1 of all four, so a U row is read once per wave (coalesced).
+      // The wave's E_prev words (128 k x 4 rows) are first copied to its own LDS
+      // strip and read back four at a time, the same address in every lane; the
+      // sums then reach the column-loop layout through the same strip.  U comes
+      // 16 rows of k at a time, the next chunk's loads issued before this
+      // chunk's FMAs.  Words written by one lane and read by another are
+      // ordered by a work-group barrier with LDS-only fences (the diagonal
+      // block's direct-to-LDS loads may stay in flight across it).
+      __shared__ __attribute__((aligned(16))) float dl[16 * B];
+      const int wv = __builtin_amdgcn_readfirstlane(t >> 6);
+      float* el = dl + wv * 4 * B;
+      const int erl = std::min((int)blockIdx.x * 16 + wv * 4 + (lane & 3), d_row - 1);
+      const float* up = U + (size_t)(i1 - B) * ldu + i1 + 2 * lane;
+      constexpr int KC = 16;
+      static_assert(B % KC == 0, "chunks of k");
+      float2 ua[2][KC];
+      float acc[4][2];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) acc[i][0] = acc[i][1] = 0.f;
+      auto ld = [&](int buf, int k0) {
+#pragma unroll
+        for (int k = 0; k < KC; ++k) ua[buf][k] = *(const float2*)(up + (size_t)(k0 + k) * ldu);
+      };
+      ld(0, 0);  // in flight while E_prev is staged
+#pragma unroll
+      for (int j = 0; j < B / 16; ++j) el[j * 64 + lane] = Eprev[(size_t)(j * 16 + (lane >> 2)) * d_row + erl];
+      auto lds_sync = [] {
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+        __builtin_amdgcn_s_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+      };
+      lds_sync();
+      static_for<0, B / KC>([&](auto cc) {
+        constexpr int c = decltype(cc)::value;
+        if constexpr ((c + 1) * KC < B) ld((c + 1) & 1, (c + 1) * KC);
+#pragma unroll
+        for (int k = 0; k < KC; ++k) {
+          const f32x4 e = *(const f32x4*)&el[4 * (c * KC + k)];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            acc[i][0] = fmaf(e[i], ua[c & 1][k].x, acc[i][0]);
+            acc[i][1] = fmaf(e[i], ua[c & 1][k].y, acc[i][1]);
+          }
+        }
+      });
+      lds_sync();  // every lane's E words read
+#pragma unroll
+      for (int i = 0; i < 4; ++i) *(float2*)&el[i * B + 2 * lane] = make_float2(acc[i][0], acc[i][1]);
+      lds_sync();
+#pragma unroll
+      for (int r = 0; r < CPL; ++r) w[r] -= el[(lane >> 4) * B + p * CPL + r];
+    } else {
+      const float* ep = Eprev + rowc;
+      const float* up = U + (size_t)(i1 - B) * ldu + i1 + p * CPL;
+      for (int k = 0; k < B; ++k) {
+        const float e = ep[(size_t)k * d_row];
+#pragma unroll
+        for (int r = 0; r < CPL; ++r)
+          if (FULL || p * CPL + r < width) w[r] = fmaf(-e, up[(size_t)k * ldu + r], w[r]);
+      }
+    }
   }
   float s = 1.f, z = 0.f;
   if (GIN == 0) {
@@ -319,13 +389,14 @@ __global__ __launch_bounds__(kThreads) void panel_kernel(
 template <int CPL, int GIN>
 hipError_t launch_panel_g(bool full, dim3 grid, hipStream_t s, float* W, int d_row, int d_col,
                           int i1, int width, const float* U, int maxq, int gwide, int ngroups,
-                          uint8_t* codes, float* scales, int32_t* zeros, float* E, double* part_e) {
+                          uint8_t* codes, float* scales, int32_t* zeros, float* E, double* part_e,
+                          const float* Eprev) {
   if (full)
     hipLaunchKernelGGL((panel_kernel<CPL, GIN, true>), grid, dim3(kThreads), 0, s, W, d_row, d_col,
-                       i1, width, U, maxq, gwide, ngroups, codes, scales, zeros, E, part_e);
+                       i1, width, U, maxq, gwide, ngroups, codes, scales, zeros, E, part_e, Eprev);
   else
     hipLaunchKernelGGL((panel_kernel<CPL, GIN, false>), grid, dim3(kThreads), 0, s, W, d_row, d_col,
-                       i1, width, U, maxq, gwide, ngroups, codes, scales, zeros, E, part_e);
+                       i1, width, U, maxq, gwide, ngroups, codes, scales, zeros, E, part_e, Eprev);
   return hipGetLastError();
 }
 
@@ -333,12 +404,12 @@ template <int CPL>
 hipError_t launch_panel(int gin, bool full, dim3 grid, hipStream_t s, float* W, int d_row,
                         int d_col, int i1, int width, const float* U, int maxq, int gwide,
                         int ngroups, uint8_t* codes, float* scales, int32_t* zeros, float* E,
-                        double* part_e) {
+                        double* part_e, const float* Eprev) {
 #define GPTQ_PANEL_CASE(G)                                                                  \
   case G:                                                                                  \
     if constexpr (G <= 16 * CPL)                                                           \
       return launch_panel_g<CPL, G>(full, grid, s, W, d_row, d_col, i1, width, U, maxq,   \
-                                    gwide, ngroups, codes, scales, zeros, E, part_e);      \
+                                    gwide, ngroups, codes, scales, zeros, E, part_e, Eprev);\
     return hipErrorInvalidValue;
   switch (gin) {
     GPTQ_PANEL_CASE(0)
@@ -425,12 +496,15 @@ QuantPlan quant_plan(int64_t d_row, int64_t d_col, int64_t B) {
   p.B = B;
   p.nblk = cdiv(d_col, B);
   p.panel_wgs = cdiv(d_row, 16);
-  p.big = d_row * d_col >= (int64_t(1) << 28);
+  // the panel has at most one work-group per CU up to 4096 rows: bound by its
+  // column chain's latency, it absorbs the even block's share nearly for free;
+  // past that, pairing pays only on large layers, through a thin launch
+  p.pair = p.panel_wgs <= 256 ? 1 : (d_row * d_col >= (int64_t(1) << 28) ? 2 : 0);
   size_t off = 0;
   p.off_w = off;
   off = align_up(off + (size_t)d_row * d_col * sizeof(float), 256);
   p.off_e = off;  // E of one block, or of two consecutive blocks when they are paired
-  off = align_up(off + (size_t)d_row * B * (p.big ? 2 : 1) * sizeof(float), 256);
+  off = align_up(off + (size_t)d_row * B * (p.pair ? 2 : 1) * sizeof(float), 256);
   p.off_part = off;
   off = align_up(off + (size_t)p.panel_wgs * sizeof(double), 256);
   p.off_err = off;
@@ -465,18 +539,23 @@ hipError_t quant_launch(const QuantPlan& p, const void* W0, int w_dtype, int64_t
     hipLaunchKernelGGL(prep_kernel<float>, dim3((unsigned)d_row), dim3(kThreads), 0, s,
                        (const float*)W0, ldw, d_col, perm, W, group == 0, maxq, scales, zeros);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  // On large layers the out-of-block update runs once per pair of blocks: after
-  // an even block only the next block's columns are brought up to date (a thin
-  // update), and after the odd block the rest of W takes both blocks' errors in
-  // one product of depth 2B, W[:, i2:] -= [E_even; E_odd] U[i0:i2, i2:], which
-  // reads and writes W there half as often.  The updates are linear in E, so the
-  // result is the same up to rounding order.  A grid of groups wider than B is
-  // fitted to fully updated columns, so such groups must start on even blocks.
-  const bool pair = p.big && (group == 0 || group <= B || group % (2 * B) == 0);
+  // Paired blocks: the out-of-block update runs once per pair of blocks.  The
+  // odd block's columns first take the even block's share (in the odd block's
+  // panel, or by a thin launch after the even block), and after the odd block
+  // the rest of W takes both blocks' errors in one product of depth 2B,
+  // W[:, i2:] -= [E_even; E_odd] U[i0:i2, i2:], which reads and writes W there
+  // half as often.  The updates are linear in E, so the result is the same up
+  // to rounding order.  A grid of groups wider than B is fitted to fully
+  // updated columns, so such groups must start on even blocks; the panel's
+  // vector reads of U need 16-byte rows.
+  const bool pair = p.pair && B % 64 == 0 && d_col % 4 == 0 && ((uintptr_t)U & 15) == 0 &&
+                    (group == 0 || group <= B || group % (2 * B) == 0);
+  const bool fused = pair && p.pair == 1;
   for (int64_t i1 = 0, blk = 0; i1 < d_col; i1 += B, ++blk) {
     const int width = (int)std::min<int64_t>(B, d_col - i1);
     const bool odd = pair && (blk & 1);
     float* Eb = odd ? E + B * d_row : E;
+    const float* Ep = (odd && fused) ? E : nullptr;
     if (group > B && i1 % group == 0) {
       const int64_t gw = std::min<int64_t>(group, d_col - i1);
       hipLaunchKernelGGL(group_grid_kernel, dim3((unsigned)cdiv(d_row, 4)), dim3(kThreads), 0, s, W,
@@ -489,13 +568,13 @@ hipError_t quant_launch(const QuantPlan& p, const void* W0, int w_dtype, int64_t
     const int ng = (int)ngroups;
     switch (B) {
       case 16: e = launch_panel<1>(gin, full, pg, s, W, (int)d_row, (int)d_col, (int)i1, width, U,
-                                   maxq, gwide, ng, cpos, scales, zeros, Eb, part_e); break;
+                                   maxq, gwide, ng, cpos, scales, zeros, Eb, part_e, Ep); break;
       case 32: e = launch_panel<2>(gin, full, pg, s, W, (int)d_row, (int)d_col, (int)i1, width, U,
-                                   maxq, gwide, ng, cpos, scales, zeros, Eb, part_e); break;
+                                   maxq, gwide, ng, cpos, scales, zeros, Eb, part_e, Ep); break;
       case 64: e = launch_panel<4>(gin, full, pg, s, W, (int)d_row, (int)d_col, (int)i1, width, U,
-                                   maxq, gwide, ng, cpos, scales, zeros, Eb, part_e); break;
+                                   maxq, gwide, ng, cpos, scales, zeros, Eb, part_e, Ep); break;
       default: e = launch_panel<8>(gin, full, pg, s, W, (int)d_row, (int)d_col, (int)i1, width, U,
-                                   maxq, gwide, ng, cpos, scales, zeros, Eb, part_e); break;
+                                   maxq, gwide, ng, cpos, scales, zeros, Eb, part_e, Ep); break;
     }
     if (e != hipSuccess) return e;
     const int64_t i2 = i1 + width;
@@ -503,10 +582,10 @@ hipError_t quant_launch(const QuantPlan& p, const void* W0, int w_dtype, int64_t
       if (!pair)
         e = trail_update_launch(W + i2, d_col, (int)d_row, (int)(d_col - i2), width, E, d_row,
                                 U + i1 * d_col + i2, d_col, s);
-      else if (!odd)
+      else if (!odd && !fused)
         e = trail_update_launch(W + i2, d_col, (int)d_row, (int)std::min<int64_t>(B, d_col - i2), width, E,
                                 d_row, U + i1 * d_col + i2, d_col, s);
-      else
+      else if (odd)
         e = trail_update_launch(W + i2, d_col, (int)d_row, (int)(d_col - i2), (int)B + width, E, d_row,
                                 U + (i1 - B) * d_col + i2, d_col, s);
       if (e != hipSuccess) return e;

@@ -1,7 +1,9 @@
-"""GPU parity of the column loop on a layer large enough (d_row * d_col >= 2^28)
-that the out-of-block update runs once per pair of blocks (itwiki "GPTQ",
-three-changes table, change 2: the deferred update is linear in the batch
-errors, so two batches' corrections can be applied as one product).
+"""GPU parity of the column loop where the out-of-block update runs once per pair
+of blocks (itwiki "GPTQ", three-changes table, change 2: the deferred update is
+linear in the batch errors, so two batches' corrections can be applied as one
+product).  A layer of d_row * d_col >= 2^28 takes the even block's share on the
+odd block's columns in a thin launch; a layer of at most 4096 rows takes it in
+the odd block's panel.
 
 Layer 16384 x 16424: 129 blocks of 128, so the pairs end on an unpaired block
 whose last 40 columns are a ragged tail.  H from 16384 layer-normed rows, 1% damping.
@@ -13,11 +15,12 @@ Each case is checked as the full-size tests are:
          whole W_hat (an fp64 product on the device), within 1%.
 Groups of 384 are wider than a block and do not start on every other block, so
 that case runs the loop one block at a time; the others run it in pairs.  Rows
-are independent in the loop, so the first 8192 rows quantized alone (a layer
-below the pairing size, updated one block at a time) must give nearly the same
-codes: >= 99%, not the tie bar, since the two differ in fp32 rounding order and
-one flipped code changes the error fed to the rest of its row (the forced
-replay above is the parity bar).
+are independent in the loop, so the first 4096 rows quantized alone (the panel
+takes the even block's share) get the same forced replay on 8 sampled rows,
+and the first 8192 rows quantized alone (one block at a time) must give nearly
+the same codes as the whole layer: >= 99%, not the tie bar, since the two differ
+in fp32 rounding order and one flipped code changes the error fed to the rest
+of its row (the forced replays are the parity bar).
 """
 import numpy as np
 import pytest
@@ -74,6 +77,16 @@ def _err_direct(H, W, w_hat):
 
 
 ROWS = np.concatenate([[0, D_ROW - 1], np.random.default_rng(63).choice(np.arange(1, D_ROW - 1), 14, replace=False)])
+ROWS4 = np.concatenate([[0, 4095], np.random.default_rng(64).choice(np.arange(1, 4095), 6, replace=False)])
+
+
+def _replay(W, Uh, bits, group, got):
+    codes, scales, zeros = got
+    r = O.gptq_quantize(W.astype(np.float64), Uh, bits, group, B, replay_codes=codes, replay_zeros=zeros)
+    assert r.adopted_codes <= 0.001 * r.codes.size, (r.adopted_codes, r.codes.size)
+    np.testing.assert_array_equal(r.codes, codes)
+    np.testing.assert_allclose(scales, r.scales, rtol=1e-5, atol=0)
+    np.testing.assert_array_equal(zeros, r.zeros)
 
 
 @pytest.mark.parametrize("bits,group", [(4, 0), (3, 256), (4, 64), (4, 384)],
@@ -83,16 +96,13 @@ def test_paired_loop(layer, bits, group):
     codes, scales, zeros, err = G.gptq_quantize_layer(layer["Wd"], layer["U"], layer["lam"], bits, group, B)
     half = G.gptq_quantize_layer(layer["Wd"][:D_ROW // 2], layer["U"], layer["lam"], bits, group, B)[0]
     same = float((half == codes[:D_ROW // 2]).double().mean().item())
+    q4 = G.gptq_quantize_layer(layer["Wd"][:4096], layer["U"], layer["lam"], bits, group, B)[:3]
     torch.cuda.synchronize()
     cg, sg, zg = codes.cpu().numpy(), scales.cpu().numpy(), zeros.cpu().numpy()
     Uh = layer["U"].cpu().numpy().astype(np.float64)
-    r = O.gptq_quantize(layer["W"][ROWS].astype(np.float64), Uh, bits, group, B,
-                        replay_codes=cg[ROWS], replay_zeros=zg[ROWS])
+    _replay(layer["W"][ROWS], Uh, bits, group, (cg[ROWS], sg[ROWS], zg[ROWS]))
+    _replay(layer["W"][ROWS4], Uh, bits, group, tuple(x.cpu().numpy()[ROWS4] for x in q4))
     del Uh
-    assert r.adopted_codes <= 0.001 * r.codes.size, (r.adopted_codes, r.codes.size)
-    np.testing.assert_array_equal(r.codes, cg[ROWS])
-    np.testing.assert_allclose(sg[ROWS], r.scales, rtol=1e-5, atol=0)
-    np.testing.assert_array_equal(zg[ROWS], r.zeros)
     assert same >= 0.99, same
     g_idx = np.arange(D_COL) // (group or D_COL)
     e_direct = _err_direct(layer["H"], layer["W"], _w_hat(cg, sg, zg, g_idx))
