@@ -428,11 +428,42 @@ __global__ __launch_bounds__(kThreads) void err_delta_kernel(
     const T* __restrict__ W0, int64_t ldw, int64_t d_row, int64_t d_col,
     const uint8_t* __restrict__ cpos, const float* __restrict__ scales,
     const int32_t* __restrict__ zeros, int g, int64_t ngroups, const int32_t* __restrict__ perm,
-    uint8_t* __restrict__ codes, double* __restrict__ part_d) {
+    uint8_t* __restrict__ codes, double* __restrict__ part_d, int vec8) {
   __shared__ double red[kThreads];
   const int t = threadIdx.x;
   double acc = 0.0;
-  for (int64_t row = blockIdx.x; row < d_row; row += gridDim.x) {
+  // natural order with 8-column runs inside one group and 16-byte (fp16) or
+  // 32-byte (fp32) aligned rows: 8 columns per thread and step
+  for (int64_t row = blockIdx.x; vec8 && row < d_row; row += gridDim.x) {
+    for (int64_t c = 8 * (int64_t)t; c < d_col; c += 8 * kThreads) {
+      const int gi = (int)(c / g);
+      const float s = scales[row * ngroups + gi];
+      const float z = (float)zeros[row * ngroups + gi];
+      const uint64_t cv = *(const uint64_t*)(cpos + row * d_col + c);
+      float wv[8];
+      if constexpr (sizeof(T) == 2) {
+        typedef _Float16 h8 __attribute__((ext_vector_type(8)));
+        const h8 x = *(const h8*)(W0 + row * ldw + c);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) wv[e] = (float)x[e];
+      } else {
+        const f32x4 x0 = *(const f32x4*)(W0 + row * ldw + c);
+        const f32x4 x1 = *(const f32x4*)(W0 + row * ldw + c + 4);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          wv[e] = x0[e];
+          wv[e + 4] = x1[e];
+        }
+      }
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float wh = s * ((float)((cv >> (8 * e)) & 255u) - z);
+        const double dlt = (double)wv[e] - (double)wh;
+        acc += dlt * dlt;
+      }
+    }
+  }
+  for (int64_t row = blockIdx.x; !vec8 && row < d_row; row += gridDim.x) {
     for (int64_t c = t; c < d_col; c += kThreads) {
       // c: position in the quantization order (groups are runs of positions)
       const int gi = (int)c / g;
@@ -593,12 +624,14 @@ hipError_t quant_launch(const QuantPlan& p, const void* W0, int w_dtype, int64_t
   }
   const unsigned nerr = (unsigned)std::min<int64_t>(kErrWGs, d_row);
   const int64_t gsz = group ? group : d_col;
+  const int vec8 = !perm && gsz % 8 == 0 && d_col % 8 == 0 && ldw % 8 == 0 && ((uintptr_t)cpos & 7) == 0 &&
+                   ((uintptr_t)W0 & (w_dtype == 1 ? 15 : 31)) == 0;
   if (w_dtype == 1)
     hipLaunchKernelGGL(err_delta_kernel<_Float16>, dim3(nerr), dim3(kThreads), 0, s,
-                       (const _Float16*)W0, ldw, d_row, d_col, cpos, scales, zeros, gsz, ngroups, perm, codes, part_d);
+                       (const _Float16*)W0, ldw, d_row, d_col, cpos, scales, zeros, gsz, ngroups, perm, codes, part_d, vec8);
   else
     hipLaunchKernelGGL(err_delta_kernel<float>, dim3(nerr), dim3(kThreads), 0, s, (const float*)W0, ldw,
-                       d_row, d_col, cpos, scales, zeros, gsz, ngroups, perm, codes, part_d);
+                       d_row, d_col, cpos, scales, zeros, gsz, ngroups, perm, codes, part_d, vec8);
   hipLaunchKernelGGL(err_final_kernel, dim3(1), dim3(kThreads), 0, s, part_e, p.panel_wgs, part_d,
                      (int64_t)nerr, lambda, out_err);
   if (g_idx)
