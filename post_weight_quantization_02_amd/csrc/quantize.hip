@@ -66,12 +66,36 @@ __global__ __launch_bounds__(kThreads) void prep_kernel(const T* __restrict__ W0
                                                         float* __restrict__ W,
                                                         int per_row, int maxq,
                                                         float* __restrict__ scales,
-                                                        int32_t* __restrict__ zeros) {
+                                                        int32_t* __restrict__ zeros, int vec8) {
   __shared__ float smn[kThreads], smx[kThreads];
   const int64_t row = blockIdx.x;
   const int t = threadIdx.x;
   float mn = INFINITY, mx = -INFINITY;
-  for (int64_t c = t; c < d_col; c += kThreads) {
+  // natural order with 16-byte (fp16) or 32-byte (fp32) aligned rows: 8 columns
+  // per thread and step
+  for (int64_t c = 8 * (int64_t)t; vec8 && c < d_col; c += 8 * kThreads) {
+    f32x4 v0, v1;
+    if constexpr (sizeof(T) == 2) {
+      typedef _Float16 h8 __attribute__((ext_vector_type(8)));
+      const h8 x = *(const h8*)(W0 + row * ldw + c);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        v0[e] = (float)x[e];
+        v1[e] = (float)x[e + 4];
+      }
+    } else {
+      v0 = *(const f32x4*)(W0 + row * ldw + c);
+      v1 = *(const f32x4*)(W0 + row * ldw + c + 4);
+    }
+    *(f32x4*)(W + row * d_col + c) = v0;
+    *(f32x4*)(W + row * d_col + c + 4) = v1;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      mn = fminf(mn, fminf(v0[e], v1[e]));
+      mx = fmaxf(mx, fmaxf(v0[e], v1[e]));
+    }
+  }
+  for (int64_t c = t; !vec8 && c < d_col; c += kThreads) {
     const float v = (float)W0[row * ldw + perm_col(perm, c, d_col)];
     W[row * d_col + c] = v;
     mn = fminf(mn, v);
@@ -563,12 +587,14 @@ hipError_t quant_launch(const QuantPlan& p, const void* W0, int w_dtype, int64_t
   const int64_t ngroups = group ? cdiv(d_col, group) : 1;
   hipError_t e;
   hipLaunchKernelGGL(zero_f64_kernel, dim3(64), dim3(kThreads), 0, s, part_e, p.panel_wgs);
+  const int pvec8 = !perm && d_col % 8 == 0 && ldw % 8 == 0 && ((uintptr_t)W0 & (w_dtype == 1 ? 15 : 31)) == 0 &&
+                    ((uintptr_t)W & 31) == 0;
   if (w_dtype == 1)
     hipLaunchKernelGGL(prep_kernel<_Float16>, dim3((unsigned)d_row), dim3(kThreads), 0, s,
-                       (const _Float16*)W0, ldw, d_col, perm, W, group == 0, maxq, scales, zeros);
+                       (const _Float16*)W0, ldw, d_col, perm, W, group == 0, maxq, scales, zeros, pvec8);
   else
     hipLaunchKernelGGL(prep_kernel<float>, dim3((unsigned)d_row), dim3(kThreads), 0, s,
-                       (const float*)W0, ldw, d_col, perm, W, group == 0, maxq, scales, zeros);
+                       (const float*)W0, ldw, d_col, perm, W, group == 0, maxq, scales, zeros, pvec8);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   // Paired blocks: the out-of-block update runs once per pair of blocks.  The
   // odd block's columns first take the even block's share (in the odd block's
