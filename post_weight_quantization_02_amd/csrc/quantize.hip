@@ -553,8 +553,8 @@ QuantPlan quant_plan(int64_t d_row, int64_t d_col, int64_t B) {
   p.panel_wgs = cdiv(d_row, 16);
   // the panel has at most one work-group per CU up to 4096 rows: bound by its
   // column chain's latency, it absorbs the even block's share nearly for free;
-  // past that, pairing pays only on large layers, through a thin launch
-  p.pair = p.panel_wgs <= 256 ? 1 : (d_row * d_col >= (int64_t(1) << 28) ? 2 : 0);
+  // past that the share takes a thin launch
+  p.pair = p.panel_wgs <= 256 ? 1 : 2;
   size_t off = 0;
   p.off_w = off;
   off = align_up(off + (size_t)d_row * d_col * sizeof(float), 256);

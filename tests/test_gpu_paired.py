@@ -1,7 +1,7 @@
 """GPU parity of the column loop where the out-of-block update runs once per pair
 of blocks (itwiki "GPTQ", three-changes table, change 2: the deferred update is
 linear in the batch errors, so two batches' corrections can be applied as one
-product).  A layer of d_row * d_col >= 2^28 takes the even block's share on the
+product).  A layer of more than 4096 rows takes the even block's share on the
 odd block's columns in a thin launch; a layer of at most 4096 rows takes it in
 the odd block's panel.
 
@@ -17,10 +17,11 @@ Groups of 384 are wider than a block and do not start on every other block, so
 that case runs the loop one block at a time; the others run it in pairs.  Rows
 are independent in the loop, so the first 4096 rows quantized alone (the panel
 takes the even block's share) get the same forced replay on 8 sampled rows,
-and the first 8192 rows quantized alone (one block at a time) must give nearly
-the same codes as the whole layer: >= 99%, not the tie bar, since the two differ
-in fp32 rounding order and one flipped code changes the error fed to the rest
-of its row (the forced replays are the parity bar).
+and the first 8192 rows quantized with blocks of 32 (never paired; the lazy
+batch gives the same result for any block size up to rounding) must give
+nearly the same codes as the whole layer: >= 99%, not the tie bar, since the
+two differ in fp32 rounding order and one flipped code changes the error fed
+to the rest of its row (the forced replays are the parity bar).
 """
 import numpy as np
 import pytest
@@ -94,7 +95,7 @@ def _replay(W, Uh, bits, group, got):
 def test_paired_loop(layer, bits, group):
     print(f"\npaired loop bits {bits} group {group}", flush=True)
     codes, scales, zeros, err = G.gptq_quantize_layer(layer["Wd"], layer["U"], layer["lam"], bits, group, B)
-    half = G.gptq_quantize_layer(layer["Wd"][:D_ROW // 2], layer["U"], layer["lam"], bits, group, B)[0]
+    half = G.gptq_quantize_layer(layer["Wd"][:D_ROW // 2], layer["U"], layer["lam"], bits, group, 32)[0]
     same = float((half == codes[:D_ROW // 2]).double().mean().item())
     q4 = G.gptq_quantize_layer(layer["Wd"][:4096], layer["U"], layer["lam"], bits, group, B)[:3]
     torch.cuda.synchronize()
