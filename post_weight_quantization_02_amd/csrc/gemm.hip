@@ -1,8 +1,8 @@
 // Out-of-block correction of the lazy batch on fp32 matrix cores:
 //   W[:, i+B:] -= E U[i:i+B, i+B:]
 // (itwiki "GPTQ", three-changes table, change 2, and the last line of
-// Algorithm 1).  K = B <= 128 (or two blocks' rows, up to 256, when the caller
-// pairs blocks), M = d_row, N = the columns after the block.
+// Algorithm 1).  K = B <= 128 (or the rows of up to four blocks, up to 512, when
+// the caller groups blocks), M = d_row, N = the columns after the block.
 //
 // E arrives transposed (Et [B x d_row], written that way by the panel kernel)
 // so that both operands stage with 16-byte loads along the M or N direction
@@ -141,8 +141,8 @@ __global__ __launch_bounds__(kThreads) void trail_kernel(float* __restrict__ C, 
 // ---------------------------------------------------------------------------
 // Aligned operands (the usual case): the same 128x128 tile, with Et and U rows
 // streamed by buffer loads straight into LDS (their row-major [k][m] / [k][n]
-// layout is already what the 32x32x2 MFMA reads), K in up to eight sub-phases of
-// 32 rows double-buffered, and the C tile read under the first sub-phase's
+// layout is already what the 32x32x2 MFMA reads), K in up to sixteen sub-phases
+// of 32 rows double-buffered, and the C tile read under the first sub-phase's
 // MFMAs in a coalesced per-wave layout.  Each wave finishes its own 64x64 quadrant through a
 // private LDS array: accumulators in, row-major out, C - acc, store.
 // Rows past K and columns past N read zeros or neighbouring data that only
@@ -310,6 +310,16 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
 
 }  // namespace
 
+// the instantiation with nsub sub-phases of 32 rows (1 .. 16)
+template <int NS>
+void launch_dma(int nsub, dim3 g, dim3 b, hipStream_t s, float* C, int64_t ldc, int M, int N, int K,
+                const float* Et, int64_t lde, const float* Ub, int64_t ldu, int64_t tm, int64_t tn) {
+  if constexpr (NS < 16) {
+    if (nsub != NS) return launch_dma<NS + 1>(nsub, g, b, s, C, ldc, M, N, K, Et, lde, Ub, ldu, tm, tn);
+  }
+  hipLaunchKernelGGL(trail_dma_kernel<NS>, g, b, 0, s, C, ldc, M, N, K, Et, lde, Ub, ldu, tm, tn);
+}
+
 hipError_t trail_update_launch(float* C, int64_t ldc, int M, int N, int K, const float* Et,
                                int64_t lde, const float* Ub, int64_t ldu, hipStream_t s) {
   if (M <= 0 || N <= 0 || K <= 0) return hipSuccess;
@@ -317,20 +327,11 @@ hipError_t trail_update_launch(float* C, int64_t ldc, int M, int N, int K, const
   const bool vec = (lde % 4 == 0) && (ldu % 4 == 0) && (((uintptr_t)Et & 15) == 0) &&
                    (((uintptr_t)Ub & 15) == 0);
   // buffer loads need 32-bit byte extents and 16-byte rows
-  const bool dma = vec && (ldc % 4 == 0) && (((uintptr_t)C & 15) == 0) && K <= 8 * kKS && N >= 4 &&
+  const bool dma = vec && (ldc % 4 == 0) && (((uintptr_t)C & 15) == 0) && K <= 16 * kKS && N >= 4 &&
                    (int64_t)K * std::max(lde, ldu) * 4 < (int64_t(1) << 31);
   if (dma) {
     const dim3 g((unsigned)(tm * tn)), b(kThreads);
-    switch ((K + kKS - 1) / kKS) {
-      case 1: hipLaunchKernelGGL(trail_dma_kernel<1>, g, b, 0, s, C, ldc, M, N, K, Et, lde, Ub, ldu, tm, tn); break;
-      case 2: hipLaunchKernelGGL(trail_dma_kernel<2>, g, b, 0, s, C, ldc, M, N, K, Et, lde, Ub, ldu, tm, tn); break;
-      case 3: hipLaunchKernelGGL(trail_dma_kernel<3>, g, b, 0, s, C, ldc, M, N, K, Et, lde, Ub, ldu, tm, tn); break;
-      case 4: hipLaunchKernelGGL(trail_dma_kernel<4>, g, b, 0, s, C, ldc, M, N, K, Et, lde, Ub, ldu, tm, tn); break;
-      case 5: hipLaunchKernelGGL(trail_dma_kernel<5>, g, b, 0, s, C, ldc, M, N, K, Et, lde, Ub, ldu, tm, tn); break;
-      case 6: hipLaunchKernelGGL(trail_dma_kernel<6>, g, b, 0, s, C, ldc, M, N, K, Et, lde, Ub, ldu, tm, tn); break;
-      case 7: hipLaunchKernelGGL(trail_dma_kernel<7>, g, b, 0, s, C, ldc, M, N, K, Et, lde, Ub, ldu, tm, tn); break;
-      default: hipLaunchKernelGGL(trail_dma_kernel<8>, g, b, 0, s, C, ldc, M, N, K, Et, lde, Ub, ldu, tm, tn); break;
-    }
+    launch_dma<1>((K + kKS - 1) / kKS, g, b, s, C, ldc, M, N, K, Et, lde, Ub, ldu, tm, tn);
   } else {
     // the register-staged kernel takes K <= 2 kKP per launch
     for (int k0 = 0; k0 < K; k0 += 2 * kKP) {

@@ -83,8 +83,9 @@ hipError_t quantize2d_launch(const Plan2D& p, const void* X, int x_dtype, int64_
 struct QuantPlan {
   int64_t d_row, d_col, B, nblk;
   int64_t panel_wgs;      // work-groups of the panel kernel
-  int pair;               // blocks paired in the out-of-block update: the odd block's
-                          // panel takes the even block's share (1) or a thin launch does (2)
+  int pair;               // blocks grouped in the out-of-block update: pairs whose odd
+                          // block's panel takes the even block's share (1), or groups of
+                          // up to four blocks with thin launches inside the group (2)
   size_t off_w, off_e, off_part, off_err, off_cpos, ws_bytes;
 };
 QuantPlan quant_plan(int64_t d_row, int64_t d_col, int64_t B);

@@ -553,13 +553,13 @@ QuantPlan quant_plan(int64_t d_row, int64_t d_col, int64_t B) {
   p.panel_wgs = cdiv(d_row, 16);
   // the panel has at most one work-group per CU up to 4096 rows: bound by its
   // column chain's latency, it absorbs the even block's share nearly for free;
-  // past that the share takes a thin launch
+  // past that the shares inside a group take thin launches
   p.pair = p.panel_wgs <= 256 ? 1 : 2;
   size_t off = 0;
   p.off_w = off;
   off = align_up(off + (size_t)d_row * d_col * sizeof(float), 256);
-  p.off_e = off;  // E of one block, or of two consecutive blocks when they are paired
-  off = align_up(off + (size_t)d_row * B * (p.pair ? 2 : 1) * sizeof(float), 256);
+  p.off_e = off;  // E of the blocks of one group (up to four), consecutive
+  off = align_up(off + (size_t)d_row * B * (p.pair == 1 ? 2 : 4) * sizeof(float), 256);
   p.off_part = off;
   off = align_up(off + (size_t)p.panel_wgs * sizeof(double), 256);
   p.off_err = off;
@@ -596,23 +596,28 @@ hipError_t quant_launch(const QuantPlan& p, const void* W0, int w_dtype, int64_t
     hipLaunchKernelGGL(prep_kernel<float>, dim3((unsigned)d_row), dim3(kThreads), 0, s,
                        (const float*)W0, ldw, d_col, perm, W, group == 0, maxq, scales, zeros, pvec8);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  // Paired blocks: the out-of-block update runs once per pair of blocks.  The
-  // odd block's columns first take the even block's share (in the odd block's
-  // panel, or by a thin launch after the even block), and after the odd block
-  // the rest of W takes both blocks' errors in one product of depth 2B,
-  // W[:, i2:] -= [E_even; E_odd] U[i0:i2, i2:], which reads and writes W there
-  // half as often.  The updates are linear in E, so the result is the same up
-  // to rounding order.  A grid of groups wider than B is fitted to fully
-  // updated columns, so such groups must start on even blocks; the panel's
-  // vector reads of U need 16-byte rows.
-  const bool pair = p.pair && B % 64 == 0 && d_col % 4 == 0 && ((uintptr_t)U & 15) == 0 &&
-                    (group == 0 || group <= B || group % (2 * B) == 0);
-  const bool fused = pair && p.pair == 1;
+  // Grouped blocks: the out-of-block update of the columns after a group of nb
+  // consecutive blocks runs once, after the group's last block, as one product of
+  // depth nb B: W[:, i2:] -= [E_0; ..; E_nb-1] U[i0:i2, i2:], which reads and
+  // writes W there 1/nb as often.  Inside the group each block's columns first
+  // take the shares of the group's earlier blocks: for pairs in the odd block's
+  // panel (nb = 2, at most 4096 rows) or by a thin launch after the even block;
+  // for quads by thin launches after block 0 (E_0 on block 1), block 1
+  // ([E_0; E_1] on blocks 2 and 3) and block 2 (E_2 on block 3).  The updates
+  // are linear in E, so the result is the same up to rounding order.  A grid of
+  // groups wider than B is fitted to fully updated columns, so such groups may
+  // start only where the columns after them are up to date; the panel's vector
+  // reads of U need 16-byte rows.
+  const bool base_ok = p.pair && B % 64 == 0 && d_col % 4 == 0 && ((uintptr_t)U & 15) == 0;
+  const bool fused = base_ok && p.pair == 1 && (group == 0 || group <= B || group % (2 * B) == 0);
+  const bool quad = base_ok && p.pair == 2 && (group == 0 || group <= 2 * B || group % (4 * B) == 0);
+  const bool pair2 = base_ok && p.pair == 2 && !quad && (group <= B || group % (2 * B) == 0);
+  const int nb = quad ? 4 : (fused || pair2) ? 2 : 1;
   for (int64_t i1 = 0, blk = 0; i1 < d_col; i1 += B, ++blk) {
     const int width = (int)std::min<int64_t>(B, d_col - i1);
-    const bool odd = pair && (blk & 1);
-    float* Eb = odd ? E + B * d_row : E;
-    const float* Ep = (odd && fused) ? E : nullptr;
+    const int r = (int)(blk % nb);  // position in the group
+    float* Eb = E + (int64_t)r * B * d_row;
+    const float* Ep = (fused && r == 1) ? E : nullptr;
     if (group > B && i1 % group == 0) {
       const int64_t gw = std::min<int64_t>(group, d_col - i1);
       hipLaunchKernelGGL(group_grid_kernel, dim3((unsigned)cdiv(d_row, 4)), dim3(kThreads), 0, s, W,
@@ -636,16 +641,27 @@ hipError_t quant_launch(const QuantPlan& p, const void* W0, int w_dtype, int64_t
     if (e != hipSuccess) return e;
     const int64_t i2 = i1 + width;
     if (i2 < d_col) {
-      if (!pair)
-        e = trail_update_launch(W + i2, d_col, (int)d_row, (int)(d_col - i2), width, E, d_row,
-                                U + i1 * d_col + i2, d_col, s);
-      else if (!odd && !fused)
-        e = trail_update_launch(W + i2, d_col, (int)d_row, (int)std::min<int64_t>(B, d_col - i2), width, E,
-                                d_row, U + i1 * d_col + i2, d_col, s);
-      else if (odd)
-        e = trail_update_launch(W + i2, d_col, (int)d_row, (int)(d_col - i2), (int)B + width, E, d_row,
-                                U + (i1 - B) * d_col + i2, d_col, s);
-      if (e != hipSuccess) return e;
+      int64_t ncols = 0, krows = 0, urow = 0;
+      const float* Et = E;
+      if (r == nb - 1) {  // the group's last block: every block of the group on the rest
+        ncols = d_col - i2;
+        krows = (int64_t)r * B + width;
+        urow = i1 - (int64_t)r * B;
+      } else if (!fused && r == 1) {  // quads: [E_0; E_1] on blocks 2 and 3
+        ncols = std::min<int64_t>(2 * B, d_col - i2);
+        krows = B + width;
+        urow = i1 - B;
+      } else if (!fused) {  // E_r on the next block
+        ncols = std::min<int64_t>(B, d_col - i2);
+        krows = width;
+        urow = i1;
+        Et = Eb;
+      }
+      if (ncols > 0) {
+        e = trail_update_launch(W + i2, d_col, (int)d_row, (int)ncols, (int)krows, Et, d_row,
+                                U + urow * d_col + i2, d_col, s);
+        if (e != hipSuccess) return e;
+      }
     }
   }
   const unsigned nerr = (unsigned)std::min<int64_t>(kErrWGs, d_row);

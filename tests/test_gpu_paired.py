@@ -1,12 +1,13 @@
-"""GPU parity of the column loop where the out-of-block update runs once per pair
+"""GPU parity of the column loop where the out-of-block update runs once per group
 of blocks (itwiki "GPTQ", three-changes table, change 2: the deferred update is
-linear in the batch errors, so two batches' corrections can be applied as one
-product).  A layer of more than 4096 rows takes the even block's share on the
-odd block's columns in a thin launch; a layer of at most 4096 rows takes it in
-the odd block's panel.
+linear in the batch errors, so several batches' corrections can be applied as
+one product).  A layer of more than 4096 rows groups four blocks (two when wide
+groups of quantization parameters only start on every other block) and brings
+each block of a group up to date with thin launches; a layer of at most 4096
+rows pairs blocks, the odd block's panel taking the even block's share.
 
-Layer 16384 x 16424: 129 blocks of 128, so the pairs end on an unpaired block
-whose last 40 columns are a ragged tail.  H from 16384 layer-normed rows, 1% damping.
+Layer 16384 x 16424: 129 blocks of 128, so the groups end on a lone block whose
+last 40 columns are a ragged tail.  H from 16384 layer-normed rows, 1% damping.
 Each case is checked as the full-size tests are:
   codes  forced replay of 16 sampled rows (the first and last among them)
          through the oracle's loop with the GPU's U: >= 99.9% identical,
@@ -14,10 +15,11 @@ Each case is checked as the full-size tests are:
   error  the reported ||X dW^T||^2 against 0.5 sum_r dW_r H dW_r^T of the GPU's
          whole W_hat (an fp64 product on the device), within 1%.
 Groups of 384 are wider than a block and do not start on every other block, so
-that case runs the loop one block at a time; the others run it in pairs.  Rows
+that case runs the loop one block at a time; groups of 768 start on every other
+block but not every fourth, so that case pairs blocks; the others group four.  Rows
 are independent in the loop, so the first 4096 rows quantized alone (the panel
 takes the even block's share) get the same forced replay on 8 sampled rows,
-and the first 8192 rows quantized with blocks of 32 (never paired; the lazy
+and the first 8192 rows quantized with blocks of 32 (never grouped; the lazy
 batch gives the same result for any block size up to rounding) must give
 nearly the same codes as the whole layer: >= 99%, not the tie bar, since the
 two differ in fp32 rounding order and one flipped code changes the error fed
@@ -90,8 +92,9 @@ def _replay(W, Uh, bits, group, got):
     np.testing.assert_array_equal(zeros, r.zeros)
 
 
-@pytest.mark.parametrize("bits,group", [(4, 0), (3, 256), (4, 64), (4, 384)],
-                         ids=["4bit_row", "3bit_g256_paired", "4bit_g64_in_block", "4bit_g384_unpaired"])
+@pytest.mark.parametrize("bits,group", [(4, 0), (3, 256), (4, 64), (4, 384), (4, 768)],
+                         ids=["4bit_row", "3bit_g256_grouped", "4bit_g64_in_block", "4bit_g384_unpaired",
+                              "4bit_g768_pairs"])
 def test_paired_loop(layer, bits, group):
     print(f"\npaired loop bits {bits} group {group}", flush=True)
     codes, scales, zeros, err = G.gptq_quantize_layer(layer["Wd"], layer["U"], layer["lam"], bits, group, B)
