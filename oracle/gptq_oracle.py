@@ -177,110 +177,131 @@ def gptq_quantize(W0: np.ndarray, U: np.ndarray, bits: int, group_size: int = 0,
                   replay_tol: float = 1e-3) -> GPTQResult:
     """Quantize W0 [d_row x d_col] given U (upper, U^T U = H_lambda^-1).
 
-    Steps (wiki Algorithm 1 / sketch), natural column order:
-      per-row grid from W0 (or per-group grid at each group start from the
-      then-current weights);
-      for each block [i1, i2): copy W1 = W[:, i1:i2]; for each column j:
-        c = quant(W1[:, j]); q = dequant(c); e = (W1[:, j] - q) / U[j, j];
-        W1[:, j:] -= e * U[j, j:]; E[:, j] = e;
-      then W[:, i2:] -= E @ U[i1:i2, i2:].
+    Derivation (wiki "OBQ에서 GPTQ로": the compensation equation, and its
+    three-changes table; "알고리즘": Algorithm 1).  In the fixed natural order,
+    the OBS step for column j has remaining set F = {j, j+1, ..} and moves the
+    remaining weights by -(w_j - q_j) / [H_F^-1]_jj * H_F^-1[:, j], with H_F
+    the rows and columns F of H_lambda.  For an upper U with U^T U =
+    H_lambda^-1 the trailing block satisfies U[F, F]^T U[F, F] = H_F^-1, so
+    H_F^-1[:, j] = U[j, j] U[j, F]^T and [H_F^-1]_jj = U[j, j]^2: the step
+    reads w_k -= e_j U[j, k] for k > j with the scaled error
+    e_j = (w_j - q_j) / U[j, j].  Unrolled, the
+    value of column j at its turn is
+
+        w_j = W0_j - sum_{i < j} e_i U[i, j]           (column recursion)
+
+    The lazy batch (change 2) splits this sum at block boundaries: the terms
+    of finished blocks are applied to every later column at once as the
+    product E_blk U[blk, later], and the terms of the current block are
+    gathered when column j is reached (a left-looking evaluation: columns of
+    the block are never updated before their turn).  Both orders give the
+    same value up to fp64 rounding.
+
+    Grid: per row from W0, or per group at the group's first column from the
+    then-current values of the group's columns (wiki "실무 변형": parameters
+    from the latest updated weights); block and group sizes divide one another,
+    so those columns are the ones inside the block (brought up to date the
+    same way) or, for a group wider than the block, fully updated columns at a
+    block start.
 
     Forced replay (``replay_codes`` given): wherever the supplied code differs
     from this oracle's, the difference is accepted only if it is 1 and
     w / scale lies within ``replay_tol`` of the half-integer between the two
     candidates; the supplied code is then adopted and the loop continues.  The
-    same applies to group zero-points with -min / scale.  Any other difference
+    same applies to zero-points with -min / scale.  Any other difference
     raises ReplayMismatch.
     """
     check_alignment(block_size, group_size)
-    W = np.array(W0, dtype=np.float64, copy=True)
     U = np.asarray(U, dtype=np.float64)
-    d_row, d_col = W.shape
+    Wr = np.array(W0, dtype=np.float64, copy=True)   # W0 minus finished blocks' terms
+    d_row, d_col = Wr.shape
     maxq = (1 << bits) - 1
     g = group_size if group_size else d_col
     n_groups = (d_col + g - 1) // g
-    codes = np.zeros((d_row, d_col), dtype=np.float64)
+    codes = np.zeros((d_row, d_col))
     scales = np.zeros((d_row, n_groups))
     zeros = np.zeros((d_row, n_groups))
-    err_sq = 0.0
-    adopted_c = adopted_z = 0
-    max_dist = 0.0
+    stats = {"codes": 0, "zeros": 0, "dist": 0.0}
+
+    def set_grid(gi, cols):
+        s, z = grid_params(cols, bits)
+        z = _replay_zero(z, -np.min(cols, axis=1) / s, replay_zeros, gi, replay_tol, stats)
+        scales[:, gi], zeros[:, gi] = s, z
 
     if not group_size:
-        s, z = grid_params(W, bits)
-        z = _replay_zero(z, -np.min(W, axis=1) / s, replay_zeros, 0, replay_tol)
-        adopted_z += int(np.sum(z[1]))
-        scales[:, 0], zeros[:, 0] = s, z[0]
+        set_grid(0, Wr)
 
-    for i1 in range(0, d_col, block_size):
-        i2 = min(i1 + block_size, d_col)
-        W1 = W[:, i1:i2].copy()
-        Ub = U[i1:i2, i1:i2]
-        E = np.zeros((d_row, i2 - i1))
-        for j in range(i2 - i1):
-            col = i1 + j
-            gi = col // g
-            if group_size and col % g == 0:
-                # group parameters from the latest weights: columns inside the
-                # block come from W1, the rest (only when g > B, where they are
-                # fully updated at a block start) from W
-                end = min(col + g, d_col)
-                cur = np.concatenate([W1[:, j:], W[:, i2:end]], axis=1)[:, :end - col]
-                s, z = grid_params(cur, bits)
-                z = _replay_zero(z, -np.min(cur, axis=1) / s, replay_zeros, gi, replay_tol)
-                adopted_z += int(np.sum(z[1]))
-                scales[:, gi], zeros[:, gi] = s, z[0]
-            s = scales[:, gi]
-            z = zeros[:, gi]
-            w = W1[:, j]
-            c = quant_codes(w, s, z, maxq)
-            if replay_codes is not None:
-                rc = np.asarray(replay_codes[:, col], dtype=np.float64)
-                diff = rc != c
-                if np.any(diff):
-                    v = w[diff] / s[diff]
-                    lo = np.minimum(rc[diff], c[diff]) - z[diff]
-                    dist = np.abs(v - (lo + 0.5))
-                    bad = (np.abs(rc[diff] - c[diff]) != 1) | (dist > replay_tol)
-                    if np.any(bad):
-                        rows = np.nonzero(diff)[0][bad]
-                        raise ReplayMismatch(
-                            f"code mismatch at column {col}, rows {rows[:8].tolist()}: "
-                            f"given {rc[rows[:8]].tolist()} oracle {c[rows[:8]].tolist()} "
-                            f"w/scale {(w[rows[:8]] / s[rows[:8]]).tolist()}")
-                    max_dist = max(max_dist, float(np.max(dist)))
-                    adopted_c += int(np.sum(diff))
-                    c = rc
-            q = dequant(c, s, z)
-            e = (w - q) / Ub[j, j]
-            W1[:, j:] -= np.outer(e, Ub[j, j:])
-            E[:, j] = e
-            codes[:, col] = c
-        err_sq += float(np.sum(E * E))
-        W[:, i2:] -= E @ U[i1:i2, i2:]
+    err_sq = 0.0
+    for b0 in range(0, d_col, block_size):
+        b1 = min(b0 + block_size, d_col)
+        Eb = np.zeros((d_row, b1 - b0))          # scaled errors of this block so far
 
-    w_hat = np.empty_like(codes)
-    for gi in range(n_groups):
-        sl = slice(gi * g, min((gi + 1) * g, d_col))
-        w_hat[:, sl] = dequant(codes[:, sl], scales[:, gi:gi + 1], zeros[:, gi:gi + 1])
+        def current(k0, k1, done):
+            # columns [k0, k1) after the block's first `done` columns' OBS steps
+            return Wr[:, k0:k1] - Eb[:, :done] @ U[b0:b0 + done, k0:k1]
+
+        for j in range(b0, b1):
+            done = j - b0
+            gi = j // g
+            if group_size and j % g == 0:
+                set_grid(gi, current(j, min(j + g, d_col), done))
+            s, z = scales[:, gi], zeros[:, gi]
+            w = current(j, j + 1, done)[:, 0]
+            c = _replay_code(quant_codes(w, s, z, maxq), w / s, z, replay_codes, j,
+                             replay_tol, stats)
+            codes[:, j] = c
+            Eb[:, done] = (w - dequant(c, s, z)) / U[j, j]
+        err_sq += float(np.sum(Eb * Eb))
+        Wr[:, b1:] -= Eb @ U[b0:b1, b1:]
+
+    gidx = np.arange(d_col) // g
+    w_hat = dequant(codes, scales[:, gidx], zeros[:, gidx])
     return GPTQResult(codes.astype(np.uint8), scales, zeros.astype(np.int64), w_hat, err_sq,
-                      adopted_c, adopted_z, max_dist)
+                      stats["codes"], stats["zeros"], stats["dist"])
 
 
-def _replay_zero(z, v, replay_zeros, gi, tol):
-    """Return (zeros, adopted-mask); adopt a supplied zero-point within tol of a tie."""
+def _replay_code(c, v, z, replay_codes, col, tol, stats):
+    """Adopt a supplied code that differs by one where v = w / scale lies within
+    tol of the half-integer tie between the two candidates (c - zero being the
+    rounded value of v); raise ReplayMismatch for any other difference."""
+    if replay_codes is None:
+        return c
+    rc = np.asarray(replay_codes[:, col], dtype=np.float64)
+    diff = rc != c
+    if not np.any(diff):
+        return c
+    tie = np.minimum(rc[diff], c[diff]) - z[diff] + 0.5
+    dist = np.abs(v[diff] - tie)
+    bad = (np.abs(rc[diff] - c[diff]) != 1) | (dist > tol)
+    if np.any(bad):
+        rows = np.nonzero(diff)[0][bad][:8]
+        raise ReplayMismatch(
+            f"code mismatch at column {col}, rows {rows.tolist()}: given {rc[rows].tolist()} "
+            f"oracle {c[rows].tolist()} w/scale {v[rows].tolist()}")
+    stats["dist"] = max(stats["dist"], float(np.max(dist)))
+    stats["codes"] += int(np.sum(diff))
+    return np.where(diff, rc, c)
+
+
+def _replay_zero(z, v, replay_zeros, gi, tol, stats):
+    """Adopt a supplied zero-point that differs by one where v = -min / scale lies
+    within tol of the half-integer tie between the two candidates; raise
+    ReplayMismatch for any other difference."""
     if replay_zeros is None:
-        return z, np.zeros(z.shape, dtype=bool)
+        return z
     rz = np.asarray(replay_zeros[:, gi], dtype=np.float64)
     diff = rz != z
-    if np.any(diff):
-        lo = np.minimum(rz[diff], z[diff])
-        bad = (np.abs(rz[diff] - z[diff]) != 1) | (np.abs(v[diff] - (lo + 0.5)) > tol)
-        if np.any(bad):
-            rows = np.nonzero(diff)[0][bad]
-            raise ReplayMismatch(f"zero-point mismatch in group {gi}, rows {rows[:8].tolist()}")
-        z = np.where(diff, rz, z)
-    return z, diff
+    if not np.any(diff):
+        return z
+    tie = np.minimum(rz[diff], z[diff]) + 0.5
+    bad = (np.abs(rz[diff] - z[diff]) != 1) | (np.abs(v[diff] - tie) > tol)
+    if np.any(bad):
+        rows = np.nonzero(diff)[0][bad][:8]
+        raise ReplayMismatch(f"zero-point mismatch in group {gi}, rows {rows.tolist()}: "
+                             f"given {rz[rows].tolist()} oracle {z[rows].tolist()} "
+                             f"-min/scale {v[rows].tolist()}")
+    stats["zeros"] += int(np.sum(diff))
+    return np.where(diff, rz, z)
 
 
 # ---------------------------------------------------------------------------

@@ -89,3 +89,68 @@ def test_replay_adopts_only_ties():
     bad[2, 3] = (int(bad[2, 3]) + 3) % 16
     with pytest.raises(O.ReplayMismatch):
         Q2.gptq2d(X, U_Q, U_P, 4, replay_codes=bad)
+
+
+def tie_case_2d():
+    """Entry (2, 3) of a 5 x 6 matrix is placed so that the value it is rounded
+    from, divided by the scale, is (k + 0.5) + 2e-4; entry (4, 1) sits at k' + 0.3.
+    Identity side factors (no feedback).  Returns (X, U_Q, U_P, bits, codes with
+    (2, 3) moved to the other side of its tie, codes with (4, 1) moved to its
+    other neighbour)."""
+    rng = np.random.default_rng(47)
+    X = 0.02 * rng.standard_normal((5, 6))
+    s, z = Q2.tensor_grid(X, 4)
+    X[2, 3] = s * (1 + 0.5 + 2e-4)
+    X[4, 1] = s * (-2 + 0.3)
+    assert Q2.tensor_grid(X, 4) == (s, z)
+    base = Q2.gptq2d(X, np.eye(5), np.eye(6), 4)
+    assert base.codes[2, 3] == 2 + z and base.codes[4, 1] == -2 + z
+    adopt, reject = base.codes.copy(), base.codes.copy()
+    adopt[2, 3] = 1 + z
+    reject[4, 1] = -1 + z
+    return X, np.eye(5), np.eye(6), 4, adopt, reject
+
+
+def test_replay_adopts_the_last_decision_at_a_tie_with_real_factors():
+    """With real side factors the last entry (m-1, n-1) is rounded from
+    X - (U_Q^T M) with M built from every other entry; X[m-1, n-1] is moved so that
+    this value sits 2e-4 past a tie (no other entry reads it, and the grid is
+    unchanged).  Replay adopts the other side of the tie, and the reported error
+    is still the metric of the adopted result."""
+    X, A, B, U_Q, U_P = _case(18, 6, 7)
+    s, z = Q2.tensor_grid(X, 4)
+    r = Q2.gptq2d(X, U_Q, U_P, 4)
+    M = np.zeros_like(X)
+    for i in range(6):
+        for j in range(7):
+            if (i, j) != (5, 6):
+                M[i, j:] += r.E[i, j] * U_P[j, j:]
+    corr = U_Q[:, 5] @ M[:, 6]
+    others = np.delete(X.ravel(), -1)
+    assert others.min() == X.min() and others.max() == X.max()   # X[5, 6] is no extreme
+    k = int(np.floor((0.5 * (X.min() + X.max()) - corr) / s))
+    X[5, 6] = corr + s * (k + 0.5 + 2e-4)
+    assert 0 < k + z < 14
+    assert Q2.tensor_grid(X, 4) == (s, z)
+    base = Q2.gptq2d(X, U_Q, U_P, 4)
+    np.testing.assert_array_equal(np.delete(base.codes.ravel(), -1), np.delete(r.codes.ravel(), -1))
+    assert base.codes[5, 6] == k + 1 + z
+    flipped = base.codes.copy()
+    flipped[5, 6] = k + z
+    rr = Q2.gptq2d(X, U_Q, U_P, 4, replay_codes=flipped)
+    assert rr.adopted_codes == 1 and rr.codes[5, 6] == k + z
+    assert Q2.two_sided_metric(X, rr.w_hat, A, B) == pytest.approx(rr.err, rel=1e-9)
+    assert rr.err != pytest.approx(base.err, rel=1e-12)
+    with pytest.raises(O.ReplayMismatch):
+        Q2.gptq2d(X, U_Q, U_P, 4, replay_codes=flipped, replay_tol=1e-4)
+
+
+def test_replay_2d_adopts_only_at_the_tie():
+    X, U_Q, U_P, bits, adopt, reject = tie_case_2d()
+    r = Q2.gptq2d(X, U_Q, U_P, bits, replay_codes=adopt)
+    assert r.adopted_codes == 1
+    np.testing.assert_array_equal(r.codes, adopt)
+    with pytest.raises(O.ReplayMismatch):
+        Q2.gptq2d(X, U_Q, U_P, bits, replay_codes=reject)
+    with pytest.raises(O.ReplayMismatch):
+        Q2.gptq2d(X, U_Q, U_P, bits, replay_codes=adopt, replay_tol=1e-4)

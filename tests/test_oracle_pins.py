@@ -305,3 +305,108 @@ def test_replay_accepts_only_near_boundary_flip():
         O.gptq_quantize(w, U, 4, 0, 8, replay_codes=flipped, replay_tol=dist * 0.5)
     rr = O.gptq_quantize(w, U, 4, 0, 8, replay_codes=flipped, replay_tol=dist * 2 + 1e-12,)
     assert rr.adopted_codes >= 1 and rr.codes[i, j] == other
+
+
+# ---------------------------------------------------------------- forced replay at ties
+# Wiki "실무 변형" (group parameters from the latest weights) makes the zero-point an
+# integer decision like the codes: round(-min / scale).  Forced replay may adopt a
+# supplied value only where that decision sits at a tie.  These cases construct a
+# tie exactly, so the adoption branch runs, and a non-tie neighbour, which must be
+# rejected.
+
+def zero_tie_case():
+    """Per-row grid (4-bit) where row 3 has -min/scale = 7.5 + 2e-4: the oracle's
+    zero-point is 8, the other side of the tie is 7 (adoptable), 9 is a neighbour
+    of 8 whose tie 8.5 is ~1 away (not adoptable).  Returns
+    (W0, U, bits, group, block, row, zeros_adopt, zeros_reject)."""
+    w, x = wl.tiny_case(41, 6, 12, 64, 0.8)
+    H_lam, _ = O.damp(O.hessian([x]), 0.01)
+    U = O.inv_hessian_factor(H_lam)
+    r, span, v = 3, 0.06, 7.5 + 2e-4
+    a = span * v / 15.0
+    w[r] = np.linspace(-a + 1e-3, span - a - 1e-3, w.shape[1])
+    w[r, 4], w[r, 9] = -a, span - a          # min and max of the row
+    base = O.gptq_quantize(w, U, 4, 0, 4)
+    assert base.zeros[r, 0] == 8
+    adopt, reject = base.zeros.copy(), base.zeros.copy()
+    adopt[r, 0], reject[r, 0] = 7, 9
+    return w, U, 4, 0, 4, r, adopt, reject
+
+
+def code_tie_case():
+    """Identity U (no feedback, so every decision is round-to-nearest of W0 / scale
+    on the per-row grid): row 2, column 5 holds w / scale = (k + 0.5) + 3e-4 with
+    the code k + 1 + zero; supplying k + zero must be adopted.  Row 1, column 6
+    (w / scale = k' + 0.3) supplied with its other neighbour must be rejected.
+    Returns (W0, U, bits, block, codes_adopt, codes_reject)."""
+    rng = np.random.default_rng(43)
+    w = 0.02 * rng.standard_normal((4, 10))
+    s, z = O.grid_params(w, 4)
+    w[2, 5] = s[2] * (2 + 0.5 + 3e-4)
+    w[1, 6] = s[1] * (-1 + 0.3)
+    s2, z2 = O.grid_params(w, 4)
+    assert np.array_equal(s, s2) and np.array_equal(z, z2)   # interior values only
+    U = np.eye(10)
+    base = O.gptq_quantize(w, U, 4, 0, 4)
+    assert base.codes[2, 5] == 3 + z[2] and base.codes[1, 6] == -1 + z[1]
+    adopt, reject = base.codes.copy(), base.codes.copy()
+    adopt[2, 5] = 2 + z[2]
+    reject[1, 6] = 0 + z[1]
+    return w, U, 4, 4, adopt, reject
+
+
+def test_replay_adopts_a_zero_point_at_a_tie():
+    w, U, bits, g, B, r, adopt, reject = zero_tie_case()
+    res = O.gptq_quantize(w, U, bits, g, B, replay_zeros=adopt)
+    assert res.adopted_zeros == 1
+    np.testing.assert_array_equal(res.zeros, adopt)
+    # the adopted zero-point is the one the row's codes and What use
+    np.testing.assert_array_equal(res.w_hat[r], res.scales[r, 0] * (res.codes[r].astype(np.float64) - 7))
+    free = O.gptq_quantize(w, U, bits, g, B)
+    np.testing.assert_array_equal(res.codes[np.arange(6) != r], free.codes[np.arange(6) != r])
+    assert not np.array_equal(res.w_hat[r], free.w_hat[r])
+
+
+def test_replay_rejects_a_zero_point_off_the_tie():
+    w, U, bits, g, B, r, adopt, reject = zero_tie_case()
+    with pytest.raises(O.ReplayMismatch):
+        O.gptq_quantize(w, U, bits, g, B, replay_zeros=reject)
+    far = adopt.copy()
+    far[r, 0] = 6                                            # two steps away
+    with pytest.raises(O.ReplayMismatch):
+        O.gptq_quantize(w, U, bits, g, B, replay_zeros=far)
+    with pytest.raises(O.ReplayMismatch):                    # tie farther than the tolerance
+        O.gptq_quantize(w, U, bits, g, B, replay_zeros=adopt, replay_tol=1e-4)
+
+
+def test_replay_adopts_a_group_zero_point_at_a_tie():
+    """Groups of 16 inside blocks of 32, identity U (each group's grid comes from
+    W0 alone): group 2 of row 1 is built with -min/scale = 4.5 - 3e-4."""
+    rng = np.random.default_rng(44)
+    w = 0.02 * rng.standard_normal((3, 64))
+    span, v = 0.05, 4.5 - 3e-4
+    a = span * v / 15.0
+    w[1, 32:48] = np.linspace(-a, span - a, 16)
+    U = np.eye(64)
+    base = O.gptq_quantize(w, U, 4, 16, 32)
+    assert base.zeros[1, 2] == 4
+    adopt = base.zeros.copy()
+    adopt[1, 2] = 5
+    res = O.gptq_quantize(w, U, 4, 16, 32, replay_zeros=adopt)
+    assert res.adopted_zeros == 1 and res.zeros[1, 2] == 5
+    np.testing.assert_array_equal(res.w_hat[1, 32:48],
+                                  res.scales[1, 2] * (res.codes[1, 32:48].astype(np.float64) - 5))
+    bad = base.zeros.copy()
+    bad[1, 2] = 3
+    with pytest.raises(O.ReplayMismatch):
+        O.gptq_quantize(w, U, 4, 16, 32, replay_zeros=bad)
+
+
+def test_replay_adopts_a_code_at_a_tie_and_rejects_a_neighbour_off_it():
+    w, U, bits, B, adopt, reject = code_tie_case()
+    res = O.gptq_quantize(w, U, bits, 0, B, replay_codes=adopt)
+    assert res.adopted_codes == 1
+    np.testing.assert_array_equal(res.codes, adopt)
+    assert res.max_boundary_dist == pytest.approx(3e-4, abs=1e-9)
+    with pytest.raises(O.ReplayMismatch):
+        O.gptq_quantize(w, U, bits, 0, B, replay_codes=reject)
