@@ -17,7 +17,10 @@
  *     width.
  *   - Pointers marked [device] are device (HBM) addresses on the current HIP
  *     device; [host] pointers are host addresses.  The caller owns every
- *     buffer; the library allocates nothing and keeps no state between calls.
+ *     buffer; the library allocates no device memory.  Its only state kept
+ *     between calls is a host-side memo, one per calling thread, of the
+ *     Hessian launch's work-group tile order for the last tile count seen (a
+ *     pure function of the shape, so no result depends on it).
  *   - `stream` is a hipStream_t (NULL = the null stream).  Every call only
  *     enqueues work on that stream and returns; results are valid once the
  *     stream has been synchronised.  Calls on different streams are

@@ -37,7 +37,9 @@ _LIB = None
 
 
 def lib_path() -> str:
-    return os.path.join(_HERE, "_lib", "libgptq.so")
+    """The in-tree libgptq.so, or the library named by GPTQ_LIBRARY (the
+    sanitizer build of the host code is tested that way)."""
+    return os.environ.get("GPTQ_LIBRARY") or os.path.join(_HERE, "_lib", "libgptq.so")
 
 
 class GPTQError(RuntimeError):
@@ -123,10 +125,24 @@ def _ptr(t) -> Optional[int]:
     return None if t is None else t.data_ptr()
 
 
-def _stream(stream) -> Optional[int]:
+def _stream(stream, *tensors) -> Optional[int]:
+    """The HIP stream handle to launch on.
+
+    With no stream, or torch's current stream, nothing else happens.  With any
+    other stream, that stream first waits for the work already queued on the
+    current stream (the producer of the inputs, in torch's usual stream
+    semantics), and every tensor the call touches (inputs, outputs and the
+    workspace) is recorded as in use on that stream, so the caching allocator
+    does not hand its memory out again before the launched kernels are done."""
     torch = _torch()
-    s = stream if stream is not None else torch.cuda.current_stream()
-    return s.cuda_stream
+    cur = torch.cuda.current_stream()
+    if stream is None or stream == cur:
+        return cur.cuda_stream
+    stream.wait_stream(cur)
+    for t in tensors:
+        if t is not None:
+            t.record_stream(stream)
+    return stream.cuda_stream
 
 
 def _dtype_code(t) -> int:
@@ -179,7 +195,7 @@ def gptq_hessian_accumulate(H, X, ws=None, stream=None):
     need = gptq_hessian_accumulate_workspace_size(d, n, code)
     ws = _workspace(need, X.device, ws)
     st = library().gptq_hessian_accumulate(H.data_ptr(), d, X.data_ptr(), code, n, X.stride(0),
-                                           ws.data_ptr(), ws.numel(), _stream(stream))
+                                           ws.data_ptr(), ws.numel(), _stream(stream, H, X, ws))
     _check(st, "gptq_hessian_accumulate")
     return H
 
@@ -197,7 +213,7 @@ def gptq_prepare_hinv(H, percdamp: float = 0.01, U=None, lam=None, info=None, ws
     ws = _workspace(gptq_prepare_hinv_workspace_size(d), dev, ws)
     st = library().gptq_prepare_hinv(H.data_ptr(), d, float(percdamp), U.data_ptr(),
                                      lam.data_ptr(), info.data_ptr(), ws.data_ptr(), ws.numel(),
-                                     _stream(stream))
+                                     _stream(stream, H, U, lam, info, ws))
     _check(st, "gptq_prepare_hinv")
     return U, lam, info
 
@@ -220,7 +236,8 @@ def gptq_quantize_layer(W0, U, lam=None, bits: int = 4, group_size: int = 0,
                                        U.data_ptr(), _ptr(lam), int(bits), int(group_size),
                                        int(block_size), codes.data_ptr(), scales.data_ptr(),
                                        zeros.data_ptr(), out_err.data_ptr(), ws.data_ptr(),
-                                       ws.numel(), _stream(stream))
+                                       ws.numel(), _stream(stream, W0, U, lam, codes, scales, zeros,
+                                                           out_err, ws))
     _check(st, "gptq_quantize_layer")
     return codes, scales, zeros, out_err
 
@@ -231,7 +248,7 @@ def gptq_act_order_perm(H, perm=None, stream=None):
     torch = _torch()
     d = H.shape[0]
     perm = perm if perm is not None else torch.empty(d, dtype=torch.int32, device=H.device)
-    st = library().gptq_act_order_perm(H.data_ptr(), d, perm.data_ptr(), _stream(stream))
+    st = library().gptq_act_order_perm(H.data_ptr(), d, perm.data_ptr(), _stream(stream, H, perm))
     _check(st, "gptq_act_order_perm")
     return perm
 
@@ -249,7 +266,8 @@ def gptq_prepare_hinv_perm(H, perm, percdamp: float = 0.01, U=None, lam=None, in
     ws = _workspace(gptq_prepare_hinv_workspace_size(d), dev, ws)
     st = library().gptq_prepare_hinv_perm(H.data_ptr(), d, perm.data_ptr(), float(percdamp),
                                           U.data_ptr(), lam.data_ptr(), info.data_ptr(),
-                                          ws.data_ptr(), ws.numel(), _stream(stream))
+                                          ws.data_ptr(), ws.numel(),
+                                          _stream(stream, H, perm, U, lam, info, ws))
     _check(st, "gptq_prepare_hinv_perm")
     return U, lam, info
 
@@ -275,7 +293,8 @@ def gptq_quantize_layer_perm(W0, U, lam, perm, bits: int = 4, group_size: int = 
                                             int(bits), int(group_size), int(block_size),
                                             codes.data_ptr(), scales.data_ptr(), zeros.data_ptr(),
                                             g_idx.data_ptr(), out_err.data_ptr(), ws.data_ptr(),
-                                            ws.numel(), _stream(stream))
+                                            ws.numel(), _stream(stream, W0, U, lam, perm, codes, scales,
+                                                                zeros, g_idx, out_err, ws))
     _check(st, "gptq_quantize_layer_perm")
     return codes, scales, zeros, g_idx, out_err
 
@@ -294,7 +313,8 @@ def gptq_pack_codes(codes, bits: int, perm=None, packed=None, stream=None):
     packed = packed if packed is not None else torch.empty(d_row, words, dtype=torch.int32,
                                                              device=codes.device)
     st = library().gptq_pack_codes(codes.data_ptr(), d_row, d_col, codes.stride(0), int(bits),
-                                   _ptr(perm), packed.data_ptr(), packed.stride(0), _stream(stream))
+                                   _ptr(perm), packed.data_ptr(), packed.stride(0),
+                                   _stream(stream, codes, perm, packed))
     _check(st, "gptq_pack_codes")
     return packed
 
@@ -320,7 +340,7 @@ def gptq2d_quantize(X, U_Q, U_P, bits: int, codes=None, scale=None, zero=None, o
     st = library().gptq2d_quantize(X.data_ptr(), _dtype_code(X), m, n, X.stride(0), U_Q.data_ptr(),
                                    U_P.data_ptr(), int(bits), codes.data_ptr(), codes.stride(0), scale.data_ptr(),
                                    zero.data_ptr(), out_err.data_ptr(), ws.data_ptr(), ws.numel(),
-                                   _stream(stream))
+                                   _stream(stream, X, U_Q, U_P, codes, scale, zero, out_err, ws))
     _check(st, "gptq2d_quantize")
     return codes, scale, zero, out_err
 
@@ -337,7 +357,8 @@ def gptq_dequantize(codes, scales, zeros, group_size: int, g_idx=None, out=None,
     _rowmajor(out, "out")
     st = library().gptq_dequantize(codes.data_ptr(), d_row, d_col, codes.stride(0), scales.data_ptr(),
                                    zeros.data_ptr(), int(group_size), _ptr(g_idx), out.data_ptr(),
-                                   _dtype_code(out), out.stride(0), _stream(stream))
+                                   _dtype_code(out), out.stride(0),
+                                   _stream(stream, codes, scales, zeros, g_idx, out))
     _check(st, "gptq_dequantize")
     return out
 
@@ -353,7 +374,7 @@ def gptq_dequant_matmul(packed, bits: int, scales, zeros, group_size: int, X, d_
     st = library().gptq_dequant_matmul(packed.data_ptr(), packed.stride(0), int(bits), scales.data_ptr(),
                                        zeros.data_ptr(), int(group_size), _ptr(perm), d_row, d_col,
                                        X.data_ptr(), _dtype_code(X), m, X.stride(0), Y.data_ptr(),
-                                       Y.stride(0), _stream(stream))
+                                       Y.stride(0), _stream(stream, packed, scales, zeros, perm, X, Y))
     _check(st, "gptq_dequant_matmul")
     return Y
 

@@ -63,5 +63,43 @@ def build(verbose: bool = True) -> str:
     return LIB
 
 
+SANITIZE = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined"]
+LIB_SAN = os.path.join(BUILD, "libgptq_sanitized.so")
+
+
+def build_sanitized(verbose: bool = False) -> str:
+    """libgptq with the C ABI layer (abi.cpp: argument validation, planning calls,
+    dispatch) built with AddressSanitizer and UndefinedBehaviorSanitizer on the
+    host side, linked with the kernels' objects of the normal build.  Loaded with
+    the sanitizer runtime preloaded (the CPU ABI tests run that way); never used
+    on a GPU.  Rebuilt when abi.cpp, the headers or the objects are newer."""
+    objs = [os.path.join(BUILD, os.path.splitext(s)[0] + ".o") for s in SOURCES if s != "abi.cpp"]
+    if not all(os.path.exists(o) for o in objs):
+        build(verbose)
+    deps = [os.path.join(CSRC, "abi.cpp"), os.path.join(CSRC, "gptq_internal.h"),
+            os.path.join(INCLUDE, "gptq.h"), *objs]
+    if os.path.exists(LIB_SAN) and os.path.getmtime(LIB_SAN) >= max(os.path.getmtime(d) for d in deps):
+        return LIB_SAN
+    abi = os.path.join(BUILD, "abi_sanitized.o")
+    flags = [f for f in FLAGS if f != "-O3"] + ["-O1", "-g", "-fno-omit-frame-pointer"]
+    for cmd in ([hipcc(), "-x", "hip", *flags, *SANITIZE, "-c", os.path.join(CSRC, "abi.cpp"), "-o", abi],
+                [hipcc(), "-shared", f"--offload-arch={ARCH}", *SANITIZE, "-o", LIB_SAN + ".tmp", abi, *objs]):
+        res = subprocess.run(cmd, capture_output=True, text=True)
+        if res.returncode != 0:
+            raise RuntimeError(f"sanitized build failed:\n{res.stdout}{res.stderr}")
+    os.replace(LIB_SAN + ".tmp", LIB_SAN)
+    return LIB_SAN
+
+
+def sanitizer_runtime() -> str:
+    """Path of the compiler's AddressSanitizer runtime (to preload)."""
+    clang = os.path.join(os.path.dirname(os.path.realpath(hipcc())), "..", "lib", "llvm", "bin", "clang")
+    if not os.path.exists(clang):
+        clang = "/opt/rocm/lib/llvm/bin/clang"
+    res = subprocess.run([clang, "-print-file-name=libclang_rt.asan-x86_64.so"], capture_output=True,
+                         text=True, check=True)
+    return res.stdout.strip()
+
+
 if __name__ == "__main__":
     build()

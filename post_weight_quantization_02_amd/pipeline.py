@@ -61,7 +61,8 @@ def quantize_model(blocks: Sequence, x_batches: Sequence, bits: int, group_size:
     tensors) as the first block's calibration inputs.  The layers' weights are
     replaced by What in place.  Returns (per-block results, the last block's
     outputs for the batches).  Raises NotPositiveDefinite if a layer's damped H
-    could not be factored (checked once per block)."""
+    could not be factored (checked once per block, before any weight of that
+    block is replaced, so the block's weights are then left as they were)."""
     torch = _torch()
     xs = list(x_batches)
     results = []
@@ -100,14 +101,19 @@ def quantize_model(blocks: Sequence, x_batches: Sequence, bits: int, group_size:
                     U, lam, info = gptq_prepare_hinv(Hs[n], percdamp, stream=stream)
                     codes, scales, zeros, err = gptq_quantize_layer(W0, U, lam, bits, group_size, block_size,
                                                                     stream=stream)
-                # enqueued after the loop that reads W0, so W0 is replaced only once it is used
-                gptq_dequantize(codes, scales, zeros, group_size, g_idx, out=W0, stream=stream)
+                # What goes to a staging tensor: the weights are replaced only once every
+                # layer of the block is known to have been factored (U is unspecified
+                # when info != 0, and a caller may catch the error and retry)
+                w_hat = gptq_dequantize(codes, scales, zeros, group_size, g_idx, out_dtype=W0.dtype,
+                                        stream=stream)
                 layers[n] = LayerQuant(codes, scales, zeros, err, lam, perm, g_idx, Hs[n] if keep_hessians else None)
-                infos.append((n, info))
+                infos.append((n, info, W0, w_hat))
             (stream or torch.cuda.current_stream()).synchronize()
-            for n, info in infos:
+            for n, info, _, _ in infos:
                 if int(info.item()) != 0:
                     raise NotPositiveDefinite(int(info.item()))
+            for _, _, W0, w_hat in infos:
+                W0.copy_(w_hat)
             results.append(BlockQuant(layers, xs if keep_inputs else None))
             xs = [block(x) for x in xs] if sequential else ys
     return results, xs
