@@ -54,7 +54,9 @@ typedef enum {
   GPTQ_ERR_WORKSPACE = 8,       /* ws NULL or smaller than the query      */
   GPTQ_ERR_BAD_DAMP = 9,        /* percdamp negative or not finite        */
   GPTQ_ERR_LAUNCH = 10,         /* a HIP launch or runtime call failed    */
-  GPTQ_ERR_TOO_LARGE = 11       /* a size exceeds the library's limits    */
+  GPTQ_ERR_TOO_LARGE = 11,      /* a size exceeds the library's limits    */
+  GPTQ_ERR_SCRATCH = 12         /* shape too large for the no-allocation  */
+                                /* entry point's fixed workspace          */
 } gptq_status;
 
 typedef enum {
@@ -160,6 +162,34 @@ gptq_status gptq_quantize_layer(const void* W0, int32_t w_dtype, int64_t d_row, 
                                 float* scales, int32_t* zeros, double* out_err, void* ws,
                                 size_t ws_bytes, void* stream);
 size_t gptq_quantize_layer_workspace_size(int64_t d_row, int64_t d_col, int64_t block_size);
+
+/*
+ * gptq_quantize_layer without a workspace argument, for callers that cannot
+ * allocate device memory: code being captured into a HIP graph, tight serving
+ * loops, harnesses that forbid hipMalloc.  Same arguments, results and kernels
+ * as gptq_quantize_layer (bitwise the same outputs) minus ws / ws_bytes; the
+ * call allocates nothing.  Its workspace is a fixed device array of
+ * GPTQ_NOALLOC_SCRATCH_BYTES bytes inside the library, one per device, which
+ * each device holds from the library's load until the process ends.
+ *
+ *   Limit: shapes with gptq_quantize_layer_workspace_size(d_row, d_col,
+ *          block_size) > GPTQ_NOALLOC_SCRATCH_BYTES are rejected with
+ *          GPTQ_ERR_SCRATCH before anything is enqueued (4096 x 4096 with
+ *          blocks of 128 fits).
+ *   Races: every call on one device shares that device's array, which keeps
+ *          the last call's contents (each call clears what it needs zeroed
+ *          with a kernel).  Calls that can overlap on one device -- on
+ *          different streams, or from different host threads without
+ *          ordering -- race on it; order them on one stream.
+ *   The first call on a device looks up the array's address there
+ *   (hipGetSymbolAddress, under a lock); later calls reuse it.
+ */
+#define GPTQ_NOALLOC_SCRATCH_BYTES (96ull << 20)
+gptq_status gptq_quantize_layer_noalloc(const void* W0, int32_t w_dtype, int64_t d_row,
+                                        int64_t d_col, int64_t ld_w, const float* U,
+                                        const float* lambda, int32_t bits, int64_t group_size,
+                                        int64_t block_size, uint8_t* codes, float* scales,
+                                        int32_t* zeros, double* out_err, void* stream);
 
 /*
  * Act-order (itwiki "GPTQ", section "실무 변형" (practical variants): an option of

@@ -22,7 +22,8 @@ __all__ = [
     "GPTQ_F32", "GPTQ_F16", "GPTQError", "NotPositiveDefinite", "library", "lib_path",
     "gptq_hessian_accumulate", "gptq_hessian_accumulate_workspace_size",
     "gptq_prepare_hinv", "gptq_prepare_hinv_workspace_size",
-    "gptq_quantize_layer", "gptq_quantize_layer_workspace_size",
+    "gptq_quantize_layer", "gptq_quantize_layer_workspace_size", "gptq_quantize_layer_noalloc",
+    "GPTQ_NOALLOC_SCRATCH_BYTES",
     "gptq_act_order_perm", "gptq_prepare_hinv_perm", "gptq_quantize_layer_perm",
     "gptq_packed_words_per_row", "gptq_pack_codes", "gptq_dequant_matmul", "gptq_dequantize",
     "gptq2d_quantize", "gptq2d_quantize_workspace_size",
@@ -31,6 +32,7 @@ __all__ = [
 
 GPTQ_F32 = 0
 GPTQ_F16 = 1
+GPTQ_NOALLOC_SCRATCH_BYTES = 96 << 20   # include/gptq.h
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB = None
@@ -77,6 +79,9 @@ def library() -> ctypes.CDLL:
     lib.gptq_quantize_layer.argtypes = [vp, i32, i64, i64, i64, vp, vp, i32, i64, i64, vp, vp, vp,
                                         vp, vp, sz, vp]
     lib.gptq_quantize_layer.restype = i32
+    lib.gptq_quantize_layer_noalloc.argtypes = [vp, i32, i64, i64, i64, vp, vp, i32, i64, i64, vp, vp,
+                                                vp, vp, vp]
+    lib.gptq_quantize_layer_noalloc.restype = i32
     lib.gptq_quantize_layer_workspace_size.argtypes = [i64, i64, i64]
     lib.gptq_quantize_layer_workspace_size.restype = sz
     lib.gptq_act_order_perm.argtypes = [vp, i64, vp, vp]
@@ -239,6 +244,31 @@ def gptq_quantize_layer(W0, U, lam=None, bits: int = 4, group_size: int = 0,
                                        ws.numel(), _stream(stream, W0, U, lam, codes, scales, zeros,
                                                            out_err, ws))
     _check(st, "gptq_quantize_layer")
+    return codes, scales, zeros, out_err
+
+
+def gptq_quantize_layer_noalloc(W0, U, lam=None, bits: int = 4, group_size: int = 0,
+                                block_size: int = 128, codes=None, scales=None, zeros=None,
+                                out_err=None, stream=None):
+    """gptq_quantize_layer without a workspace: the library's fixed per-device
+    array (GPTQ_NOALLOC_SCRATCH_BYTES) serves as one.  Pass every output to keep
+    the call free of allocations (e.g. under graph capture).  Calls that may
+    overlap on one device race on that array."""
+    torch = _torch()
+    _rowmajor(W0, "W0")
+    d_row, d_col = W0.shape
+    dev = W0.device
+    ng = -(-d_col // group_size) if group_size else 1
+    codes = codes if codes is not None else torch.empty(d_row, d_col, dtype=torch.uint8, device=dev)
+    scales = scales if scales is not None else torch.empty(d_row, ng, dtype=torch.float32, device=dev)
+    zeros = zeros if zeros is not None else torch.empty(d_row, ng, dtype=torch.int32, device=dev)
+    out_err = out_err if out_err is not None else torch.empty(1, dtype=torch.float64, device=dev)
+    st = library().gptq_quantize_layer_noalloc(W0.data_ptr(), _dtype_code(W0), d_row, d_col, W0.stride(0),
+                                               U.data_ptr(), _ptr(lam), int(bits), int(group_size),
+                                               int(block_size), codes.data_ptr(), scales.data_ptr(),
+                                               zeros.data_ptr(), out_err.data_ptr(),
+                                               _stream(stream, W0, U, lam, codes, scales, zeros, out_err))
+    _check(st, "gptq_quantize_layer_noalloc")
     return codes, scales, zeros, out_err
 
 

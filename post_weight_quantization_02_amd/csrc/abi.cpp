@@ -7,6 +7,8 @@
 
 #include "gptq_internal.h"
 
+static_assert(gptq::kNoAllocScratchBytes == GPTQ_NOALLOC_SCRATCH_BYTES, "scratch size");
+
 namespace {
 
 constexpr int64_t kMaxDim = int64_t(1) << 20;        // d_col and d_row limits
@@ -91,12 +93,10 @@ size_t gptq_quantize_layer_workspace_size(int64_t d_row, int64_t d_col, int64_t 
   return gptq::quant_plan(d_row, d_col, block_size).ws_bytes;
 }
 
-static gptq_status quantize_layer(const void* W0, int32_t w_dtype, int64_t d_row, int64_t d_col,
-                                  int64_t ld_w, const float* U, const float* lambda,
-                                  const int32_t* perm, int32_t bits, int64_t group_size,
-                                  int64_t block_size, uint8_t* codes, float* scales, int32_t* zeros,
-                                  int32_t* g_idx, double* out_err, void* ws, size_t ws_bytes,
-                                  void* stream) {
+static gptq_status check_quantize_args(const void* W0, int32_t w_dtype, int64_t d_row, int64_t d_col,
+                                       int64_t ld_w, const float* U, int32_t bits, int64_t group_size,
+                                       int64_t block_size, const uint8_t* codes, const float* scales,
+                                       const int32_t* zeros, const double* out_err) {
   if (d_row <= 0 || d_col <= 0) return GPTQ_ERR_BAD_SIZE;
   if (d_row > kMaxDim || d_col > kMaxDim) return GPTQ_ERR_TOO_LARGE;
   if (w_dtype != GPTQ_F32 && w_dtype != GPTQ_F16) return GPTQ_ERR_BAD_DTYPE;
@@ -110,6 +110,18 @@ static gptq_status quantize_layer(const void* W0, int32_t w_dtype, int64_t d_row
                                             (group_size % block_size != 0 &&
                                              block_size % group_size != 0))))
     return GPTQ_ERR_BAD_GROUP;
+  return GPTQ_OK;
+}
+
+static gptq_status quantize_layer(const void* W0, int32_t w_dtype, int64_t d_row, int64_t d_col,
+                                  int64_t ld_w, const float* U, const float* lambda,
+                                  const int32_t* perm, int32_t bits, int64_t group_size,
+                                  int64_t block_size, uint8_t* codes, float* scales, int32_t* zeros,
+                                  int32_t* g_idx, double* out_err, void* ws, size_t ws_bytes,
+                                  void* stream) {
+  if (gptq_status st = check_quantize_args(W0, w_dtype, d_row, d_col, ld_w, U, bits, group_size,
+                                           block_size, codes, scales, zeros, out_err))
+    return st;
   const gptq::QuantPlan plan = gptq::quant_plan(d_row, d_col, block_size);
   if (gptq_status st = ws_check(ws, ws_bytes, plan.ws_bytes)) return st;
   return from_hip(gptq::quant_launch(plan, W0, w_dtype, ld_w, U, lambda, perm, bits, group_size, codes,
@@ -123,6 +135,21 @@ gptq_status gptq_quantize_layer(const void* W0, int32_t w_dtype, int64_t d_row, 
                                 size_t ws_bytes, void* stream) {
   return quantize_layer(W0, w_dtype, d_row, d_col, ld_w, U, lambda, nullptr, bits, group_size,
                         block_size, codes, scales, zeros, nullptr, out_err, ws, ws_bytes, stream);
+}
+
+gptq_status gptq_quantize_layer_noalloc(const void* W0, int32_t w_dtype, int64_t d_row, int64_t d_col,
+                                        int64_t ld_w, const float* U, const float* lambda, int32_t bits,
+                                        int64_t group_size, int64_t block_size, uint8_t* codes,
+                                        float* scales, int32_t* zeros, double* out_err, void* stream) {
+  if (gptq_status st = check_quantize_args(W0, w_dtype, d_row, d_col, ld_w, U, bits, group_size,
+                                           block_size, codes, scales, zeros, out_err))
+    return st;
+  const gptq::QuantPlan plan = gptq::quant_plan(d_row, d_col, block_size);
+  if (plan.ws_bytes > gptq::kNoAllocScratchBytes) return GPTQ_ERR_SCRATCH;
+  void* scratch = nullptr;
+  if (gptq::noalloc_scratch(&scratch) != hipSuccess) return GPTQ_ERR_LAUNCH;
+  return from_hip(gptq::quant_launch(plan, W0, w_dtype, ld_w, U, lambda, nullptr, bits, group_size, codes,
+                                     scales, zeros, nullptr, out_err, scratch, (hipStream_t)stream));
 }
 
 gptq_status gptq_quantize_layer_perm(const void* W0, int32_t w_dtype, int64_t d_row, int64_t d_col,
@@ -223,6 +250,9 @@ const char* gptq_status_string(int32_t status) {
     case GPTQ_ERR_BAD_DAMP: return "percdamp must be finite and >= 0";
     case GPTQ_ERR_LAUNCH: return "a HIP launch or runtime call failed";
     case GPTQ_ERR_TOO_LARGE: return "a size exceeds the library limits";
+    case GPTQ_ERR_SCRATCH:
+      return "the shape needs more workspace than the no-allocation entry point holds "
+             "(gptq_quantize_layer_workspace_size > GPTQ_NOALLOC_SCRATCH_BYTES)";
     default: return "unknown status";
   }
 }

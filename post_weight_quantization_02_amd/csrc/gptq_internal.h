@@ -97,6 +97,12 @@ hipError_t quant_launch(const QuantPlan& p, const void* W0, int w_dtype, int64_t
                         int64_t group, uint8_t* codes, float* scales, int32_t* zeros,
                         int32_t* g_idx, double* out_err, void* ws, hipStream_t s);
 
+// The no-allocation entry point's workspace: a device array of this many bytes
+// (one per device), and its address on the current device (looked up once per
+// device, then kept).
+constexpr size_t kNoAllocScratchBytes = size_t(96) << 20;
+hipError_t noalloc_scratch(void** out);
+
 // W[:, i+B:] -= E U[i:i+B, i+B:] with E given transposed: C [M x N] (ldc) -=
 // Et^T [M x K] * Ub [K x N]; Et is [K x M] (lde), Ub [K x N] (ldu); K <= 128.
 hipError_t trail_update_launch(float* C, int64_t ldc, int M, int N, int K, const float* Et,

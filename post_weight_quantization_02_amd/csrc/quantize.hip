@@ -22,6 +22,8 @@
 // after U is staged.
 #include "gptq_internal.h"
 
+#include <mutex>
+
 namespace gptq {
 namespace {
 
@@ -543,6 +545,32 @@ __global__ __launch_bounds__(kThreads) void g_idx_kernel(const int32_t* __restri
 constexpr int64_t kErrWGs = 1024;
 
 }  // namespace
+
+// The workspace of the no-allocation entry point: one array per device, loaded
+// with the code object and held until the process ends.  Host code reaches it
+// only through the address hipGetSymbolAddress returns for the current device
+// (the array's name in host code is a host-side stand-in, not that address).
+static __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+
+hipError_t noalloc_scratch(void** out) {
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static void* addr[kMaxDevices] = {};
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (addr[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (p == nullptr) return hipErrorInvalidSymbol;
+    addr[dev] = p;
+  }
+  *out = addr[dev];
+  return hipSuccess;
+}
 
 QuantPlan quant_plan(int64_t d_row, int64_t d_col, int64_t B) {
   QuantPlan p{};

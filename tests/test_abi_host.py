@@ -26,7 +26,7 @@ def _status(name):
     return {"GPTQ_OK": 0, "GPTQ_ERR_NULL_POINTER": 1, "GPTQ_ERR_BAD_SIZE": 2,
             "GPTQ_ERR_BAD_LEADING_DIM": 3, "GPTQ_ERR_BAD_DTYPE": 4, "GPTQ_ERR_BAD_BITS": 5,
             "GPTQ_ERR_BAD_BLOCK": 6, "GPTQ_ERR_BAD_GROUP": 7, "GPTQ_ERR_WORKSPACE": 8,
-            "GPTQ_ERR_BAD_DAMP": 9, "GPTQ_ERR_LAUNCH": 10, "GPTQ_ERR_TOO_LARGE": 11}[name]
+            "GPTQ_ERR_BAD_DAMP": 9, "GPTQ_ERR_LAUNCH": 10, "GPTQ_ERR_TOO_LARGE": 11, "GPTQ_ERR_SCRATCH": 12}[name]
 
 
 def test_header_status_values_match():
@@ -46,7 +46,7 @@ def test_every_declared_symbol_is_exported():
 
 def test_version_and_status_strings():
     assert G.gptq_version().startswith("gptq-gfx950")
-    for s in range(12):
+    for s in range(13):
         assert G.gptq_status_string(s) and G.gptq_status_string(s) != "unknown status"
     assert G.gptq_status_string(99) == "unknown status"
 
@@ -216,3 +216,24 @@ def test_gptq2d_validation():
     assert f(*a) == _status("GPTQ_ERR_WORKSPACE")
     a = list(ok); a[3] = (1 << 20) + 1; a[4] = a[3]; a[9] = a[3]
     assert f(*a) == _status("GPTQ_ERR_TOO_LARGE")
+
+
+def test_noalloc_validation_and_scratch_limit():
+    f = G.library().gptq_quantize_layer_noalloc
+    assert G.GPTQ_NOALLOC_SCRATCH_BYTES == 96 << 20
+    text = open(HEADER).read()
+    assert "#define GPTQ_NOALLOC_SCRATCH_BYTES (96ull << 20)" in text
+    # same argument checks as gptq_quantize_layer, all before any device call
+    assert f(FAKE, 1, 0, 64, 64, FAKE, FAKE, 4, 0, 128, FAKE, FAKE, FAKE, FAKE, None) == _status("GPTQ_ERR_BAD_SIZE")
+    assert f(None, 1, 8, 64, 64, FAKE, FAKE, 4, 0, 128, FAKE, FAKE, FAKE, FAKE, None) == _status("GPTQ_ERR_NULL_POINTER")
+    assert f(FAKE, 1, 8, 64, 64, FAKE, FAKE, 9, 0, 128, FAKE, FAKE, FAKE, FAKE, None) == _status("GPTQ_ERR_BAD_BITS")
+    assert f(FAKE, 1, 8, 64, 64, FAKE, FAKE, 4, 24, 128, FAKE, FAKE, FAKE, FAKE, None) == _status("GPTQ_ERR_BAD_GROUP")
+    assert f(FAKE, 1, 8, 64, 32, FAKE, FAKE, 4, 0, 128, FAKE, FAKE, FAKE, FAKE, None) == _status("GPTQ_ERR_BAD_LEADING_DIM")
+    # the limit is the workspace query against the fixed array
+    fits = G.gptq_quantize_layer_workspace_size(4096, 4096, 128)
+    assert 0 < fits <= G.GPTQ_NOALLOC_SCRATCH_BYTES
+    big = G.gptq_quantize_layer_workspace_size(4096, 8192, 128)
+    assert big > G.GPTQ_NOALLOC_SCRATCH_BYTES
+    assert f(FAKE, 1, 4096, 8192, 8192, FAKE, FAKE, 4, 128, 128, FAKE, FAKE, FAKE, FAKE, None) == \
+        _status("GPTQ_ERR_SCRATCH")
+    assert "no-allocation" in G.gptq_status_string(12)
