@@ -410,3 +410,16 @@ def test_replay_adopts_a_code_at_a_tie_and_rejects_a_neighbour_off_it():
     assert res.max_boundary_dist == pytest.approx(3e-4, abs=1e-9)
     with pytest.raises(O.ReplayMismatch):
         O.gptq_quantize(w, U, bits, 0, B, replay_codes=reject)
+
+
+def test_trailing_block_of_U_is_the_factor_of_the_trailing_block():
+    """For upper U with U^T U = H^-1, rows and columns k.. of U form the factor of
+    (H[k:, k:])^-1: H = Ut Ut^T with Ut = U^-1 upper gives H[k:, k:] =
+    Ut[k:, k:] Ut[k:, k:]^T.  This is what lets a trailing block of a factor too
+    wide for the host be checked against the oracle on its own."""
+    rng = np.random.default_rng(12)
+    a = rng.standard_normal((400, 160))
+    Hl, _ = O.damp(a.T @ a, 0.01)
+    U = O.inv_hessian_factor(Hl)
+    for k in (0, 1, 37, 100, 159):
+        np.testing.assert_allclose(U[k:, k:], O.inv_hessian_factor(Hl[k:, k:]), rtol=0, atol=1e-12)

@@ -70,3 +70,48 @@ def test_powerlaw_mix_is_orthogonal_with_k_inverse_spectrum():
     np.testing.assert_allclose(Q @ Q.T, np.eye(24), atol=1e-12)
     k = np.arange(1, 25)
     np.testing.assert_allclose(s ** 2, 24.0 / (k * np.sum(1.0 / k)), rtol=1e-12)
+
+
+# ---------------------------------------------------------------- device recipes
+# The device generator draws other random numbers than the host one; what must
+# agree is the law.  Each check inverts the recipe's deterministic part on the
+# CPU build of torch and looks at what is left.
+
+def _device_chunk(spec, rows):
+    from workloads import device as D
+    return D.make_x_chunk_device(spec, 0, rows=rows, device="cpu").float().numpy().astype(np.float64)
+
+
+def test_device_powerlaw_inverts_to_white_noise():
+    spec = wl.workload_layers(5)[0].scaled(d_col=3 * 256)
+    x = _device_chunk(spec, 8192)
+    m, s, signs, q3, perm = wl._powerlaw_params(spec)
+    y = x[:, perm].reshape(-1, 3, 1 << m)                  # undo the permutation
+    y = wl._fwht_rows(y) * 2.0 ** (-m / 2.0)               # the normalised transform is its own inverse
+    y = np.einsum("ba,rbk->rak", q3, y).reshape(-1, spec.d_col) / (s * signs)
+    # fp16 storage rounds x by <= 2^-11 relative; the whitened values stay N(0, 1)
+    assert abs(y.mean()) < 0.01
+    v = y.var(axis=0)
+    assert abs(v.mean() - 1.0) < 0.01 and v.max() < 1.2 and v.min() > 0.8
+
+
+def test_device_lowrank_lies_in_the_mixing_row_space():
+    spec = wl.workload_layers(3)[0].scaled(d_col=512)
+    x = _device_chunk(spec, 4096)
+    a, ch = wl._lowrank_params(spec)
+    x[:, ch] /= 20.0
+    z = x @ np.linalg.pinv(a)
+    resid = np.linalg.norm(x - z @ a) / np.linalg.norm(x)
+    assert resid < 2e-3                                   # fp16 rounding only
+    assert abs(z.var() - 1.0) < 0.05
+
+
+def test_device_silu_moments():
+    spec = wl.workload_layers(4)[1].scaled(d_col=256)
+    x = _device_chunk(spec, 16384)
+    # E[SiLU(a) b] = 0, E[(SiLU(a) b)^2] = E[SiLU(a)^2] (b independent, unit variance)
+    t = np.linspace(-12, 12, 200001)
+    phi = np.exp(-t * t / 2) / np.sqrt(2 * np.pi)
+    m2 = np.trapezoid((t / (1 + np.exp(-t))) ** 2 * phi, t)
+    assert abs(x.mean()) < 0.01
+    assert abs((x * x).mean() - m2) < 0.01 * m2 * 3
