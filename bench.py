@@ -11,9 +11,12 @@ columns in descending-diagonal order (order from the GPU's H, then the
 reordered factor and loop), as a separate measurement.
 
 Prints one JSON line.  The metric is seconds per layer (lower is better), with
-per-stage TFLOP/s and the dominant kernel's roofline fraction.  The CPU
-baseline is the fp64 oracle timed on a bounded sample of the same layer and
-scaled to one layer.
+per-stage TFLOP/s and three roofline entries: the dominant kernel (the Hessian
+syrk, against the fp16 matrix peak) and, from a separate pass of the same run
+whose launches are bracketed one by one with HIP events, the in-block panel
+(algorithmic bytes against the HBM peak) and the out-of-block products (flop
+against the fp32 matrix peak).  The CPU baseline is the fp64 oracle run on the
+whole layer (every calibration row, every weight row) on the host's cores.
 """
 from __future__ import annotations
 
@@ -69,41 +72,44 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def cpu_baseline(spec, W, X_chunk0, act_order=False):
-    """The fp64 oracle on a bounded sample of the same layer, scaled to one layer."""
-    import numpy as np
-    import oracle as O
+def _blas_threads():
     try:
         from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+        return max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     except Exception:  # pragma: no cover
-        threads = len(os.sched_getaffinity(0))
-    n_chunks = spec.n_rows // X_chunk0.shape[0]
+        return len(os.sched_getaffinity(0))
+
+
+def cpu_baseline(spec, W, X_chunks, act_order=False):
+    """The fp64 oracle on the whole layer: H over every calibration row, the
+    sketch route's factor, the loop over every weight row, the error."""
+    import numpy as np
+    import oracle as O
     t0 = time.perf_counter()
-    H = O.hessian([X_chunk0])
-    t_h = (time.perf_counter() - t0) * n_chunks
+    H = O.hessian(X_chunks)
+    t_h = time.perf_counter() - t0
     t0 = time.perf_counter()
     if act_order:
         perm = O.act_order_perm(H)
-        Hl, lam = O.damp((H * n_chunks)[np.ix_(perm, perm)], spec.percdamp)
+        Hl, lam = O.damp(H[np.ix_(perm, perm)], spec.percdamp)
     else:
-        Hl, lam = O.damp(H * n_chunks, spec.percdamp)
+        Hl, lam = O.damp(H, spec.percdamp)
     U = O.inv_hessian_factor(Hl)
     t_f = time.perf_counter() - t0
-    rows = 256
     t0 = time.perf_counter()
     if act_order:
-        O.gptq_quantize_act_order(W[:rows].astype(np.float64), U, perm, spec.bits, spec.group_size,
-                                  spec.block_size)
+        res = O.gptq_quantize_act_order(W.astype(np.float64), U, perm, spec.bits, spec.group_size,
+                                        spec.block_size)
     else:
-        O.gptq_quantize(W[:rows].astype(np.float64), U, spec.bits, spec.group_size, spec.block_size)
-    t_q = (time.perf_counter() - t0) * (spec.d_row / rows)
+        res = O.gptq_quantize(W.astype(np.float64), U, spec.bits, spec.group_size, spec.block_size)
+    err = O.output_error(W, res.w_hat, H)
+    t_q = time.perf_counter() - t0
     total = t_h + t_f + t_q
-    return {"value": total, "unit": "s/layer", "cores": int(threads), "kind": "oracle",
-            "sample": (f"H over {X_chunk0.shape[0]} of {spec.n_rows} calibration rows (x{n_chunks}), "
-                       f"full {spec.d_col}x{spec.d_col} fp64 factor, loop on {rows} of {spec.d_row} "
-                       f"weight rows (x{spec.d_row // rows}); scaled to one layer"),
-            "stages_s": {"hessian": t_h, "factor": t_f, "loop": t_q}}
+    return {"value": total, "unit": "s/layer", "cores": int(_blas_threads()), "kind": "oracle",
+            "sample": (f"the whole layer, unsampled: H over all {spec.n_rows} calibration rows, the "
+                       f"{spec.d_col}x{spec.d_col} fp64 factor, the loop over all {spec.d_row} weight "
+                       f"rows and the output error"),
+            "stages_s": {"hessian": t_h, "factor": t_f, "loop_and_error": t_q}, "err": err}
 
 
 GEMV_TRAFFIC = os.path.join(ROOT, "profiles", "dequant_gemv_fc49152_traffic.json")
@@ -697,11 +703,11 @@ def main():
     t0 = time.perf_counter()
     W = wl.make_weight(spec)
     Xd = torch.empty(spec.n_rows, spec.d_col, dtype=torch.float16, device=dev)
-    x0 = None
+    x_host = []                    # the same bytes, kept for the CPU oracle's run
     for c in range(wl.n_chunks(spec)):
         xc = wl.make_x_chunk(spec, c)
-        if c == 0:
-            x0 = xc
+        if not args.no_cpu_baseline:
+            x_host.append(xc)
         Xd[c * wl.CHUNK_ROWS:(c + 1) * wl.CHUNK_ROWS].copy_(torch.from_numpy(xc))
     Wd = torch.from_numpy(W).to(dev)
     torch.cuda.synchronize()
@@ -769,6 +775,44 @@ def main():
     log(f"bench: stages ms hessian {t_h * 1e3:.3f} factor {t_f * 1e3:.3f} quantize {t_q * 1e3:.3f}; "
         f"wall/step {per_step * 1e3:.3f} ms; err {float(err.item()):.6g}")
 
+    # Separate pass: the loop's panel and out-of-block product launches, each
+    # bracketed by HIP events on the library's stream (the same step's U).
+    G.gptq_launch_timing(True)
+    for _ in range(3):
+        if args.act_order:
+            G.gptq_quantize_layer_perm(Wd, U, lam, perm, spec.bits, spec.group_size, spec.block_size,
+                                       codes, scales, zeros, g_idx, err, ws=ws_q, stream=stream)
+        else:
+            G.gptq_quantize_layer(Wd, U, lam, spec.bits, spec.group_size, spec.block_size, codes,
+                                  scales, zeros, err, ws=ws_q, stream=stream)
+    G.gptq_launch_timing(False)
+    p_ms, p_n, p_bytes = G.gptq_launch_timing_read(G.TIMING_PANEL)
+    g_ms, g_n, g_flop = G.gptq_launch_timing_read(G.TIMING_PRODUCT)
+    panel_gbs = p_bytes / (p_ms / 1e3) / 1e9
+    gemm_tfs = g_flop / (g_ms / 1e3) / 1e12
+    log(f"bench: panel {p_n // 3} launches/layer, {p_ms / p_n * 1e3:.2f} us each, {panel_gbs:.1f} GB/s; "
+        f"out-of-block product {g_n // 3} launches/layer, {g_ms / g_n * 1e3:.2f} us each, {gemm_tfs:.2f} TFLOP/s")
+
+    def _traffic(path):
+        try:
+            with open(path) as f:
+                return json.load(f).get("hbm_bytes_per_launch")
+        except Exception:
+            return None
+
+    roof_panel = {"bound": "hbm", "kernel": "panel_kernel (in-block column loop, a7)",
+                  "achieved": round(panel_gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                  "frac": round(panel_gbs / PEAK_HBM_GBS, 4),
+                  "bytes_per_launch": round(p_bytes / p_n), "us_per_launch": round(p_ms / p_n * 1e3, 3),
+                  "launches_per_layer": p_n // 3,
+                  "traffic": _traffic(os.path.join(ROOT, "profiles", "panel_attn4096_traffic.json"))}
+    roof_gemm = {"bound": "mfma", "kernel": "out-of-block product launches (trail_dma_kernel, a8)",
+                 "achieved": round(gemm_tfs, 2), "peak": PEAK_F32_MFMA_TFLOPS, "unit": "TFLOP/s",
+                 "frac": round(gemm_tfs / PEAK_F32_MFMA_TFLOPS, 4),
+                 "flop_per_layer": g_flop / 3, "a8_flop_per_layer": float(flops_gemm),
+                 "us_per_launch": round(g_ms / g_n * 1e3, 3), "launches_per_layer": g_n // 3,
+                 "traffic": _traffic(os.path.join(ROOT, "profiles", "trail_attn4096_traffic.json"))}
+
     traffic = None
     if args.traffic and os.path.exists(args.traffic):
         try:
@@ -806,14 +850,18 @@ def main():
             "hessian_ms": round(t_h * 1e3, 4), "hessian_tflops": round(flops_h / t_h / 1e12, 2),
             "factor_ms": round(t_f * 1e3, 4), "factor_tflops": round(flops_f / t_f / 1e12, 3),
             "quantize_ms": round(t_q * 1e3, 4),
-            "quantize_trailing_gemm_tflops_if_whole_stage": round(flops_gemm / t_q / 1e12, 2),
             "err": float(err.item()),
         },
         "roofline": roof,
+        "roofline_panel": roof_panel,
+        "roofline_gemm": roof_gemm,
     }
     if not args.no_cpu_baseline:
-        log("bench: timing the fp64 oracle on a bounded sample (CPU)")
-        cb = cpu_baseline(spec, W, x0, args.act_order)
+        log("bench: timing the fp64 oracle on the whole layer (CPU)")
+        del Xd
+        torch.cuda.empty_cache()
+        cb = cpu_baseline(spec, W, x_host, args.act_order)
+        cb["err_rel_to_gpu"] = round(abs(cb["err"] - float(err.item())) / cb["err"], 6)
         out["cpu_baseline"] = cb
         out["gpu_speedup_vs_cpu_oracle"] = round(cb["value"] / per_step, 1)
     print(json.dumps(out), flush=True)

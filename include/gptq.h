@@ -311,6 +311,30 @@ gptq_status gptq2d_quantize(const void* X, int32_t x_dtype, int64_t m, int64_t n
                             const float* U_P, int32_t bits, uint8_t* codes, int64_t ld_codes, float* scale,
                             int32_t* zero, double* out_err, void* ws, size_t ws_bytes, void* stream);
 
+/*
+ * Per-launch timing of the quantization loop -- a measurement aid, off by
+ * default.  gptq_launch_timing(1) switches it on for the calling host thread:
+ * every later gptq_quantize_layer / _perm / _noalloc call made from that
+ * thread brackets each of its in-block panel launches (kind 0) and each
+ * out-of-block product launch (kind 1) with a pair of HIP events recorded on
+ * the call's stream (so it also times any gaps the stream has between them),
+ * and notes the launch's algorithmic work.  gptq_launch_timing(0) switches it
+ * off; events already recorded stay readable.
+ *
+ * gptq_launch_timing_read(kind, ms, launches, work) waits for the recorded
+ * events of that kind, returns [host] their summed duration in milliseconds,
+ * the number of launches and their summed work, and forgets them.  Work of a
+ * panel launch (kind 0): the bytes the block's step must move at least --
+ * W block read (4 d_row w), its scaled errors E written (4 d_row w), codes
+ * written (d_row w), U's diagonal block read (4 w^2) and the grid parameters of
+ * groups starting in the block written (8 d_row per group), w the block width.
+ * Work of a product launch (kind 1): 2 M N K flop.  Uses HIP events, created on
+ * first use and kept per thread for reuse; not for the no-allocation path's
+ * callers that forbid event creation.
+ */
+gptq_status gptq_launch_timing(int32_t enable);
+gptq_status gptq_launch_timing_read(int32_t kind, double* ms, int64_t* launches, double* work);
+
 /* [host] static description of a status code; never NULL. */
 const char* gptq_status_string(int32_t status);
 /* [host] library version string, e.g. "gptq-gfx950 0.1.0". */

@@ -27,12 +27,14 @@ __all__ = [
     "gptq_act_order_perm", "gptq_prepare_hinv_perm", "gptq_quantize_layer_perm",
     "gptq_packed_words_per_row", "gptq_pack_codes", "gptq_dequant_matmul", "gptq_dequantize",
     "gptq2d_quantize", "gptq2d_quantize_workspace_size",
+    "gptq_launch_timing", "gptq_launch_timing_read", "TIMING_PANEL", "TIMING_PRODUCT",
     "gptq_status_string", "gptq_version", "quantize_layer",
 ]
 
 GPTQ_F32 = 0
 GPTQ_F16 = 1
 GPTQ_NOALLOC_SCRATCH_BYTES = 96 << 20   # include/gptq.h
+TIMING_PANEL, TIMING_PRODUCT = 0, 1     # kinds of gptq_launch_timing_read
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB = None
@@ -104,6 +106,11 @@ def library() -> ctypes.CDLL:
     lib.gptq2d_quantize.restype = i32
     lib.gptq_dequantize.argtypes = [vp, i64, i64, i64, vp, vp, i64, vp, vp, i32, i64, vp]
     lib.gptq_dequantize.restype = i32
+    lib.gptq_launch_timing.argtypes = [i32]
+    lib.gptq_launch_timing.restype = i32
+    lib.gptq_launch_timing_read.argtypes = [i32, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(i64),
+                                            ctypes.POINTER(ctypes.c_double)]
+    lib.gptq_launch_timing_read.restype = i32
     lib.gptq_status_string.argtypes = [i32]
     lib.gptq_status_string.restype = ctypes.c_char_p
     lib.gptq_version.argtypes = []
@@ -407,6 +414,22 @@ def gptq_dequant_matmul(packed, bits: int, scales, zeros, group_size: int, X, d_
                                        Y.stride(0), _stream(stream, packed, scales, zeros, perm, X, Y))
     _check(st, "gptq_dequant_matmul")
     return Y
+
+
+def gptq_launch_timing(enable: bool) -> None:
+    """Switch per-launch timing of the loop's panel and product launches on or
+    off for the calling thread (a measurement aid)."""
+    _check(library().gptq_launch_timing(1 if enable else 0), "gptq_launch_timing")
+
+
+def gptq_launch_timing_read(kind: int):
+    """(milliseconds, launches, work) summed over the recorded launches of
+    ``kind`` (TIMING_PANEL: work in bytes; TIMING_PRODUCT: work in flop), which
+    are then forgotten.  Waits for the recorded events."""
+    ms, n, work = ctypes.c_double(), ctypes.c_int64(), ctypes.c_double()
+    _check(library().gptq_launch_timing_read(int(kind), ctypes.byref(ms), ctypes.byref(n), ctypes.byref(work)),
+           "gptq_launch_timing_read")
+    return ms.value, n.value, work.value
 
 
 def quantize_layer(W0, x_chunks: Iterable, bits: int = 4, group_size: int = 0,

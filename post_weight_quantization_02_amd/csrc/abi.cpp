@@ -4,6 +4,7 @@
 #include "gptq.h"
 
 #include <cmath>
+#include <vector>
 
 #include "gptq_internal.h"
 
@@ -25,6 +26,67 @@ gptq_status ws_check(const void* ws, size_t have, size_t need) {
 gptq_status from_hip(hipError_t e) { return e == hipSuccess ? GPTQ_OK : GPTQ_ERR_LAUNCH; }
 
 }  // namespace
+
+// ---------------------------------------------------------------- per-launch timing
+namespace gptq {
+
+struct LaunchTimer {
+  struct Rec {
+    int kind;
+    double work;
+    hipEvent_t a, b;
+  };
+  bool on = false;
+  hipEvent_t open = nullptr;          // begin event of the launch being bracketed
+  std::vector<Rec> recs;
+  std::vector<hipEvent_t> pool;       // events of earlier reads, reused
+
+  hipError_t take(hipEvent_t* e) {
+    if (!pool.empty()) {
+      *e = pool.back();
+      pool.pop_back();
+      return hipSuccess;
+    }
+    return hipEventCreate(e);
+  }
+  ~LaunchTimer() {
+    for (auto& r : recs) {
+      (void)hipEventDestroy(r.a);
+      (void)hipEventDestroy(r.b);
+    }
+    for (auto e : pool) (void)hipEventDestroy(e);
+    if (open) (void)hipEventDestroy(open);
+  }
+};
+
+static LaunchTimer& thread_timer() {
+  thread_local LaunchTimer t;
+  return t;
+}
+
+LaunchTimer* launch_timer() {
+  LaunchTimer& t = thread_timer();
+  return t.on ? &t : nullptr;
+}
+
+hipError_t timer_begin(LaunchTimer* t, hipStream_t s) {
+  if (!t) return hipSuccess;
+  hipError_t e = t->open ? hipSuccess : t->take(&t->open);
+  return e == hipSuccess ? hipEventRecord(t->open, s) : e;
+}
+
+hipError_t timer_end(LaunchTimer* t, int kind, double work, hipStream_t s) {
+  if (!t || !t->open) return hipSuccess;
+  hipEvent_t b = nullptr;
+  hipError_t e = t->take(&b);
+  if (e == hipSuccess) e = hipEventRecord(b, s);
+  if (e != hipSuccess) return e;
+  t->recs.push_back({kind, work, t->open, b});
+  t->open = nullptr;
+  return hipSuccess;
+}
+
+}  // namespace gptq
 
 extern "C" {
 
@@ -234,6 +296,37 @@ gptq_status gptq_dequant_matmul(const uint32_t* packed, int64_t ld_packed, int32
   return from_hip(gptq::dequant_matmul_launch(packed, ld_packed, bits, scales, zeros, group_size, perm,
                                               d_row, d_col, X, x_dtype, (int)m, ld_x, Y, ld_y,
                                               (hipStream_t)stream));
+}
+
+gptq_status gptq_launch_timing(int32_t enable) {
+  gptq::thread_timer().on = enable != 0;
+  return GPTQ_OK;
+}
+
+gptq_status gptq_launch_timing_read(int32_t kind, double* ms, int64_t* launches, double* work) {
+  if (ms == nullptr || launches == nullptr || work == nullptr) return GPTQ_ERR_NULL_POINTER;
+  if (kind < 0 || kind >= gptq::kTimeKinds) return GPTQ_ERR_BAD_SIZE;
+  gptq::LaunchTimer& t = gptq::thread_timer();
+  *ms = 0.0;
+  *launches = 0;
+  *work = 0.0;
+  std::vector<gptq::LaunchTimer::Rec> keep;
+  for (auto& r : t.recs) {
+    if (r.kind != kind) {
+      keep.push_back(r);
+      continue;
+    }
+    float dt = 0.f;
+    if (hipEventSynchronize(r.b) != hipSuccess || hipEventElapsedTime(&dt, r.a, r.b) != hipSuccess)
+      return GPTQ_ERR_LAUNCH;
+    *ms += dt;
+    *launches += 1;
+    *work += r.work;
+    t.pool.push_back(r.a);
+    t.pool.push_back(r.b);
+  }
+  t.recs.swap(keep);
+  return GPTQ_OK;
 }
 
 const char* gptq_status_string(int32_t status) {

@@ -97,6 +97,18 @@ hipError_t quant_launch(const QuantPlan& p, const void* W0, int w_dtype, int64_t
                         int64_t group, uint8_t* codes, float* scales, int32_t* zeros,
                         int32_t* g_idx, double* out_err, void* ws, hipStream_t s);
 
+// ---------------------------------------------------------------- per-launch timing
+// A measurement aid, off by default: when switched on for the calling host
+// thread, the loop brackets each in-block panel launch (kind 0) and each
+// out-of-block product launch (kind 1) with a pair of HIP events recorded on
+// the call's stream, and notes the launch's algorithmic work (bytes for the
+// panel, flop for the product).
+enum { kTimePanel = 0, kTimeTrail = 1, kTimeKinds = 2 };
+struct LaunchTimer;
+LaunchTimer* launch_timer();   // the calling thread's timer, or nullptr when off
+hipError_t timer_begin(LaunchTimer* t, hipStream_t s);
+hipError_t timer_end(LaunchTimer* t, int kind, double work, hipStream_t s);
+
 // The no-allocation entry point's workspace: a device array of this many bytes
 // (one per device), and its address on the current device (looked up once per
 // device, then kept).

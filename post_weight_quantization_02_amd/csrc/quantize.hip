@@ -641,6 +641,7 @@ hipError_t quant_launch(const QuantPlan& p, const void* W0, int w_dtype, int64_t
   const bool quad = base_ok && p.pair == 2 && (group == 0 || group <= 2 * B || group % (4 * B) == 0);
   const bool pair2 = base_ok && p.pair == 2 && !quad && (group <= B || group % (2 * B) == 0);
   const int nb = quad ? 4 : (fused || pair2) ? 2 : 1;
+  LaunchTimer* timer = launch_timer();
   for (int64_t i1 = 0, blk = 0; i1 < d_col; i1 += B, ++blk) {
     const int width = (int)std::min<int64_t>(B, d_col - i1);
     const int r = (int)(blk % nb);  // position in the group
@@ -656,6 +657,7 @@ hipError_t quant_launch(const QuantPlan& p, const void* W0, int w_dtype, int64_t
     const int gin = (group > 0 && group <= B) ? (int)group : 0;
     const int gwide = (group > B) ? (int)group : 0;
     const int ng = (int)ngroups;
+    if ((e = timer_begin(timer, s)) != hipSuccess) return e;
     switch (B) {
       case 16: e = launch_panel<1>(gin, full, pg, s, W, (int)d_row, (int)d_col, (int)i1, width, U,
                                    maxq, gwide, ng, cpos, scales, zeros, Eb, part_e, Ep); break;
@@ -667,6 +669,13 @@ hipError_t quant_launch(const QuantPlan& p, const void* W0, int w_dtype, int64_t
                                    maxq, gwide, ng, cpos, scales, zeros, Eb, part_e, Ep); break;
     }
     if (e != hipSuccess) return e;
+    if (timer) {
+      // algorithmic bytes of the block's step: W block in, E and codes out, U's
+      // diagonal block, the grid parameters of the groups that start here
+      const int64_t gstarts = group ? (int64_t)(cdiv(i1 + width, group) - cdiv(i1, group)) : 0;
+      const double bytes = 9.0 * (double)d_row * width + 4.0 * width * width + 8.0 * (double)d_row * gstarts;
+      if ((e = timer_end(timer, kTimePanel, bytes, s)) != hipSuccess) return e;
+    }
     const int64_t i2 = i1 + width;
     if (i2 < d_col) {
       int64_t ncols = 0, krows = 0, urow = 0;
@@ -686,9 +695,11 @@ hipError_t quant_launch(const QuantPlan& p, const void* W0, int w_dtype, int64_t
         Et = Eb;
       }
       if (ncols > 0) {
+        if ((e = timer_begin(timer, s)) != hipSuccess) return e;
         e = trail_update_launch(W + i2, d_col, (int)d_row, (int)ncols, (int)krows, Et, d_row,
                                 U + urow * d_col + i2, d_col, s);
         if (e != hipSuccess) return e;
+        if ((e = timer_end(timer, kTimeTrail, 2.0 * (double)d_row * ncols * krows, s)) != hipSuccess) return e;
       }
     }
   }

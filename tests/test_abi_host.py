@@ -237,3 +237,14 @@ def test_noalloc_validation_and_scratch_limit():
     assert f(FAKE, 1, 4096, 8192, 8192, FAKE, FAKE, 4, 128, 128, FAKE, FAKE, FAKE, FAKE, None) == \
         _status("GPTQ_ERR_SCRATCH")
     assert "no-allocation" in G.gptq_status_string(12)
+
+
+def test_launch_timing_host_side():
+    G.gptq_launch_timing(True)
+    assert G.gptq_launch_timing_read(G.TIMING_PANEL) == (0.0, 0, 0.0)   # nothing recorded yet
+    G.gptq_launch_timing(False)
+    f = G.library().gptq_launch_timing_read
+    import ctypes
+    ms, n, w = ctypes.c_double(), ctypes.c_int64(), ctypes.c_double()
+    assert f(7, ctypes.byref(ms), ctypes.byref(n), ctypes.byref(w)) == _status("GPTQ_ERR_BAD_SIZE")
+    assert f(0, None, ctypes.byref(n), ctypes.byref(w)) == _status("GPTQ_ERR_NULL_POINTER")

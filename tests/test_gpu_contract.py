@@ -86,3 +86,27 @@ def test_pipeline_leaves_weights_untouched_when_a_factor_fails():
     for b, ref in zip(blocks, before):
         for n, p in b.named_parameters():
             assert torch.equal(p, ref[n]), n
+
+
+def test_launch_timing_counts_every_panel_and_product_launch():
+    W, X = _case(256, 640, 2048, 9)
+    H = torch.zeros(640, 640, device="cuda")
+    G.gptq_hessian_accumulate(H, X)
+    U, lam, info = G.gptq_prepare_hinv(H, 0.01)
+    G.gptq_launch_timing(True)
+    try:
+        ref = G.gptq_quantize_layer(W, U, lam, 4, 32, 128)
+    finally:
+        G.gptq_launch_timing(False)
+    ms, n, work = G.gptq_launch_timing_read(G.TIMING_PANEL)
+    assert n == 5 and ms > 0.0                      # 640 columns in blocks of 128
+    # 9 bytes per weight (W in, E out, code out), U's diagonal blocks, 8 bytes per group start
+    assert work == 9.0 * 256 * 640 + 4.0 * 128 * 128 * 5 + 8.0 * 256 * (640 // 32)
+    gms, gn, gflop = G.gptq_launch_timing_read(G.TIMING_PRODUCT)
+    assert gn >= 2 and gms > 0.0 and gflop > 0.0
+    assert G.gptq_launch_timing_read(G.TIMING_PANEL) == (0.0, 0, 0.0)   # read once
+    # timing changes nothing in the results
+    again = G.gptq_quantize_layer(W, U, lam, 4, 32, 128)
+    torch.cuda.synchronize()
+    for a, b in zip(ref, again):
+        assert torch.equal(a, b)
