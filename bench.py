@@ -72,6 +72,48 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
+def _traffic(path):
+    """HBM bytes per launch from a committed rocprofv3 counter summary, if any."""
+    try:
+        with open(path) as f:
+            return json.load(f).get("hbm_bytes_per_launch")
+    except Exception:
+        return None
+
+
+def loop_rooflines(G, run_once, reps, a8_flop, tag):
+    """A separate pass over the quantization loop with every panel launch and every
+    out-of-block product launch bracketed by HIP events on the library's stream:
+    the panel's algorithmic bytes per second against the HBM peak, the products'
+    flop per second against the fp32 matrix peak."""
+    G.gptq_launch_timing(True)
+    try:
+        for _ in range(reps):
+            run_once()
+    finally:
+        G.gptq_launch_timing(False)
+    p_ms, p_n, p_bytes = G.gptq_launch_timing_read(G.TIMING_PANEL)
+    g_ms, g_n, g_flop = G.gptq_launch_timing_read(G.TIMING_PRODUCT)
+    panel_gbs = p_bytes / (p_ms / 1e3) / 1e9
+    gemm_tfs = g_flop / (g_ms / 1e3) / 1e12
+    log(f"bench: panel {p_n // reps} launches/layer, {p_ms / p_n * 1e3:.2f} us each, {panel_gbs:.1f} GB/s; "
+        f"out-of-block product {g_n // reps} launches/layer, {g_ms / g_n * 1e3:.2f} us each, "
+        f"{gemm_tfs:.2f} TFLOP/s")
+    roof_panel = {"bound": "hbm", "kernel": "in-block panel launches (a7)",
+                  "achieved": round(panel_gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                  "frac": round(panel_gbs / PEAK_HBM_GBS, 4),
+                  "bytes_per_launch": round(p_bytes / p_n), "us_per_launch": round(p_ms / p_n * 1e3, 3),
+                  "launches_per_layer": p_n // reps,
+                  "traffic": _traffic(os.path.join(ROOT, "profiles", f"panel_{tag}_traffic.json"))}
+    roof_gemm = {"bound": "mfma", "kernel": "out-of-block product launches (trail_dma_kernel, a8)",
+                 "achieved": round(gemm_tfs, 2), "peak": PEAK_F32_MFMA_TFLOPS, "unit": "TFLOP/s",
+                 "frac": round(gemm_tfs / PEAK_F32_MFMA_TFLOPS, 4),
+                 "flop_per_layer": g_flop / reps, "a8_flop_per_layer": float(a8_flop),
+                 "us_per_launch": round(g_ms / g_n * 1e3, 3), "launches_per_layer": g_n // reps,
+                 "traffic": _traffic(os.path.join(ROOT, "profiles", f"trail_{tag}_traffic.json"))}
+    return roof_panel, roof_gemm
+
+
 def _blas_threads():
     try:
         from threadpoolctl import threadpool_info
@@ -549,6 +591,7 @@ def loop_ffn_bench(args):
     flops_gemm = dr * d * (d - spec.block_size)     # sum over blocks of 2 * d_row * B * (d - i2)
     ach = flops_gemm / t / 1e12
     log(f"bench: lazy-batch loop {t * 1e3:.2f} ms at {dr}x{d}; factor {t_factor * 1e3:.2f} ms")
+    roof_panel, roof_gemm = loop_rooflines(G, step, 1, flops_gemm, "ffn49152")
     out = {
         "metric": "lazy-batch loop s/layer (175B-class FFN W_fc 49152x12288, 3-bit g128)",
         "value": round(t, 6),
@@ -568,10 +611,8 @@ def loop_ffn_bench(args):
                    "block_size": spec.block_size, "parallelism": "single-gpu"},
         "stages": {"factor_ms": round(t_factor * 1e3, 3), "err": float(err.item()),
                    "trailing_gemm_tflop": round(flops_gemm / 1e12, 3)},
-        # the whole loop's time stands in for the correction's own: a lower bound on its rate
-        "roofline": {"bound": "mfma", "kernel": "trail_dma_kernel (whole-loop time, a lower bound on its rate)",
-                     "achieved": round(ach, 2), "peak": 157.3, "unit": "TFLOP/s",
-                     "frac": round(ach / 157.3, 4), "traffic": None},
+        "roofline": roof_gemm,
+        "roofline_panel": roof_panel,
         "cpu_baseline": None,
     }
     print(json.dumps(out), flush=True)
@@ -775,43 +816,15 @@ def main():
     log(f"bench: stages ms hessian {t_h * 1e3:.3f} factor {t_f * 1e3:.3f} quantize {t_q * 1e3:.3f}; "
         f"wall/step {per_step * 1e3:.3f} ms; err {float(err.item()):.6g}")
 
-    # Separate pass: the loop's panel and out-of-block product launches, each
-    # bracketed by HIP events on the library's stream (the same step's U).
-    G.gptq_launch_timing(True)
-    for _ in range(3):
+    def quantize_once():
         if args.act_order:
             G.gptq_quantize_layer_perm(Wd, U, lam, perm, spec.bits, spec.group_size, spec.block_size,
                                        codes, scales, zeros, g_idx, err, ws=ws_q, stream=stream)
         else:
             G.gptq_quantize_layer(Wd, U, lam, spec.bits, spec.group_size, spec.block_size, codes,
                                   scales, zeros, err, ws=ws_q, stream=stream)
-    G.gptq_launch_timing(False)
-    p_ms, p_n, p_bytes = G.gptq_launch_timing_read(G.TIMING_PANEL)
-    g_ms, g_n, g_flop = G.gptq_launch_timing_read(G.TIMING_PRODUCT)
-    panel_gbs = p_bytes / (p_ms / 1e3) / 1e9
-    gemm_tfs = g_flop / (g_ms / 1e3) / 1e12
-    log(f"bench: panel {p_n // 3} launches/layer, {p_ms / p_n * 1e3:.2f} us each, {panel_gbs:.1f} GB/s; "
-        f"out-of-block product {g_n // 3} launches/layer, {g_ms / g_n * 1e3:.2f} us each, {gemm_tfs:.2f} TFLOP/s")
 
-    def _traffic(path):
-        try:
-            with open(path) as f:
-                return json.load(f).get("hbm_bytes_per_launch")
-        except Exception:
-            return None
-
-    roof_panel = {"bound": "hbm", "kernel": "panel_kernel (in-block column loop, a7)",
-                  "achieved": round(panel_gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                  "frac": round(panel_gbs / PEAK_HBM_GBS, 4),
-                  "bytes_per_launch": round(p_bytes / p_n), "us_per_launch": round(p_ms / p_n * 1e3, 3),
-                  "launches_per_layer": p_n // 3,
-                  "traffic": _traffic(os.path.join(ROOT, "profiles", "panel_attn4096_traffic.json"))}
-    roof_gemm = {"bound": "mfma", "kernel": "out-of-block product launches (trail_dma_kernel, a8)",
-                 "achieved": round(gemm_tfs, 2), "peak": PEAK_F32_MFMA_TFLOPS, "unit": "TFLOP/s",
-                 "frac": round(gemm_tfs / PEAK_F32_MFMA_TFLOPS, 4),
-                 "flop_per_layer": g_flop / 3, "a8_flop_per_layer": float(flops_gemm),
-                 "us_per_launch": round(g_ms / g_n * 1e3, 3), "launches_per_layer": g_n // 3,
-                 "traffic": _traffic(os.path.join(ROOT, "profiles", "trail_attn4096_traffic.json"))}
+    roof_panel, roof_gemm = loop_rooflines(G, quantize_once, 3, flops_gemm, "attn4096")
 
     traffic = None
     if args.traffic and os.path.exists(args.traffic):

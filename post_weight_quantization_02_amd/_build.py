@@ -19,7 +19,8 @@ BUILD = os.path.join(ROOT, "_build")
 LIBDIR = os.path.join(HERE, "_lib")
 LIB = os.path.join(LIBDIR, "libgptq.so")
 
-SOURCES = ["abi.cpp", "hessian.hip", "factor.hip", "gemm.hip", "quantize.hip", "packed.hip", "gptq2d.hip"]
+SOURCES = ["panel_row_group.hip", "panel_row_grid.hip", "abi.cpp", "hessian.hip", "factor.hip", "gemm.hip",
+           "quantize.hip", "packed.hip", "gptq2d.hip"]
 ARCH = "gfx950"
 FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",

@@ -115,6 +115,16 @@ hipError_t timer_end(LaunchTimer* t, int kind, double work, hipStream_t s);
 constexpr size_t kNoAllocScratchBytes = size_t(96) << 20;
 hipError_t noalloc_scratch(void** out);
 
+// The one-row-per-lane panel for full blocks of 128 columns (layers with many
+// rows): one grid per row (or per group wider than the block), or one group per
+// block.  grid.x * block.x >= d_row, block.x a multiple of 64 up to 256.
+hipError_t row_panel_launch_grid(dim3 grid, dim3 block, hipStream_t s, float* W, int d_row, int d_col, int i1,
+                                 const float* U, int maxq, int gwide, int ngroups, uint8_t* codes,
+                                 float* scales, int32_t* zeros, float* E, double* part_e);
+hipError_t row_panel_launch_group(dim3 grid, dim3 block, hipStream_t s, float* W, int d_row, int d_col, int i1,
+                                  const float* U, int maxq, int gwide, int ngroups, uint8_t* codes,
+                                  float* scales, int32_t* zeros, float* E, double* part_e);
+
 // W[:, i+B:] -= E U[i:i+B, i+B:] with E given transposed: C [M x N] (ldc) -=
 // Et^T [M x K] * Ub [K x N]; Et is [K x M] (lde), Ub [K x N] (ldu); K <= 128.
 hipError_t trail_update_launch(float* C, int64_t ldc, int M, int N, int K, const float* Et,

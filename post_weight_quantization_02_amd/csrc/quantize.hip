@@ -543,6 +543,10 @@ __global__ __launch_bounds__(kThreads) void g_idx_kernel(const int32_t* __restri
 }
 
 constexpr int64_t kErrWGs = 1024;
+#ifndef GPTQ_ROW_PANEL_MIN_ROWS
+#define GPTQ_ROW_PANEL_MIN_ROWS 32768
+#endif
+constexpr int64_t kRowPanelMinRows = GPTQ_ROW_PANEL_MIN_ROWS;
 
 }  // namespace
 
@@ -642,6 +646,9 @@ hipError_t quant_launch(const QuantPlan& p, const void* W0, int w_dtype, int64_t
   const bool pair2 = base_ok && p.pair == 2 && !quad && (group <= B || group % (2 * B) == 0);
   const int nb = quad ? 4 : (fused || pair2) ? 2 : 1;
   LaunchTimer* timer = launch_timer();
+  // enough rows for one row per lane to fill the chip (and no in-panel share)
+  const bool row_panel = B == 128 && d_row >= kRowPanelMinRows && d_col % 4 == 0 &&
+                         ((uintptr_t)U & 15) == 0;
   for (int64_t i1 = 0, blk = 0; i1 < d_col; i1 += B, ++blk) {
     const int width = (int)std::min<int64_t>(B, d_col - i1);
     const int r = (int)(blk % nb);  // position in the group
@@ -658,7 +665,15 @@ hipError_t quant_launch(const QuantPlan& p, const void* W0, int w_dtype, int64_t
     const int gwide = (group > B) ? (int)group : 0;
     const int ng = (int)ngroups;
     if ((e = timer_begin(timer, s)) != hipSuccess) return e;
-    switch (B) {
+    if (row_panel && !Ep && full && (gin == 0 || gin == B)) {
+      // one row per lane: 64 to 256 rows per work-group, sized so that the
+      // work-groups cover the CUs about once
+      const int64_t waves = cdiv(d_row, 64);
+      const int nw = (int)std::min<int64_t>(4, std::max<int64_t>(1, cdiv(waves, 256)));
+      const dim3 rg((unsigned)cdiv(d_row, 64 * nw)), rb((unsigned)(64 * nw));
+      e = (gin == B ? row_panel_launch_group : row_panel_launch_grid)(
+          rg, rb, s, W, (int)d_row, (int)d_col, (int)i1, U, maxq, gwide, ng, cpos, scales, zeros, Eb, part_e);
+    } else switch (B) {
       case 16: e = launch_panel<1>(gin, full, pg, s, W, (int)d_row, (int)d_col, (int)i1, width, U,
                                    maxq, gwide, ng, cpos, scales, zeros, Eb, part_e, Ep); break;
       case 32: e = launch_panel<2>(gin, full, pg, s, W, (int)d_row, (int)d_col, (int)i1, width, U,

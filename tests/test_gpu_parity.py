@@ -206,6 +206,21 @@ Q_CASES = [
                                        O.hessian([case_x("silu", 8192, 512, np.float16, 38)])), 3, 0, 128),
     ("one_row", 11, lambda: (case_w(1, 16, np.float32, 39),
                              O.hessian([case_x("ar1", 100, 16, np.float32, 40)])), 4, 0, 16),
+    # layers with 32768 rows or more take the one-row-per-lane panel for full
+    # blocks of 128 with one grid per row, per block-wide group or per wider
+    # group; a ragged last block and groups inside the block take the other panel
+    ("rows32768_fp16_g128_ragged", 12, lambda: (case_w(32768, 400, np.float16, 41, 0.015),
+                                                O.hessian([case_x("lowrank", 8192, 400, np.float16, 42)])),
+     3, 128, 128),
+    ("rows32800_fp32_perrow", 13, lambda: (case_w(32800, 384, np.float32, 43),
+                                           O.hessian([case_x("ar1", 4000, 384, np.float32, 44)])), 4, 0, 128),
+    ("rows33000_fp16_g256", 14, lambda: (case_w(33000, 512, np.float16, 45, 0.015),
+                                         O.hessian([case_x("powerlaw", 8192, 768, np.float16, 46)[:, :512]])),
+     4, 256, 128),
+    ("rows32768_g64_in_block", 15, lambda: (case_w(32768, 256, np.float32, 47),
+                                            O.hessian([case_x("ar1", 3000, 256, np.float32, 48)])), 3, 64, 128),
+    ("rows8192_fp16_g128", 16, lambda: (case_w(8192, 384, np.float16, 49, 0.015),
+                                        O.hessian([case_x("lowrank", 8192, 384, np.float16, 50)])), 4, 128, 128),
 ]
 
 
