@@ -16,12 +16,16 @@
 // fp32 (MFMA), whose error stays ~1e-6.
 //
 // Kernels: damp (lambda, info = 0) -> reversed fp64 copy with lambda on the
-// diagonal -> one launch per 64-column block (blocked right-looking Cholesky
-// with look-ahead; each diagonal block's inverse comes out of its
-// factorization); past 96 blocks the trailing updates of each step are confined
-// to its group of eight blocks (512 columns), with one rank-512 update of the
-// rest of the matrix after each group -> recursive-doubling triangular inverse,
-// two batched fp32 MFMA products per level -> reversed write of U.
+// diagonal -> one launch per 64-column block (blocked Cholesky with look-ahead;
+// each diagonal block's inverse comes out of its factorization).  Up to 16
+// blocks every step updates the whole trailing triangle.  From 17 to 96 blocks
+// a block column receives the updates of all earlier steps late, two launches
+// before its own factorization, as split-K partial products that the next
+// launch folds in, so every launch carries about the same update work; past 96
+// blocks the trailing updates of each step are confined to its group of eight
+// blocks (512 columns), with one rank-512 update of the rest of the matrix
+// after each group -> recursive-doubling triangular inverse, two batched fp32
+// MFMA products per level -> reversed write of U.
 #include "gptq_internal.h"
 
 namespace gptq {
@@ -93,17 +97,38 @@ __global__ __launch_bounds__(kThreads) void rev_copy_kernel(const float* __restr
 //      (each P work-group redundantly), and solve its own tile:
 //      L[r][c] = T Lcc^-T.  The r == c work-group writes Lcc^-1 as the
 //      diagonal block of L^-1 (Lcc itself is never needed again).
+// and either (deferred updates, 17 to 96 blocks)
+//   RED (tiles (i, k+2), i >= k+2): A[i][k+2] -= (the partial products of steps
+//      0 .. k-1 that the previous launch left, chunk by chunk) + L[i][k] L[k+2][k]^T,
+//      which brings block column k+2 up to date for the next launch's P;
+//   DEF (tiles (i, k+3), i >= k+3, one chunk of kDefSteps steps each): the
+//      partial product  sum_{s in chunk} L[i][s] L[k+3][s]^T  of steps 0 .. k,
+//      into this launch's half of a double buffer;
+// block column j thus receives steps 0 .. j-3 as DEF products in launch j-3,
+// folds them in with step j-2 in launch j-2 (RED), and takes step j-1 in the
+// P work-groups of launch j-1.  No tile is written by two work-groups of one
+// launch, and every launch's update work is about (rows left) x (steps done).
+// or (right-looking updates: one group spanning the matrix up to 16 blocks,
+// groups of eight blocks past 96)
 //   UC (tiles (i, j), i >= j >= k+2, j < jend): A[i][j] -= L[i][k] L[j][k]^T
 //      (fp64 MFMA); jend is the end of the step's column group, whose steps
 //      reach the block columns past it in one rank-512 update instead.  The
 //      first launch of a group (skip_step) finds step k already applied.
 // ---------------------------------------------------------------------------
+constexpr int kDefSteps = 4;        // steps per deferred partial product (K = 256)
+constexpr int kDeferMinBlocks = 17;  // deferred updates from 17 to 96 blocks (1025 .. 6144 columns)
+constexpr int kDeferMaxBlocks = 96;
+inline bool deferred_updates(int64_t nblk) { return nblk >= kDeferMinBlocks && nblk <= kDeferMaxBlocks; }
+
 struct StepArgs {
   double* A;
   float* Linv;
   int32_t* info;
   int d, nblk, k;
-  int np, nuc;
+  int np, nuc, nred, ndef;
+  int red_chunks;        // partial products RED folds in (chunks of the previous launch)
+  const double* part_r;  // the previous launch's partial products
+  double* part_w;        // this launch's
   int jend;       // update tiles only in block columns < jend
   int skip_step;  // step k already applied (by the column group's rank-512 update)
 };
@@ -365,6 +390,64 @@ __device__ __forceinline__ void ldl_stacked(double* S0, double* S1, double* dv, 
   });
 }
 
+// ---------------------------------------------------------------------------
+// acc (this wave's 32x32 quadrant of a 64x64 tile) +=
+//   A[R0 .. R0+63][K0 .. K0+nk) A[C0 .. C0+63][K0 .. K0+nk)^T   (fp64 MFMA),
+// rows past d read as zeros.  K is staged kGK columns at a time through S0 and
+// S1 ([64][kGP] each, few registers live), the next stage loading into
+// registers under the current products.  nk is a multiple of kGK; the LDS is
+// free again on return.
+// ---------------------------------------------------------------------------
+constexpr int kGK = 32;       // K columns per stage
+constexpr int kGP = kGK + 1;  // LDS pitch (doubles) of the [row][k] stages
+
+__device__ __forceinline__ void mma_nt_stream(const double* __restrict__ A, int64_t d, int64_t R0, int64_t C0,
+                                              int64_t K0, int nk, double* S0, double* S1, f64x4 (&acc)[2][2],
+                                              int t) {
+  const int lane = t & 63, w = t >> 6, wm = w & 1, wn = w >> 1;
+  // staging: thread t covers row t / 4 of a [64][32] stage, columns 8 (t % 4) .. + 7
+  const int sr = t >> 2, sc = 8 * (t & 3);
+  double va[8], vb[8];
+  auto gload = [&](double (&v)[8], int64_t row0, int64_t k0) {
+    const int64_t row = row0 + sr;
+    const bool ok = row < d;
+    const double* src = A + (ok ? row : 0) * d + k0 + sc;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) v[e] = ok ? src[e] : 0.0;
+  };
+  gload(va, R0, K0);
+  gload(vb, C0, K0);
+  const int nst = nk / kGK;
+  for (int st = 0; st < nst; ++st) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      S0[sr * kGP + sc + e] = va[e];
+      S1[sr * kGP + sc + e] = vb[e];
+    }
+    __syncthreads();
+    if (st + 1 < nst) {
+      gload(va, R0, K0 + (int64_t)(st + 1) * kGK);
+      gload(vb, C0, K0 + (int64_t)(st + 1) * kGK);
+    }
+#pragma unroll
+    for (int k4 = 0; k4 < kGK / 4; ++k4) {
+      const int k = 4 * k4 + (lane >> 4);
+      double a[2], bb[2];
+#pragma unroll
+      for (int f = 0; f < 2; ++f) {
+        a[f] = S0[(wm * 32 + f * 16 + (lane & 15)) * kGP + k];
+        bb[f] = S1[(wn * 32 + f * 16 + (lane & 15)) * kGP + k];
+      }
+#pragma unroll
+      for (int fm = 0; fm < 2; ++fm)
+#pragma unroll
+        for (int fn = 0; fn < 2; ++fn)
+          acc[fm][fn] = __builtin_amdgcn_mfma_f64_16x16x4f64(a[fm], bb[fn], acc[fm][fn], 0, 0, 0);
+    }
+    __syncthreads();
+  }
+}
+
 struct PanelSmem {
   double S0[kNB * kP], S1[kNB * kP];
   double dv[kNB], rdv[kNB], sq[kNB], rsq[kNB];
@@ -498,6 +581,71 @@ __device__ __forceinline__ void task_update_chol(const StepArgs a, int b, PanelS
       }
 }
 
+// Partial products keep each thread's 16 accumulator values in MFMA layout:
+// value u of thread t at [u * kThreads + t] of the tile's 4096 doubles.
+__device__ __forceinline__ int64_t part_tile(int chunk, int ntile, int ti) {
+  return ((int64_t)chunk * ntile + ti) * (kNB * kNB);
+}
+
+// RED: tile row i = k+2+b of block column j = k+2
+__device__ __forceinline__ void task_reduce(const StepArgs a, int b, PanelSmem& sm) {
+  const int t = threadIdx.x, lane = t & 63, w = t >> 6, wm = w & 1, wn = w >> 1;
+  const int64_t d = a.d;
+  const int j = a.k + 2, nt = a.nblk - j;
+  const int64_t R0 = (int64_t)(j + b) * kNB, C0 = (int64_t)j * kNB, K0 = (int64_t)a.k * kNB;
+  load_tile_f64(sm.S0, a.A, d, R0, K0, t);
+  load_tile_f64(sm.S1, a.A, d, C0, K0, t);
+  double c[16];
+#pragma unroll
+  for (int fm = 0; fm < 2; ++fm)
+#pragma unroll
+    for (int fn = 0; fn < 2; ++fn)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int64_t row = R0 + nt_row(lane, wm, fm, q), col = C0 + nt_col(lane, wn, fn);
+        c[(fm * 2 + fn) * 4 + q] = (row < d && col <= row) ? a.A[row * d + col] : 0.0;
+      }
+  // the deferred steps, chunk by chunk in step order
+  for (int ch = 0; ch < a.red_chunks; ++ch) {
+    const double* p = a.part_r + part_tile(ch, nt, b);
+#pragma unroll
+    for (int u = 0; u < 16; ++u) c[u] -= p[u * kThreads + t];
+  }
+  __syncthreads();
+  f64x4 acc[2][2];
+  zero_acc(acc);
+  mma_nt_f64(sm.S0, sm.S1, acc, lane, wm, wn);
+#pragma unroll
+  for (int fm = 0; fm < 2; ++fm)
+#pragma unroll
+    for (int fn = 0; fn < 2; ++fn)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int64_t row = R0 + nt_row(lane, wm, fm, q), col = C0 + nt_col(lane, wn, fn);
+        if (row < d && col <= row) a.A[row * d + col] = c[(fm * 2 + fn) * 4 + q] - acc[fm][fn][q];
+      }
+}
+
+// DEF: block column j = k+3; work-group b takes tile row i = j + b % nt and
+// steps [kDefSteps c, kDefSteps (c+1)) of 0 .. k, c = b / nt
+__device__ __forceinline__ void task_deferred(const StepArgs a, int b, PanelSmem& sm) {
+  const int t = threadIdx.x;
+  const int j = a.k + 3, nt = a.nblk - j;
+  const int ch = b / nt, ti = b % nt;
+  const int s0 = ch * kDefSteps, s1 = std::min(s0 + kDefSteps, a.k + 1);
+  f64x4 acc[2][2];
+  zero_acc(acc);
+  mma_nt_stream(a.A, a.d, (int64_t)(j + ti) * kNB, (int64_t)j * kNB, (int64_t)s0 * kNB, (s1 - s0) * kNB, sm.S0,
+                sm.S1, acc, t);
+  double* p = a.part_w + part_tile(ch, nt, ti);
+#pragma unroll
+  for (int fm = 0; fm < 2; ++fm)
+#pragma unroll
+    for (int fn = 0; fn < 2; ++fn)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) p[((fm * 2 + fn) * 4 + q) * kThreads + t] = acc[fm][fn][q];
+}
+
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) void chol_step_kernel(StepArgs a) {
   __shared__ PanelSmem sm;
   int b = blockIdx.x;
@@ -506,6 +654,16 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
     return;
   }
   b -= a.np;
+  if (b < a.nred) {
+    task_reduce(a, b, sm);
+    return;
+  }
+  b -= a.nred;
+  if (b < a.ndef) {
+    task_deferred(a, b, sm);
+    return;
+  }
+  b -= a.ndef;
   if (b < a.nuc) task_update_chol(a, b, sm);
 }
 
@@ -513,13 +671,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
 // The steps of one column group (blocks jb .. je-1) applied at once to the block
 // columns past it: A[i][j] -= sum_s L[i][s] L[j][s]^T, je <= j <= i (fp64 MFMA,
 // K = 64 (je - jb)).  One 64x64 tile per work-group, C read and written once
-// after the products; K staged 32 columns at a time (34 KB of LDS and few
-// registers, so four work-groups share a CU), the next stage loading into
-// registers under the current products.
+// after the products; 34 KB of LDS and few registers, so four work-groups share
+// a CU.
 // ---------------------------------------------------------------------------
-constexpr int kGK = 32;       // K columns per stage
-constexpr int kGP = kGK + 1;  // LDS pitch (doubles) of the [row][k] stages
-
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) void chol_group_update_kernel(
     double* __restrict__ A, int d, int jb, int je) {
   __shared__ double S0[kNB * kGP], S1[kNB * kGP];
@@ -531,50 +685,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
   const int j = b - i * (i + 1) / 2;
   const int64_t dd = d;
   const int64_t R0 = (int64_t)(je + i) * kNB, C0 = (int64_t)(je + j) * kNB;
-  // staging: thread t covers row t / 4 of a [64][32] stage, columns 8 (t % 4) .. + 7
-  const int sr = t >> 2, sc = 8 * (t & 3);
-  double va[8], vb[8];
-  auto gload = [&](double (&v)[8], int64_t row0, int64_t k0) {
-    const int64_t row = row0 + sr;
-    const bool ok = row < dd;
-    const double* src = A + (ok ? row : 0) * dd + k0 + sc;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) v[e] = ok ? src[e] : 0.0;
-  };
-  const int64_t K0 = (int64_t)jb * kNB;
-  gload(va, R0, K0);
-  gload(vb, C0, K0);
   f64x4 acc[2][2];
   zero_acc(acc);
-  const int nst = (je - jb) * (kNB / kGK);
-  for (int st = 0; st < nst; ++st) {
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      S0[sr * kGP + sc + e] = va[e];
-      S1[sr * kGP + sc + e] = vb[e];
-    }
-    __syncthreads();
-    if (st + 1 < nst) {
-      gload(va, R0, K0 + (int64_t)(st + 1) * kGK);
-      gload(vb, C0, K0 + (int64_t)(st + 1) * kGK);
-    }
-#pragma unroll
-    for (int k4 = 0; k4 < kGK / 4; ++k4) {
-      const int k = 4 * k4 + (lane >> 4);
-      double a[2], bb[2];
-#pragma unroll
-      for (int f = 0; f < 2; ++f) {
-        a[f] = S0[(wm * 32 + f * 16 + (lane & 15)) * kGP + k];
-        bb[f] = S1[(wn * 32 + f * 16 + (lane & 15)) * kGP + k];
-      }
-#pragma unroll
-      for (int fm = 0; fm < 2; ++fm)
-#pragma unroll
-        for (int fn = 0; fn < 2; ++fn)
-          acc[fm][fn] = __builtin_amdgcn_mfma_f64_16x16x4f64(a[fm], bb[fn], acc[fm][fn], 0, 0, 0);
-    }
-    __syncthreads();
-  }
+  mma_nt_stream(A, dd, R0, C0, (int64_t)jb * kNB, (je - jb) * kNB, S0, S1, acc, t);
   // C after the products (few registers live across the K loop)
   double c[16];
 #pragma unroll
@@ -800,9 +913,19 @@ FactorPlan factor_plan(int64_t d) {
     const size_t e = (size_t)kNB * (size_t)sb;
     tw = std::max(tw, (size_t)(np - 1) * e * e + (size_t)nc_last * kNB * e);
   }
+  // deferred partial products (up to 96 blocks): per launch k, nblk - k - 3
+  // tiles of block column k+3 times cdiv(k + 1, kDefSteps) chunks, two launches'
+  // worth (double buffer)
+  size_t part_tiles = 0;
+  if (deferred_updates(p.nblk))
+    for (int64_t k = 0; k + 3 < p.nblk; ++k)
+      part_tiles = std::max(part_tiles, (size_t)(p.nblk - k - 3) * (size_t)cdiv(k + 1, kDefSteps));
+  p.part_slot = part_tiles * kNB * kNB;
   size_t off = 0;
   p.off_a64 = off;
   off = align_up(off + (size_t)d * d * sizeof(double), 256);
+  p.off_part = off;
+  off = align_up(off + 2 * p.part_slot * sizeof(double), 256);
   p.off_tw = off;
   off = align_up(off + tw * sizeof(float), 256);
   p.off_tmp = off;  // L^-1 (d*d fp32)
@@ -818,6 +941,7 @@ hipError_t factor_launch(const FactorPlan& p, const float* H, const int32_t* per
   const int64_t d = p.d;
   char* base = (char*)ws;
   double* A = (double*)(base + p.off_a64);
+  double* part = (double*)(base + p.off_part);
   float* Tw = (float*)(base + p.off_tw);
   float* Linv = (float*)(base + p.off_tmp);
   double* lam = (double*)(base + p.off_lam);
@@ -827,16 +951,8 @@ hipError_t factor_launch(const FactorPlan& p, const float* H, const int32_t* per
   hipLaunchKernelGGL(rev_copy_kernel, dim3(nt, nt), dim3(kThreads), 0, s, H, d, lam, perm, A);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   const int nblk = (int)p.nblk;
-  // 64-column blocks per column group.  Up to 96 blocks one group spans the
-  // matrix (every step updates the whole trailing triangle under the panel
-  // chain); past that the trailing updates outgrow the chain and groups of 8
-  // blocks (512 columns) with one rank-512 update each are faster (measured:
-  // equal at d = 6144, 9% faster at 8192, 20% at 12288, 5-10% slower at
-  // 2048-4096).
-  const int kGroup = nblk > 96 ? 8 : nblk;
-  for (int jb = 0; jb < nblk; jb += kGroup) {
-    const int je = std::min(jb + kGroup, nblk);
-    for (int k = jb - 1; k < je - 1; ++k) {
+  if (deferred_updates(nblk)) {
+    for (int k = -1; k <= nblk - 2; ++k) {
       StepArgs a{};
       a.A = A;
       a.Linv = Linv;
@@ -845,19 +961,49 @@ hipError_t factor_launch(const FactorPlan& p, const float* H, const int32_t* per
       a.nblk = nblk;
       a.k = k;
       a.np = nblk - (k + 1);
-      a.jend = je;
-      a.skip_step = (jb > 0 && k == jb - 1) ? 1 : 0;
-      const int m = nblk - (k + 2);  // block rows past column k+1
-      const int w = je - (k + 2);    // block columns of the group past column k+1
-      a.nuc = (k >= 0 && !a.skip_step && w > 0) ? w * m - w * (w - 1) / 2 : 0;
-      hipLaunchKernelGGL(chol_step_kernel, dim3((unsigned)(a.np + a.nuc)), dim3(kThreads), 0, s, a);
+      a.jend = nblk;
+      // RED on block column k+2 with the chunks the previous launch's DEF wrote
+      // (steps 0 .. k-1); DEF on block column k+3 with steps 0 .. k
+      a.nred = (k >= 0 && k + 2 < nblk) ? nblk - (k + 2) : 0;
+      a.red_chunks = (a.nred > 0 && k >= 1) ? (int)cdiv(k, kDefSteps) : 0;
+      a.ndef = (k >= 0 && k + 3 < nblk) ? (nblk - (k + 3)) * (int)cdiv(k + 1, kDefSteps) : 0;
+      a.part_w = part + (size_t)(k & 1) * p.part_slot;
+      a.part_r = part + (size_t)((k + 1) & 1) * p.part_slot;
+      hipLaunchKernelGGL(chol_step_kernel, dim3((unsigned)(a.np + a.nred + a.ndef)), dim3(kThreads), 0, s, a);
       if ((e = hipGetLastError()) != hipSuccess) return e;
     }
-    if (je < nblk) {
-      const int m = nblk - je;
-      hipLaunchKernelGGL(chol_group_update_kernel, dim3((unsigned)(m * (m + 1) / 2)), dim3(kThreads), 0, s, A,
-                         (int)d, jb, je);
-      if ((e = hipGetLastError()) != hipSuccess) return e;
+  } else {
+    // up to 16 blocks every step updates the whole trailing triangle (measured:
+    // 2% faster than the deferred scheme at 512 columns, equal at 1024); past
+    // 96 blocks groups of 8 blocks (512 columns): each step updates the tiles of
+    // its own group, and one rank-512 update per group reaches the rest of the
+    // matrix (the deferred launches would outgrow the panel chain there)
+    const int kGroup = nblk > kDeferMaxBlocks ? 8 : nblk;
+    for (int jb = 0; jb < nblk; jb += kGroup) {
+      const int je = std::min(jb + kGroup, nblk);
+      for (int k = jb - 1; k < je - 1; ++k) {
+        StepArgs a{};
+        a.A = A;
+        a.Linv = Linv;
+        a.info = info;
+        a.d = (int)d;
+        a.nblk = nblk;
+        a.k = k;
+        a.np = nblk - (k + 1);
+        a.jend = je;
+        a.skip_step = (jb > 0 && k == jb - 1) ? 1 : 0;
+        const int m = nblk - (k + 2);  // block rows past column k+1
+        const int w = je - (k + 2);    // block columns of the group past column k+1
+        a.nuc = (k >= 0 && !a.skip_step && w > 0) ? w * m - w * (w - 1) / 2 : 0;
+        hipLaunchKernelGGL(chol_step_kernel, dim3((unsigned)(a.np + a.nuc)), dim3(kThreads), 0, s, a);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+      }
+      if (je < nblk) {
+        const int m = nblk - je;
+        hipLaunchKernelGGL(chol_group_update_kernel, dim3((unsigned)(m * (m + 1) / 2)), dim3(kThreads), 0, s, A,
+                           (int)d, jb, je);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+      }
     }
   }
   const bool vec = (d % 4) == 0;

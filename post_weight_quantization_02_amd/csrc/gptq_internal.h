@@ -47,7 +47,8 @@ struct FactorPlan {
   int64_t d;
   int nb;                 // Cholesky block
   int64_t nblk;
-  size_t off_a64, off_tw, off_tmp, off_lam, ws_bytes;
+  size_t part_slot;       // doubles per half of the deferred-product double buffer
+  size_t off_a64, off_part, off_tw, off_tmp, off_lam, ws_bytes;
 };
 FactorPlan factor_plan(int64_t d);
 // perm: NULL, or the order in which the columns are factored (H[perm][:, perm])

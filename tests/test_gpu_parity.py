@@ -133,6 +133,11 @@ F_CASES = [
     ("tiny_2", lambda: O.hessian([case_x("ar1", 10, 2, np.float32, 14)])),
     ("tiny_1", lambda: O.hessian([case_x("ar1", 10, 1, np.float32, 15)])),
     ("powerlaw_1536", lambda: O.hessian([case_x("powerlaw", 6144, 1536, np.float16, 16)])),
+    # 17 to 96 blocks: updates deferred as split-K partial products; the first
+    # such size, a ragged one, and the last (96 blocks, the last 20 wide)
+    ("ar1_1025_deferred", lambda: O.hessian([case_x("ar1", 4096, 1025, np.float32, 18)])),
+    ("ar1_1100_ragged_deferred", lambda: O.hessian([case_x("ar1", 4096, 1100, np.float32, 19)])),
+    ("lowrank_6100_ragged_deferred", lambda: O.hessian([case_x("lowrank", 4096, 6100, np.float16, 20)])),
     # 97 blocks of 64, the last 56 wide: past 96 blocks the factor runs in column
     # groups of 512 with one rank-512 update per group
     ("lowrank_6200_grouped", lambda: O.hessian([case_x("lowrank", 4096, 6200, np.float16, 17)])),
@@ -152,7 +157,7 @@ def test_factor_parity_attn4096_size():
 
 
 def test_factor_reports_not_positive_definite():
-    for H in (np.zeros((96, 96), np.float32), -np.eye(70, dtype=np.float32)):
+    for H in (np.zeros((96, 96), np.float32), -np.eye(70, dtype=np.float32), -np.eye(1200, dtype=np.float32)):
         pd = 0.0 if not H.any() else 0.01
         U, lam, info = G.gptq_prepare_hinv(dev(H), pd)
         torch.cuda.synchronize()
