@@ -156,20 +156,38 @@ __global__ __launch_bounds__(kThreads) void group_grid_kernel(const float* __res
 // parameters group_grid_kernel wrote at the block start).  FULL: width == B.
 // Both are compile-time so the fully unrolled column loop carries the group
 // code only at the group starts.
-// Eprev: NULL, or (blocks paired in the out-of-block correction) the previous
-// block's E, whose share W[:, i1:i1+width] -= E_prev U[i1-B:i1, i1:i1+width] the
-// work-group applies to its own rows before the column loop.
-template <int CPL, int GIN, bool FULL>
-__global__ __launch_bounds__(kThreads) void panel_kernel(
+// Blocks paired in the out-of-block correction: the previous block's share
+// W[:, i1:i1+width] -= E_prev U[i1-B:i1, i1:i1+width] is applied by the
+// work-group to its own rows before the column loop, with E_prev either read
+// from memory (kEprevMem: Eprev, NULL when there is no share) or, when the same
+// work-group has just quantized those rows through the previous block, taken
+// from each lane's errors in registers (kEprevRegs: er on entry).
+enum { kEprevMem = 0, kEprevRegs = 1 };
+
+// LDS of one block: U's diagonal block, the per-wave strips of the share
+// (blocks of 128), 1/U_jj, the error reduction
+template <int CPL>
+struct PanelLds {
+  static constexpr int B = 16 * CPL;
+  float Us[B * B];
+  float dl[CPL == 8 ? 16 * B : 4];
+  float rd[B];
+  double red[kThreads / 64];
+};
+
+template <int CPL, int GIN, bool FULL, int EMODE>
+__device__ __forceinline__ void panel_body(
     float* __restrict__ W, int d_row, int d_col, int i1, int width,
     const float* __restrict__ U, int maxq, int gwide, int ngroups,
     uint8_t* __restrict__ codes, float* __restrict__ scales, int32_t* __restrict__ zeros,
-    float* __restrict__ E, double* __restrict__ part_e, const float* __restrict__ Eprev) {
+    float* __restrict__ E, double* __restrict__ part_e, const float* __restrict__ Eprev,
+    float (&er)[CPL], PanelLds<CPL>& L) {
   constexpr int B = 16 * CPL;
   static_assert(GIN == 0 || (GIN % 16 == 0 && B % GIN == 0), "group inside block");
-  __shared__ __attribute__((aligned(16))) float Us[B * B];
-  __shared__ float rd[B];
-  __shared__ double red[kThreads / 64];
+  static_assert(EMODE == kEprevMem || (FULL && CPL == 8), "shares from registers: full blocks of 128");
+  float* Us = L.Us;
+  float* rd = L.rd;
+  double* red = L.red;
   const int t = threadIdx.x;
   const size_t ldu = (size_t)d_col;
   // stage U's diagonal block in LDS.  Full blocks of 64 or 128 columns: whole
@@ -234,15 +252,14 @@ __global__ __launch_bounds__(kThreads) void panel_kernel(
   const int row = blockIdx.x * 16 + (t >> 6) * 4 + (lane >> 4);
   const bool valid = row < d_row;
   const size_t rowc = (size_t)(valid ? row : d_row - 1);
-  float w[CPL], cr[CPL], er[CPL];
+  float w[CPL], cr[CPL];
 #pragma unroll
   for (int r = 0; r < CPL; ++r) {
     const int col = p * CPL + r;
     w[r] = (FULL || col < width) ? W[rowc * d_col + i1 + col] : 0.f;
     cr[r] = 0.f;
-    er[r] = 0.f;
   }
-  if (Eprev) {
+  if (EMODE == kEprevRegs || Eprev) {
     // E_prev is stored [k][row].  U rows are 16-byte aligned here (the caller
     // pairs blocks only then).
     if constexpr (FULL && CPL == 8) {
@@ -255,9 +272,8 @@ __global__ __launch_bounds__(kThreads) void panel_kernel(
       // chunk's FMAs.  Words written by one lane and read by another are
       // ordered by a work-group barrier with LDS-only fences (the diagonal
       // block's direct-to-LDS loads may stay in flight across it).
-      __shared__ __attribute__((aligned(16))) float dl[16 * B];
       const int wv = __builtin_amdgcn_readfirstlane(t >> 6);
-      float* el = dl + wv * 4 * B;
+      float* el = L.dl + wv * 4 * B;
       const int erl = std::min((int)blockIdx.x * 16 + wv * 4 + (lane & 3), d_row - 1);
       const float* up = U + (size_t)(i1 - B) * ldu + i1 + 2 * lane;
       constexpr int KC = 16;
@@ -271,8 +287,14 @@ __global__ __launch_bounds__(kThreads) void panel_kernel(
         for (int k = 0; k < KC; ++k) ua[buf][k] = *(const float2*)(up + (size_t)(k0 + k) * ldu);
       };
       ld(0, 0);  // in flight while E_prev is staged
+      if constexpr (EMODE == kEprevRegs) {
+        // this lane's row is row lane / 16 of the wave; its errors are columns p CPL + r
 #pragma unroll
-      for (int j = 0; j < B / 16; ++j) el[j * 64 + lane] = Eprev[(size_t)(j * 16 + (lane >> 2)) * d_row + erl];
+        for (int r = 0; r < CPL; ++r) el[4 * (p * CPL + r) + (lane >> 4)] = er[r];
+      } else {
+#pragma unroll
+        for (int j = 0; j < B / 16; ++j) el[j * 64 + lane] = Eprev[(size_t)(j * 16 + (lane >> 2)) * d_row + erl];
+      }
       auto lds_sync = [] {
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
         __builtin_amdgcn_s_barrier();
@@ -309,6 +331,8 @@ __global__ __launch_bounds__(kThreads) void panel_kernel(
       }
     }
   }
+#pragma unroll
+  for (int r = 0; r < CPL; ++r) er[r] = 0.f;
   float s = 1.f, z = 0.f;
   if (GIN == 0) {
     // per-row grid (one column of scales) or a group wider than the block
@@ -410,6 +434,55 @@ __global__ __launch_bounds__(kThreads) void panel_kernel(
   if (lane == 0) red[t >> 6] = se;
   __syncthreads();
   if (t == 0) part_e[blockIdx.x] += (red[0] + red[1]) + (red[2] + red[3]);
+}
+
+template <int CPL, int GIN, bool FULL>
+__global__ __launch_bounds__(kThreads) void panel_kernel(
+    float* __restrict__ W, int d_row, int d_col, int i1, int width,
+    const float* __restrict__ U, int maxq, int gwide, int ngroups,
+    uint8_t* __restrict__ codes, float* __restrict__ scales, int32_t* __restrict__ zeros,
+    float* __restrict__ E, double* __restrict__ part_e, const float* __restrict__ Eprev) {
+  __shared__ __attribute__((aligned(16))) PanelLds<CPL> L;
+  float er[CPL];
+  panel_body<CPL, GIN, FULL, kEprevMem>(W, d_row, d_col, i1, width, U, maxq, gwide, ngroups, codes, scales,
+                                         zeros, E, part_e, Eprev, er, L);
+}
+
+// Two full blocks of 128 columns, [i1, i1 + 128) and [i1 + 128, i1 + 256), for
+// 16 rows per work-group: the second block's share of the first block's
+// correction depends only on the work-group's own rows, so the same work-group
+// applies it from the errors it has just computed and goes on (one launch per
+// pair instead of two; E of the two blocks consecutive, E and E + 128 d_row).
+template <int GIN>
+__global__ __launch_bounds__(kThreads) void panel_pair_kernel(
+    float* __restrict__ W, int d_row, int d_col, int i1, const float* __restrict__ U, int maxq, int gwide,
+    int ngroups, uint8_t* __restrict__ codes, float* __restrict__ scales, int32_t* __restrict__ zeros,
+    float* __restrict__ E, double* __restrict__ part_e) {
+  __shared__ __attribute__((aligned(16))) PanelLds<8> L;
+  float er[8];
+  panel_body<8, GIN, true, kEprevMem>(W, d_row, d_col, i1, 128, U, maxq, gwide, ngroups, codes, scales, zeros, E,
+                                      part_e, nullptr, er, L);
+  panel_body<8, GIN, true, kEprevRegs>(W, d_row, d_col, i1 + 128, 128, U, maxq, gwide, ngroups, codes, scales,
+                                       zeros, E + (size_t)128 * d_row, part_e, nullptr, er, L);
+}
+
+hipError_t launch_panel_pair(int gin, dim3 grid, hipStream_t s, float* W, int d_row, int d_col, int i1,
+                             const float* U, int maxq, int gwide, int ngroups, uint8_t* codes, float* scales,
+                             int32_t* zeros, float* E, double* part_e) {
+#define GPTQ_PAIR_CASE(G)                                                                                   \
+  case G:                                                                                                  \
+    hipLaunchKernelGGL(panel_pair_kernel<G>, grid, dim3(kThreads), 0, s, W, d_row, d_col, i1, U, maxq, gwide, \
+                       ngroups, codes, scales, zeros, E, part_e);                                          \
+    return hipGetLastError();
+  switch (gin) {
+    GPTQ_PAIR_CASE(0)
+    GPTQ_PAIR_CASE(16)
+    GPTQ_PAIR_CASE(32)
+    GPTQ_PAIR_CASE(64)
+    GPTQ_PAIR_CASE(128)
+    default: return hipErrorInvalidValue;
+  }
+#undef GPTQ_PAIR_CASE
 }
 
 template <int CPL, int GIN>
@@ -649,11 +722,16 @@ hipError_t quant_launch(const QuantPlan& p, const void* W0, int w_dtype, int64_t
   // enough rows for one row per lane to fill the chip (and no in-panel share)
   const bool row_panel = B == 128 && d_row >= kRowPanelMinRows && d_col % 4 == 0 &&
                          ((uintptr_t)U & 15) == 0;
+  // a fused pair of full blocks of 128 takes one launch (panel_pair_kernel)
+  bool pair_launched = false;
   for (int64_t i1 = 0, blk = 0; i1 < d_col; i1 += B, ++blk) {
     const int width = (int)std::min<int64_t>(B, d_col - i1);
     const int r = (int)(blk % nb);  // position in the group
     float* Eb = E + (int64_t)r * B * d_row;
     const float* Ep = (fused && r == 1) ? E : nullptr;
+    const bool pair_here = fused && r == 0 && B == 128 && i1 + 2 * B <= d_col && !row_panel;
+    const bool skip_panel = fused && r == 1 && pair_launched;
+    pair_launched = pair_here;
     if (group > B && i1 % group == 0) {
       const int64_t gw = std::min<int64_t>(group, d_col - i1);
       hipLaunchKernelGGL(group_grid_kernel, dim3((unsigned)cdiv(d_row, 4)), dim3(kThreads), 0, s, W,
@@ -664,8 +742,13 @@ hipError_t quant_launch(const QuantPlan& p, const void* W0, int w_dtype, int64_t
     const int gin = (group > 0 && group <= B) ? (int)group : 0;
     const int gwide = (group > B) ? (int)group : 0;
     const int ng = (int)ngroups;
-    if ((e = timer_begin(timer, s)) != hipSuccess) return e;
-    if (row_panel && !Ep && full && (gin == 0 || gin == B)) {
+    if (!skip_panel && (e = timer_begin(timer, s)) != hipSuccess) return e;
+    if (skip_panel) {
+      e = hipSuccess;
+    } else if (pair_here) {
+      e = launch_panel_pair(gin, pg, s, W, (int)d_row, (int)d_col, (int)i1, U, maxq, gwide, ng, cpos, scales,
+                            zeros, E, part_e);
+    } else if (row_panel && !Ep && full && (gin == 0 || gin == B)) {
       // one row per lane: 64 to 256 rows per work-group, sized so that the
       // work-groups cover the CUs about once
       const int64_t waves = cdiv(d_row, 64);
@@ -684,11 +767,15 @@ hipError_t quant_launch(const QuantPlan& p, const void* W0, int w_dtype, int64_t
                                    maxq, gwide, ng, cpos, scales, zeros, Eb, part_e, Ep); break;
     }
     if (e != hipSuccess) return e;
-    if (timer) {
-      // algorithmic bytes of the block's step: W block in, E and codes out, U's
-      // diagonal block, the grid parameters of the groups that start here
-      const int64_t gstarts = group ? (int64_t)(cdiv(i1 + width, group) - cdiv(i1, group)) : 0;
-      const double bytes = 9.0 * (double)d_row * width + 4.0 * width * width + 8.0 * (double)d_row * gstarts;
+    if (timer && !skip_panel) {
+      // algorithmic bytes of the launch's blocks: W block in, E and codes out, U's
+      // diagonal block, the grid parameters of the groups that start there
+      double bytes = 0.0;
+      for (int64_t b1 = i1; b1 < i1 + (pair_here ? 2 * B : width); b1 += B) {
+        const int64_t wb = std::min<int64_t>(B, d_col - b1);
+        const int64_t gstarts = group ? (int64_t)(cdiv(b1 + wb, group) - cdiv(b1, group)) : 0;
+        bytes += 9.0 * (double)d_row * wb + 4.0 * wb * wb + 8.0 * (double)d_row * gstarts;
+      }
       if ((e = timer_end(timer, kTimePanel, bytes, s)) != hipSuccess) return e;
     }
     const int64_t i2 = i1 + width;
