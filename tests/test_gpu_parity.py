@@ -165,6 +165,33 @@ def test_factor_reports_not_positive_definite():
 
 
 # ------------------------------------------------------------------ quantize loop
+def _scale_tol(W0, U, r, bits, group):
+    """Per-scale tolerance.  A group's grid comes from the then-current values of
+    its columns (itwiki "GPTQ", practical variants: parameters from the latest
+    updated weights), which the GPU forms in fp32 as W0_c minus the compensation
+    terms e_i U[i, c] of the n columns before the group's start.  A sum of n + 1
+    fp32 terms in any order is within (n + 1) 2^-24 of the sum of their
+    magnitudes, so each of the group's min and max, and hence
+    scale = (max - min) / maxq, may differ from the fp64 replay's by up to
+    2 (n + 1) 2^-24 max_c (|W0_c| + sum_i |e_i| |U[i, c]|) / maxq; the grid
+    formula itself rounds to 1e-5 relative.  The oracle's scaled errors follow
+    from its result: W0 - W_hat = E U with U upper triangular."""
+    from scipy.linalg import solve_triangular
+    U64 = np.asarray(U, np.float64)
+    W64 = np.asarray(W0, np.float64)
+    E = solve_triangular(U64, (W64 - r.w_hat).T, trans="T", lower=False).T
+    mag = np.abs(W64) + np.abs(E) @ np.abs(np.triu(U64, 1))
+    d_col = W64.shape[1]
+    g = group if group else d_col
+    maxq = (1 << bits) - 1
+    tol = np.empty_like(r.scales)
+    for gi in range(r.scales.shape[1]):
+        c0, c1 = gi * g, min(gi * g + g, d_col)
+        n = c0 + 1 if group else 1          # per-row grids come from W0 itself
+        tol[:, gi] = 1e-5 * np.abs(r.scales[:, gi]) + 2.0 * n * 2.0**-24 * mag[:, c0:c1].max(axis=1) / maxq
+    return tol
+
+
 def _quant_case(W0, Ho, bits, group, B, tol_err=0.01):
     H32 = Ho.astype(np.float32)
     Hd, lam = O.damp(H32.astype(np.float64), 0.01)
@@ -179,7 +206,8 @@ def _quant_case(W0, Ho, bits, group, B, tol_err=0.01):
     assert r.adopted_codes <= 0.001 * n, (r.adopted_codes, n)
     np.testing.assert_array_equal(r.codes, cg)
     assert cg.max() <= (1 << bits) - 1
-    np.testing.assert_allclose(sg, r.scales, rtol=1e-5, atol=0)
+    tol = _scale_tol(W0, U32, r, bits, group)
+    assert np.all(np.abs(sg - r.scales) <= tol), float(np.max(np.abs(sg - r.scales) / tol))
     np.testing.assert_array_equal(zg, r.zeros)
     e_o = O.output_error(W0, r.w_hat, H32.astype(np.float64))
     e_g = float(err.item())
@@ -226,6 +254,16 @@ Q_CASES = [
                                             O.hessian([case_x("ar1", 3000, 256, np.float32, 48)])), 3, 64, 128),
     ("rows8192_fp16_g128", 16, lambda: (case_w(8192, 384, np.float16, 49, 0.015),
                                         O.hessian([case_x("lowrank", 8192, 384, np.float16, 50)])), 4, 128, 128),
+    # at most 4096 rows a pair of full 128-column blocks is one panel launch:
+    # groups of 64 and of 16 inside the blocks, and a pair, a lone full block and
+    # a ragged last block (700 columns) at 4096 rows
+    ("pair_g64_in_block", 17, lambda: (case_w(300, 512, np.float32, 51),
+                                       O.hessian([case_x("ar1", 3000, 512, np.float32, 52)])), 4, 64, 128),
+    ("pair_g16_in_block_ragged", 18, lambda: (case_w(200, 700, np.float16, 53, 0.015),
+                                              O.hessian([case_x("lowrank", 4000, 700, np.float16, 54)])),
+     3, 16, 128),
+    ("pair_rows4096_perrow_ragged", 19, lambda: (case_w(4096, 700, np.float32, 55),
+                                                 O.hessian([case_x("ar1", 3000, 700, np.float32, 56)])), 4, 0, 128),
 ]
 
 
