@@ -89,9 +89,9 @@ __global__ __launch_bounds__(kThreads) void rev_copy_kernel(const float* __restr
 
 // ---------------------------------------------------------------------------
 // One step of the blocked Cholesky (64-column blocks) with look-ahead.  Launch
-// k (k = -1 .. nblk-2) runs two kinds of independent work-groups; every input
-// a work-group reads was finished by an earlier launch, so no work-group ever
-// waits on another:
+// k (k = -1 .. nblk-2) runs independent work-groups of the kinds below; every
+// input a work-group reads was finished by an earlier launch, so no work-group
+// ever waits on another:
 //   P  (rows r = k+1 .. nblk-1): apply step k to column block c = k+1 (tile
 //      (r, c) and the diagonal tile (c, c)), factor the diagonal tile in LDS
 //      (each P work-group redundantly), and solve its own tile:
