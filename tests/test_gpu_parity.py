@@ -157,7 +157,9 @@ def test_factor_parity_attn4096_size():
 
 
 def test_factor_reports_not_positive_definite():
-    for H in (np.zeros((96, 96), np.float32), -np.eye(70, dtype=np.float32), -np.eye(1200, dtype=np.float32)):
+    # right-looking (96, 70 columns), deferred (1200) and grouped (6208) Cholesky updates
+    for H in (np.zeros((96, 96), np.float32), -np.eye(70, dtype=np.float32), -np.eye(1200, dtype=np.float32),
+              -np.eye(6208, dtype=np.float32)):
         pd = 0.0 if not H.any() else 0.01
         U, lam, info = G.gptq_prepare_hinv(dev(H), pd)
         torch.cuda.synchronize()
