@@ -520,23 +520,47 @@ __device__ __forceinline__ void task_panel(const StepArgs a, int b, PanelSmem& s
     // stored: nothing reads the diagonal blocks of L again, and the other panel
     // work-groups of this launch may still be reading A[c1][c1] (with more of
     // them than the GPU runs at once, late ones start after this one ends).
-    for (int idx = t; idx < kNB * kNB; idx += kThreads) {
-      const int i = idx >> 6, c = idx & 63;
-      if (C0 + i < d && C0 + c < d)
-        a.Linv[(C0 + i) * d + C0 + c] = (c <= i) ? (float)(sm.S1[c * kP + i] * sm.sq[i]) : 0.f;
+    // two adjacent columns per thread: 8-byte stores where d is even
+    for (int idx = t; idx < kNB * kNB / 2; idx += kThreads) {
+      const int i = idx >> 5, c = 2 * (idx & 31);
+      if (C0 + i >= d) continue;
+      float v[2];
+#pragma unroll
+      for (int e = 0; e < 2; ++e) v[e] = (c + e <= i) ? (float)(sm.S1[(c + e) * kP + i] * sm.sq[i]) : 0.f;
+      float* dst = a.Linv + (C0 + i) * d + C0 + c;
+      if ((d & 1) == 0 && C0 + c + 1 < d) {
+        *(float2*)dst = make_float2(v[0], v[1]);
+      } else {
+#pragma unroll
+        for (int e = 0; e < 2; ++e)
+          if (C0 + c + e < d) dst[e] = v[e];
+      }
     }
     if (t == 0 && sm.fail < nbe && *a.info == 0) *a.info = (int32_t)(d - (C0 + sm.fail));
     return;
   }
   // L[r][c1] = m_T D^1/2, and its fp32 rounding at the same place of L^-1's
   // buffer: the block is read there by the one triangular-inverse product that
-  // needs it, before the product after it overwrites the block with L^-1's
-  for (int idx = t; idx < kNB * kNB; idx += kThreads) {
-    const int i = idx >> 6, c = idx & 63;
-    if (R0 + i < d && c < nbe) {
-      const double v = sm.S1[i * kP + c] * sm.sq[c];
-      a.A[(R0 + i) * d + C0 + c] = v;
-      a.Linv[(R0 + i) * d + C0 + c] = (float)v;
+  // needs it, before the product after it overwrites the block with L^-1's.
+  // Two adjacent columns per thread: 16- and 8-byte stores where d is even.
+  for (int idx = t; idx < kNB * kNB / 2; idx += kThreads) {
+    const int i = idx >> 5, c = 2 * (idx & 31);
+    if (R0 + i >= d || c >= nbe) continue;
+    double v[2];
+#pragma unroll
+    for (int e = 0; e < 2; ++e) v[e] = sm.S1[i * kP + c + e] * sm.sq[c + e];
+    double* da = a.A + (R0 + i) * d + C0 + c;
+    float* dl = a.Linv + (R0 + i) * d + C0 + c;
+    if ((d & 1) == 0 && c + 1 < nbe) {
+      *(f64x2*)da = f64x2{v[0], v[1]};
+      *(float2*)dl = make_float2((float)v[0], (float)v[1]);
+    } else {
+      da[0] = v[0];
+      dl[0] = (float)v[0];
+      if (c + 1 < nbe) {
+        da[1] = v[1];
+        dl[1] = (float)v[1];
+      }
     }
   }
 }
