@@ -144,7 +144,17 @@ __global__ __launch_bounds__(kTh) void corr2d_kernel(int m, int n, const float* 
 }
 
 // KB: one work-group per tile of the anti-diagonal: C = the partial corrections
-// added in chunk order, then the tile's own 63 anti-diagonals.
+// added in chunk order (all four waves), then the tile's own 63 anti-diagonals on
+// wave 0, one column per pair of lanes (j and j + 32, rows 0-15 and 16-31).  A
+// pair keeps column j of the tile's part of M in registers; at step s its entry
+// is row i = s - j, whose dot product sum_{i' <= i} U_Q[i'][i] M[i'][j] needs only
+// its own column (U_Q's column i comes from LDS, stored transposed; the two halves
+// meet by a lane swap, so both round the same value), and the step's errors, one
+// per row, meet in a 32-word LDS vector from which every lane adds
+// e_k U_P[s - k][j] to its rows k.  The factors U_P[s - k][j] for a lane's 16 rows
+// are one contiguous run of column j of U_P stored reversed, kept in four copies
+// shifted by one word so that every step reads its run with aligned 16-byte
+// loads.  No barrier inside the sweep, and the step loop stays rolled.
 template <typename T>
 __global__ __launch_bounds__(kTh) void tile2d_kernel(const T* __restrict__ X, int64_t ldx, int m, int n,
                                                      const float* __restrict__ UQ, const float* __restrict__ UP,
@@ -152,89 +162,183 @@ __global__ __launch_bounds__(kTh) void tile2d_kernel(const T* __restrict__ X, in
                                                      const float* __restrict__ part, const float* __restrict__ gridv,
                                                      int maxq, uint8_t* __restrict__ codes, int64_t ldc,
                                                      double* __restrict__ errp, int K, int I_lo, int Nb, int nchunk) {
-  __shared__ float xs[kT][kT + 1];      // X - C, then the tile's E
-  __shared__ float ml[kT][kT + 1];      // the tile's part of M: E_tile U_P(J, J)
-  __shared__ float uq[kT][kT + 1], up[kT][kT + 1];
+  constexpr int kH = kT / 2;             // rows per lane
+  constexpr int kUQ = kT + 4;            // pitch of uqt: rows 16-byte aligned, row reads spread over banks
+  constexpr int kRun = 2 * kT - 1;       // reversed column j of U_P: rv[z] = U_P[kRun - 1 - z][j]
+  constexpr int kUW = 3 * kT + 4;        // pitch of a reversed column (a run starts at z <= 62, ends <= 93)
+  __shared__ float xs[kT][kT];           // X - C, then the tile's E (pitch 32: an anti-diagonal's
+                                         // entries fall in 32 different banks)
+  __shared__ __attribute__((aligned(16))) float uqt[kT][kUQ];      // uqt[i][i'] = U_Q(I, I)[i'][i]
+  __shared__ __attribute__((aligned(16))) float upw[4][kT][kUW];   // upw[r][j][z] = rv_j[z + r]
+  __shared__ float up[kT][kT + 1];       // U_P(J, J), staged for upw; then the tile's part of M
+  __shared__ float fac[kT][kT];          // (1 / U_Q[i][i]) / U_P[j][j]
+  __shared__ __attribute__((aligned(16))) float es[kT];            // the step's errors, by row
+  __shared__ uint8_t cs[kT][kT];         // codes
   __shared__ double red[kTh];
   const int tile = (int)blockIdx.x, I = I_lo + tile, J = K - I;
   const int r0 = I * kT, c0 = J * kT;
   const int t = threadIdx.x, rr = t >> 3, cb = (t & 7) * 4;
+  // every global load of the set-up is issued before the values are used:
+  // addresses are clamped into the matrix and the results selected afterwards
+  float xv[4], qv[4], pv[4], qd[4], pd[4];
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int gi = min(r0 + rr, m - 1), gj = min(c0 + cb + u, n - 1);
+    xv[u] = (float)X[(int64_t)gi * ldx + gj];
+  }
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int e = t + kTh * q, i = e >> 5, j = e & 31;
+    const int qi = min(r0 + i, m - 1), qj = min(r0 + j, m - 1), pi = min(c0 + i, n - 1), pj = min(c0 + j, n - 1);
+    qv[q] = UQ[(int64_t)qi * m + qj];
+    pv[q] = UP[(int64_t)pi * n + pj];
+    qd[q] = UQ[(int64_t)qi * m + qi];
+    pd[q] = UP[(int64_t)pj * n + pj];
+  }
   float acc[4] = {0.f, 0.f, 0.f, 0.f};
   const int nc = (I + kChunk) / kChunk;   // chunks that hold tile-rows <= I
-  for (int ch = 0; ch < nc; ++ch) {
-    const float* pp = part + ((int64_t)tile * nchunk + ch) * (kT * kT) + rr * kT + cb;
+  const float* pp = part + (int64_t)tile * nchunk * (kT * kT) + rr * kT + cb;
+  int ch = 0;
+  for (; ch + 8 <= nc; ch += 8) {   // eight chunks' loads in flight, added in chunk order
+    f32x4 x[8];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) acc[u] += pp[u];
+    for (int q = 0; q < 8; ++q) x[q] = *(const f32x4*)(pp + (ch + q) * (kT * kT));
+#pragma unroll
+    for (int q = 0; q < 8; ++q)
+#pragma unroll
+      for (int u = 0; u < 4; ++u) acc[u] += x[q][u];
+  }
+  for (; ch < nc; ++ch) {
+    const f32x4 x = *(const f32x4*)(pp + ch * (kT * kT));
+#pragma unroll
+    for (int u = 0; u < 4; ++u) acc[u] += x[u];
   }
 #pragma unroll
   for (int u = 0; u < 4; ++u) {
     const int gi = r0 + rr, gj = c0 + cb + u;
-    xs[rr][cb + u] = (gi < m && gj < n) ? (float)X[(int64_t)gi * ldx + gj] - acc[u] : 0.f;
+    xs[rr][cb + u] = (gi < m && gj < n) ? xv[u] - acc[u] : 0.f;
   }
-  for (int e = t; e < kT * kT; e += kTh) {
-    const int i = e >> 5, j = e & 31;
-    uq[i][j] = (r0 + i < m && r0 + j < m) ? (i <= j ? UQ[(int64_t)(r0 + i) * m + r0 + j] : 0.f) : (i == j ? 1.f : 0.f);
-    up[i][j] = (c0 + i < n && c0 + j < n) ? (i <= j ? UP[(int64_t)(c0 + i) * n + c0 + j] : 0.f) : (i == j ? 1.f : 0.f);
-    ml[i][j] = 0.f;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int e = t + kTh * q, i = e >> 5, j = e & 31;
+    // the tiles' upper parts; the identity outside the matrix
+    uqt[j][i] = (r0 + i < m && r0 + j < m) ? (i <= j ? qv[q] : 0.f) : (i == j ? 1.f : 0.f);
+    up[i][j] = (c0 + i < n && c0 + j < n) ? (i <= j ? pv[q] : 0.f) : (i == j ? 1.f : 0.f);
+    fac[i][j] = (1.f / (r0 + i < m ? qd[q] : 1.f)) / (c0 + j < n ? pd[q] : 1.f);
+  }
+  if (t < kT) es[t] = 0.f;
+  // the reversed columns of U_P in four shifted copies: zeros first, then the
+  // 32 values of each column (rv_j[y] = U_P[62 - y][j] for y = 31 .. 62) into
+  // every copy r at z = y - r
+  {
+    float* w = &upw[0][0][0];
+    for (int e = t; e < 4 * kT * kUW / 4; e += kTh) *(f32x4*)(w + 4 * e) = f32x4{0.f, 0.f, 0.f, 0.f};
   }
   __syncthreads();
-  const float scale = gridv[0], zero = gridv[1], fmaxq = (float)maxq;
-  const float rs = 1.f / scale;
-  // row i of the tile belongs to the eight lanes 8 i .. 8 i + 7 (a wave holds eight
-  // rows): lane p takes every eighth term of the row's dot product and owns the
-  // row's columns p, p + 8, p + 16, p + 24 of the tile's part of M in registers
-  // (published to LDS for the other rows' dot products); the eight partial sums
-  // meet by DPP moves, so all eight lanes round the same value.  A step's
-  // entries never read each other's updates (a row is read by other rows only at
-  // columns below its own entry); the barrier after each step publishes the row
-  // to the other waves.
-  const int i = t >> 3, p = t & 7;
-  const float rq = 1.f / uq[i][i];
-  float mr[kT / 8] = {0.f, 0.f, 0.f, 0.f};
-  double eacc = 0.0;
-  for (int s = 0; s < 2 * kT - 1; ++s) {
-    const int j = s - i;
-    const bool on = j >= 0 && j < kT && r0 + i < m && c0 + j < n;
-    float d = 0.f;
-    if (on) {
+  {
+    const int j = t & 31, c0w = (t >> 5) * 4;   // rows c0w .. c0w + 3 of column j
+    float cv[4];
 #pragma unroll
-      for (int u = 0; u < kT / 8; ++u) {
-        const int ip = p + 8 * u;
-        d = fmaf(ip <= i ? uq[ip][i] : 0.f, ml[ip][j], d);
-      }
+    for (int q = 0; q < 4; ++q) cv[q] = up[c0w + q][j];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int y = kRun - 1 - (c0w + q);
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        if (y - r >= 0) upw[r][j][y - r] = cv[q];
     }
-    // the eight lanes' sum by DPP: quad_perm [1,0,3,2], quad_perm [2,3,0,1], then
-    // row_half_mirror (lane k of an 8-lane group reads lane 7 - k: the other quad)
-    d += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, d), 0xB1, 0xF, 0xF, false));
-    d += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, d), 0x4E, 0xF, 0xF, false));
-    d += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, d), 0x141, 0xF, 0xF, false));
-    if (on) {
-      const float v = xs[i][j] - d;
-      const float c = fminf(fmaxf(rintf(v * rs) + zero, 0.f), fmaxq);
-      const float e = (v - scale * (c - zero)) * (rq / up[j][j]);
-      if (p == 0) {
-        codes[(int64_t)(r0 + i) * ldc + c0 + j] = (uint8_t)c;
-        eacc += (double)e * (double)e;
-        xs[i][j] = e;
-      }
+  }
+  __syncthreads();
+  double eacc = 0.0;
+  if (t < 64) {
+    const int j = t & 31, h = t >> 5;
+    float mc[kH];
 #pragma unroll
-      for (int u = 0; u < kT / 8; ++u) {
-        const int jj = p + 8 * u;
-        if (jj >= j) {
-          mr[u] = fmaf(e, up[j][jj], mr[u]);
-          ml[i][jj] = mr[u];
+    for (int k = 0; k < kH; ++k) mc[k] = 0.f;
+    const float scale = gridv[0], zero = gridv[1], fmaxq = (float)maxq;
+    const float rs = 1.f / scale;
+    const bool colv = c0 + j < n;
+    // the operands of a step that do not depend on the previous step (U_Q's
+    // column, X - C, the error factor) are read one step ahead, under the
+    // previous step's error exchange
+    f32x4 un[kH / 4];
+    float xn, fn;
+    auto fetch = [&](int sn) __attribute__((always_inline)) {
+      const int ic = min(max(sn - j, 0), kT - 1);
+      xn = xs[ic][j];
+      fn = fac[ic][j];
+      const f32x4* urow = (const f32x4*)&uqt[ic][kH * h];
+#pragma unroll
+      for (int q = 0; q < kH / 4; ++q) un[q] = urow[q];
+    };
+    fetch(0);
+    for (int s = 0; s < kRun; ++s) {
+      const int i = s - j;
+      if (i >= 0 && i < kT) {
+        // dot product over i' <= i (U_Q upper: uqt[i][i'] = 0 past i), each half
+        // over its 16 rows, the halves added by a swap of lanes j and j + 32
+        float dq[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int q = 0; q < kH / 4; ++q)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) dq[r] = fmaf(un[q][r], mc[4 * q + r], dq[r]);
+        const float dh = (dq[0] + dq[1]) + (dq[2] + dq[3]);
+        // swap the upper half of one copy with the lower half of another: the
+        // first result then holds rows 0-15's sum and the second rows 16-31's, in
+        // both halves (the results are copied out as scalars before the casts)
+        const unsigned du = __builtin_bit_cast(unsigned, dh);
+        const auto sw = __builtin_amdgcn_permlane32_swap(du, du, false, false);
+        const unsigned lo = sw[0], hi = sw[1];
+        const float d = __builtin_bit_cast(float, lo) + __builtin_bit_cast(float, hi);
+        const float v = xn - d;
+        const float c = fminf(fmaxf(rintf(v * rs) + zero, 0.f), fmaxq);
+        float e = (v - scale * (c - zero)) * fn;
+        if (!(colv && r0 + i < m)) e = 0.f;
+        if (h == 0) {
+          if (colv && r0 + i < m) {
+            cs[i][j] = (uint8_t)c;
+            eacc += (double)e * (double)e;
+            xs[i][j] = e;
+          }
+          es[i] = e;
         }
       }
+      // row s - 32 had its last entry (column 31) in the previous step
+      if (t == kT - 1 && s >= kT) es[s - kT] = 0.f;
+      // the writes above come before the reads below in this wave's LDS queue,
+      // which the hardware keeps in order; only the compiler must not move them
+      __atomic_signal_fence(__ATOMIC_SEQ_CST);
+      f32x4 ev[kH / 4], uv[kH / 4];
+#pragma unroll
+      for (int q = 0; q < kH / 4; ++q) ev[q] = *(const f32x4*)&es[kH * h + 4 * q];
+      {
+        // U_P[s - k][j] = rv_j[kRun - 1 - s + k] for this lane's rows k = 16 h + k'
+        const int o = kRun - 1 - s, r = o & 3;
+        const f32x4* run = (const f32x4*)&upw[r][j][o - r + kH * h];
+#pragma unroll
+        for (int q = 0; q < kH / 4; ++q) uv[q] = run[q];
+      }
+      if (s + 1 < kRun) fetch(s + 1);
+      // M[k][j] += e_k U_P[s - k][j]; rows without an entry in this step have
+      // e_k = 0, and U_P[s - k][j] = 0 where s - k is not in 0 .. j
+#pragma unroll
+      for (int q = 0; q < kH / 4; ++q)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) mc[4 * q + r] = fmaf(ev[q][r], uv[q][r], mc[4 * q + r]);
+      __atomic_signal_fence(__ATOMIC_SEQ_CST);
     }
-    __syncthreads();
+#pragma unroll
+    for (int k = 0; k < kH; ++k) up[kH * h + k][j] = mc[k];
   }
-  // E tile to the workspace, M(I, J) += ml
+  __syncthreads();
+  // E, codes and M(I, J) += the tile's part of M
 #pragma unroll
   for (int u = 0; u < 4; ++u) {
     const int gi = r0 + rr, gj = c0 + cb + u;
     if (gi < m && gj < n) {
       E[(int64_t)gi * n + gj] = xs[rr][cb + u];
-      M[(int64_t)gi * n + gj] += ml[rr][cb + u];
+      codes[(int64_t)gi * ldc + gj] = cs[rr][cb + u];
+      M[(int64_t)gi * n + gj] += up[rr][cb + u];
     }
   }
   red[t] = eacc;
