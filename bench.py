@@ -529,8 +529,8 @@ def gptq2d_bench(args):
                    "m": m, "n": n, "bits": bits, "parallelism": "single-gpu"},
         "stages": {"side_factors_ms": round(t_factors * 1e3, 3), "sweep_launches": m // 32 + n // 32 - 1,
                    "err": float(err.item())},
-        "roofline": {"bound": "alu", "kernel": "the sweep: corr2d_kernel + tile2d_kernel + feed2d_kernel per 32-tile "
-                                               "anti-diagonal",
+        "roofline": {"bound": "alu", "kernel": "the sweep: fc2d_kernel (corrections and feedback) + tile2d_kernel "
+                                               "per 32-tile anti-diagonal",
                      "achieved": round(ach, 3), "peak": PEAK_F32_VALU_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(ach / PEAK_F32_VALU_TFLOPS, 4), "traffic": None},
     }

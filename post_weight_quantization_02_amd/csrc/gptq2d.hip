@@ -11,15 +11,17 @@
 //
 // MI355X: the matrix is cut into 32 x 32 tiles swept by tile anti-diagonals (the
 // tiles of one are independent: tile (I, J) needs only tiles above and to the left
-// of it).  Three launches per tile anti-diagonal:
-//   corr2d  the correction C = sum over I' <= I of U_Q(I', I)^T M(I', J), split in
-//           chunks of 8 tile-rows, one work-group per (tile, chunk), on fp32 MFMA
-//           (v_mfma_f32_32x32x2f32) with every load issued before the products;
+// of it).  Two launches per tile anti-diagonal K:
+//   fc2d    the partial corrections C = sum over I' <= I of U_Q(I', I)^T M(I', J)
+//           of anti-diagonal K, split in chunks of 8 tile-rows, one work-group per
+//           (tile, chunk), together with the feedback of anti-diagonal K - 1,
+//           M(I, J'') += E(I, J) U_P(J, J'') for J'' >= J + 2, one work-group per
+//           (tile, 8 tiles of J''); both on fp32 MFMA (v_mfma_f32_32x32x2f32) with
+//           every load issued before the products;
 //   tile2d  per tile: the chunks' partial sums added in order, then the tile's own
-//           63 anti-diagonals on 256 threads (eight lanes per row share its dot
-//           product and its update), writing codes, E and M(I, J);
-//   feed2d  M(I, J'') += E(I, J) U_P(J, J'') for the tiles to the right, one
-//           work-group per (tile, 8 tiles of J''), on fp32 MFMA.
+//           63 anti-diagonals on one wave (one column per pair of lanes), writing
+//           codes, E and M(I, J), and the right neighbour's feedback
+//           M(I, J + 1) += E(I, J) U_P(J, J + 1), which the next correction needs.
 // The grid comes from a min / max reduction first; every tile's sum of e^2 is
 // kept in fp64 and the sums are added in a fixed order at the end.
 #include "gptq_internal.h"
@@ -102,11 +104,11 @@ constexpr int kChunk = 8;   // tiles per work-group in the correction and the fe
 // reads row k = 2 kk + l / 32 of the two tiles at column l % 32: 128 contiguous
 // bytes per half-wave), all of a wave's loads issued before its products; the
 // four waves' sums are added in LDS in wave order.
-__global__ __launch_bounds__(kTh) void corr2d_kernel(int m, int n, const float* __restrict__ UQ,
-                                                     const float* __restrict__ M, float* __restrict__ part,
-                                                     int K, int I_lo, int nchunk) {
+__device__ __forceinline__ void corr2d_body(int bid, int m, int n, const float* __restrict__ UQ,
+                                            const float* __restrict__ M, float* __restrict__ part, int K, int I_lo,
+                                            int nchunk) {
   __shared__ float red[kTh / 64][16][64];
-  const int tile = (int)blockIdx.x / nchunk, ch = (int)blockIdx.x % nchunk;
+  const int tile = bid / nchunk, ch = bid % nchunk;
   const int I = I_lo + tile, J = K - I;
   const int i0 = ch * kChunk, i1 = min(i0 + kChunk, I + 1);
   if (i0 >= i1) return;
@@ -174,6 +176,8 @@ __global__ __launch_bounds__(kTh) void tile2d_kernel(const T* __restrict__ X, in
   __shared__ float fac[kT][kT];          // (1 / U_Q[i][i]) / U_P[j][j]
   __shared__ __attribute__((aligned(16))) float es[kT];            // the step's errors, by row
   __shared__ uint8_t cs[kT][kT];         // codes
+  __shared__ float upn[kT][kT + 1];      // U_P(J, J + 1), for the right neighbour's feedback
+  __shared__ float mo[2][kT][kT];        // M(I, J) and M(I, J + 1) as they stand
   __shared__ double red[kTh];
   const int tile = (int)blockIdx.x, I = I_lo + tile, J = K - I;
   const int r0 = I * kT, c0 = J * kT;
@@ -329,6 +333,18 @@ __global__ __launch_bounds__(kTh) void tile2d_kernel(const T* __restrict__ X, in
     }
 #pragma unroll
     for (int k = 0; k < kH; ++k) up[kH * h + k][j] = mc[k];
+  } else if (t >= 64) {
+    // waves 1-3, idle during the sweep, stage U_P(J, J + 1), M(I, J) and M(I, J + 1)
+    // (no other work-group of this launch writes these two tiles of M)
+    for (int e = t - 64; e < kT * kT; e += kTh - 64) {
+      const int k = e >> 5, c = e & 31;
+      const int gi = min(r0 + k, m - 1), gj = min(c0 + c, n - 1), gn = min(c0 + kT + c, n - 1);
+      const float u = UP[(int64_t)min(c0 + k, n - 1) * n + gn];
+      const float a = M[(int64_t)gi * n + gj], b = M[(int64_t)gi * n + gn];
+      upn[k][c] = (c0 + k < n && c0 + kT + c < n) ? u : 0.f;
+      mo[0][k][c] = a;
+      mo[1][k][c] = b;
+    }
   }
   __syncthreads();
   // E, codes and M(I, J) += the tile's part of M
@@ -338,7 +354,23 @@ __global__ __launch_bounds__(kTh) void tile2d_kernel(const T* __restrict__ X, in
     if (gi < m && gj < n) {
       E[(int64_t)gi * n + gj] = xs[rr][cb + u];
       codes[(int64_t)gi * ldc + gj] = cs[rr][cb + u];
-      M[(int64_t)gi * n + gj] += up[rr][cb + u];
+      M[(int64_t)gi * n + gj] = mo[0][rr][cb + u] + up[rr][cb + u];
+    }
+  }
+  // the right neighbour's feedback, M(I, J + 1) += E(I, J) U_P(J, J + 1), before
+  // its correction is formed in the next launch
+  if (J + 1 < Nb) {
+    float o[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll 8
+    for (int k = 0; k < kT; ++k) {
+      const float ev = xs[rr][k];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) o[u] = fmaf(ev, upn[k][cb + u], o[u]);
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int gi = r0 + rr, gj = c0 + kT + cb + u;
+      if (gi < m && gj < n) M[(int64_t)gi * n + gj] = mo[1][rr][cb + u] + o[u];
     }
   }
   red[t] = eacc;
@@ -350,17 +382,18 @@ __global__ __launch_bounds__(kTh) void tile2d_kernel(const T* __restrict__ X, in
   if (t == 0) errp[(int64_t)I * Nb + J] = red[0];
 }
 
-// KC: feedback to the tiles to the right.  Work-group (tile, chunk) adds
-// E(I, J) U_P(J, J'') to M(I, J'') for J'' in J + 1 + [8 chunk, 8 chunk + 8), on
+// KC: feedback to the tiles to the right but one (the tile kernel itself feeds
+// its right neighbour, J + 1).  Work-group (tile, chunk) adds E(I, J) U_P(J, J'')
+// to M(I, J'') for J'' in J + 2 + [8 chunk, 8 chunk + 8), on
 // v_mfma_f32_32x32x2f32: E from LDS, U_P rows straight from memory (coalesced),
 // wave w taking J'' = j0 + w and + w + 4 and writing its own output tiles.
-__global__ __launch_bounds__(kTh) void feed2d_kernel(int m, int n, const float* __restrict__ UP,
-                                                     float* __restrict__ M, const float* __restrict__ E, int K,
-                                                     int I_lo, int Nb, int nchunk) {
+__device__ __forceinline__ void feed2d_body(int bid, int m, int n, const float* __restrict__ UP,
+                                            float* __restrict__ M, const float* __restrict__ E, int K, int I_lo,
+                                            int Nb, int nchunk) {
   __shared__ float se[kT][kT + 1];
-  const int tile = (int)blockIdx.x / nchunk, ch = (int)blockIdx.x % nchunk;
+  const int tile = bid / nchunk, ch = bid % nchunk;
   const int I = I_lo + tile, J = K - I;
-  const int j0 = J + 1 + ch * kChunk, j1 = min(j0 + kChunk, Nb);
+  const int j0 = J + 2 + ch * kChunk, j1 = min(j0 + kChunk, Nb);
   if (j0 >= j1) return;
   const int r0 = I * kT, c0 = J * kT;
   const int t = threadIdx.x, lane = t & 63, w = t >> 6, col = lane & 31, kh = lane >> 5;
@@ -405,6 +438,22 @@ __global__ __launch_bounds__(kTh) void feed2d_kernel(int m, int n, const float* 
       if (gi < m && gj < n) M[(int64_t)gi * n + gj] = mv[u][r] + acc[r];
     }
   }
+}
+
+// One launch between two tile sweeps: the feedback of anti-diagonal K - 1 (the
+// first nfeed work-groups) and the partial corrections of anti-diagonal K.  They
+// touch disjoint parts of M: the correction of tile (I, K - I) reads M(I', K - I)
+// for I' <= I, which the feedback of anti-diagonal K - 1 (tile (I', K - 1 - I')
+// to J'' >= K + 1 - I') never writes.
+__global__ __launch_bounds__(kTh) void fc2d_kernel(int m, int n, const float* __restrict__ UQ,
+                                                   const float* __restrict__ UP, float* __restrict__ M,
+                                                   const float* __restrict__ E, float* __restrict__ part, int Kf,
+                                                   int lo_f, int ncc, int nfeed, int K, int lo, int nca, int Nb) {
+  const int b = (int)blockIdx.x;
+  if (b < nfeed)
+    feed2d_body(b, m, n, UP, M, E, Kf, lo_f, Nb, ncc);
+  else
+    corr2d_body(b - nfeed, m, n, UQ, M, part, K, lo, nca);
 }
 
 __global__ __launch_bounds__(kTh) void err2d_kernel(const double* __restrict__ errp, int64_t count,
@@ -468,18 +517,22 @@ hipError_t quantize2d_launch(const Plan2D& p, const void* X, int x_dtype, int64_
   for (int K = 0; K <= Mb + Nb - 2; ++K) {
     const int lo = std::max(0, K - Nb + 1), hi = std::min(K, Mb - 1), ntile = hi - lo + 1;
     const int nca = (hi + kChunk) / kChunk;              // correction chunks of the deepest tile
-    hipLaunchKernelGGL(corr2d_kernel, dim3(ntile * nca), dim3(kTh), 0, s, (int)p.m, (int)p.n, UQ, M, cpart, K, lo,
-                       nca);
+    // feedback of anti-diagonal K - 1 past the right neighbours, in the same launch
+    int lo_f = 0, ncc = 0, nfeed = 0;
+    if (K >= 1) {
+      const int Kf = K - 1, hi_f = std::min(Kf, Mb - 1);
+      lo_f = std::max(0, Kf - Nb + 1);
+      ncc = (Nb - (Kf - hi_f) - 2 + kChunk - 1) / kChunk;   // chunks of the leftmost tile
+      nfeed = ncc > 0 ? (hi_f - lo_f + 1) * ncc : 0;
+    }
+    hipLaunchKernelGGL(fc2d_kernel, dim3(nfeed + ntile * nca), dim3(kTh), 0, s, (int)p.m, (int)p.n, UQ, UP, M, E,
+                       cpart, K - 1, lo_f, std::max(ncc, 1), nfeed, K, lo, nca, Nb);
     if (x_dtype == 1)
       hipLaunchKernelGGL(tile2d_kernel<_Float16>, dim3(ntile), dim3(kTh), 0, s, (const _Float16*)X, ldx, (int)p.m,
                          (int)p.n, UQ, UP, M, E, cpart, gridv, maxq, codes, ldc, errp, K, lo, Nb, nca);
     else
       hipLaunchKernelGGL(tile2d_kernel<float>, dim3(ntile), dim3(kTh), 0, s, (const float*)X, ldx, (int)p.m,
                          (int)p.n, UQ, UP, M, E, cpart, gridv, maxq, codes, ldc, errp, K, lo, Nb, nca);
-    const int ncc = (Nb - (K - hi) - 1 + kChunk - 1) / kChunk;   // feedback chunks of the leftmost tile
-    if (ncc > 0)
-      hipLaunchKernelGGL(feed2d_kernel, dim3(ntile * ncc), dim3(kTh), 0, s, (int)p.m, (int)p.n, UP, M, E, K, lo, Nb,
-                         ncc);
   }
   hipLaunchKernelGGL(err2d_kernel, dim3(1), dim3(kTh), 0, s, errp, p.Mb * p.Nb, out_err);
   return hipGetLastError();
