@@ -168,14 +168,16 @@ __global__ __launch_bounds__(kTh) void tile2d_kernel(const T* __restrict__ X, in
   constexpr int kUQ = kT + 4;            // pitch of uqt: rows 16-byte aligned, row reads spread over banks
   constexpr int kRun = 2 * kT - 1;       // reversed column j of U_P: rv[z] = U_P[kRun - 1 - z][j]
   constexpr int kUW = 3 * kT + 4;        // pitch of a reversed column (a run starts at z <= 62, ends <= 93)
-  __shared__ float xs[kT][kT];           // X - C, then the tile's E (pitch 32: an anti-diagonal's
-                                         // entries fall in 32 different banks)
+  __shared__ float xs[kT + 1][kT];       // X - C, then the tile's E (pitch 32: an anti-diagonal's
+                                         // entries fall in 32 different banks); row 32 takes the
+                                         // sweep's discarded writes
   __shared__ __attribute__((aligned(16))) float uqt[kT][kUQ];      // uqt[i][i'] = U_Q(I, I)[i'][i]
   __shared__ __attribute__((aligned(16))) float upw[4][kT][kUW];   // upw[r][j][z] = rv_j[z + r]
   __shared__ float up[kT][kT + 1];       // U_P(J, J), staged for upw; then the tile's part of M
   __shared__ float fac[kT][kT];          // (1 / U_Q[i][i]) / U_P[j][j]
-  __shared__ __attribute__((aligned(16))) float es[kT];            // the step's errors, by row
-  __shared__ uint8_t cs[kT][kT];         // codes
+  __shared__ __attribute__((aligned(16))) float es[kT + 4];        // the step's errors, by row (+ a
+                                                                   // slot for discarded writes)
+  __shared__ uint8_t cs[kT + 1][kT];     // codes (row 32: discarded writes)
   __shared__ float upn[kT][kT + 1];      // U_P(J, J + 1), for the right neighbour's feedback
   __shared__ float mo[2][kT][kT];        // M(I, J) and M(I, J + 1) as they stand
   __shared__ double red[kTh];
@@ -277,38 +279,38 @@ __global__ __launch_bounds__(kTh) void tile2d_kernel(const T* __restrict__ X, in
     };
     fetch(0);
     for (int s = 0; s < kRun; ++s) {
+      // every lane runs every instruction of a step (no branches): a lane whose
+      // column has no entry on this anti-diagonal computes on row ic's operands
+      // and sends its writes to the spare row and slot
       const int i = s - j;
-      if (i >= 0 && i < kT) {
-        // dot product over i' <= i (U_Q upper: uqt[i][i'] = 0 past i), each half
-        // over its 16 rows, the halves added by a swap of lanes j and j + 32
-        float dq[4] = {0.f, 0.f, 0.f, 0.f};
+      const bool inr = (unsigned)i < (unsigned)kT;
+      const bool val = inr && colv && r0 + i < m;
+      // dot product over i' <= i (U_Q upper: uqt[i][i'] = 0 past i), each half
+      // over its 16 rows, the halves added by a swap of lanes j and j + 32
+      float dq[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int q = 0; q < kH / 4; ++q)
+      for (int q = 0; q < kH / 4; ++q)
 #pragma unroll
-          for (int r = 0; r < 4; ++r) dq[r] = fmaf(un[q][r], mc[4 * q + r], dq[r]);
-        const float dh = (dq[0] + dq[1]) + (dq[2] + dq[3]);
-        // swap the upper half of one copy with the lower half of another: the
-        // first result then holds rows 0-15's sum and the second rows 16-31's, in
-        // both halves (the results are copied out as scalars before the casts)
-        const unsigned du = __builtin_bit_cast(unsigned, dh);
-        const auto sw = __builtin_amdgcn_permlane32_swap(du, du, false, false);
-        const unsigned lo = sw[0], hi = sw[1];
-        const float d = __builtin_bit_cast(float, lo) + __builtin_bit_cast(float, hi);
-        const float v = xn - d;
-        const float c = fminf(fmaxf(rintf(v * rs) + zero, 0.f), fmaxq);
-        float e = (v - scale * (c - zero)) * fn;
-        if (!(colv && r0 + i < m)) e = 0.f;
-        if (h == 0) {
-          if (colv && r0 + i < m) {
-            cs[i][j] = (uint8_t)c;
-            eacc += (double)e * (double)e;
-            xs[i][j] = e;
-          }
-          es[i] = e;
-        }
-      }
+        for (int r = 0; r < 4; ++r) dq[r] = fmaf(un[q][r], mc[4 * q + r], dq[r]);
+      const float dh = (dq[0] + dq[1]) + (dq[2] + dq[3]);
+      // swap the upper half of one copy with the lower half of another: the
+      // first result then holds rows 0-15's sum and the second rows 16-31's, in
+      // both halves (the results are copied out as scalars before the casts)
+      const unsigned du = __builtin_bit_cast(unsigned, dh);
+      const auto sw = __builtin_amdgcn_permlane32_swap(du, du, false, false);
+      const unsigned lo = sw[0], hi = sw[1];
+      const float d = __builtin_bit_cast(float, lo) + __builtin_bit_cast(float, hi);
+      const float v = xn - d;
+      const float c = fminf(fmaxf(rintf(v * rs) + zero, 0.f), fmaxq);
+      const float e = val ? (v - scale * (c - zero)) * fn : 0.f;
+      const double de = h == 0 ? (double)e : 0.0;
+      eacc = fma(de, de, eacc);
+      const int iw = (val && h == 0) ? i : kT;
+      cs[iw][j] = (uint8_t)c;
+      xs[iw][j] = e;
+      es[(inr && h == 0) ? i : kT] = e;
       // row s - 32 had its last entry (column 31) in the previous step
-      if (t == kT - 1 && s >= kT) es[s - kT] = 0.f;
+      es[(t == kT - 1 && s >= kT) ? s - kT : kT] = 0.f;
       // the writes above come before the reads below in this wave's LDS queue,
       // which the hardware keeps in order; only the compiler must not move them
       __atomic_signal_fence(__ATOMIC_SEQ_CST);
@@ -322,7 +324,7 @@ __global__ __launch_bounds__(kTh) void tile2d_kernel(const T* __restrict__ X, in
 #pragma unroll
         for (int q = 0; q < kH / 4; ++q) uv[q] = run[q];
       }
-      if (s + 1 < kRun) fetch(s + 1);
+      fetch(s + 1);   // past the last step it reads a clamped row and is not used
       // M[k][j] += e_k U_P[s - k][j]; rows without an entry in this step have
       // e_k = 0, and U_P[s - k][j] = 0 where s - k is not in 0 .. j
 #pragma unroll
