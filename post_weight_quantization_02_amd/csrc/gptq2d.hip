@@ -303,8 +303,6 @@ __global__ __launch_bounds__(kTh) void tile2d_kernel(const T* __restrict__ X, in
       const float v = xn - d;
       const float c = fminf(fmaxf(rintf(v * rs) + zero, 0.f), fmaxq);
       const float e = val ? (v - scale * (c - zero)) * fn : 0.f;
-      const double de = h == 0 ? (double)e : 0.0;
-      eacc = fma(de, de, eacc);
       const int iw = (val && h == 0) ? i : kT;
       cs[iw][j] = (uint8_t)c;
       xs[iw][j] = e;
@@ -349,12 +347,14 @@ __global__ __launch_bounds__(kTh) void tile2d_kernel(const T* __restrict__ X, in
     }
   }
   __syncthreads();
-  // E, codes and M(I, J) += the tile's part of M
+  // E (and its squares, in fp64), codes and M(I, J) += the tile's part of M
 #pragma unroll
   for (int u = 0; u < 4; ++u) {
     const int gi = r0 + rr, gj = c0 + cb + u;
     if (gi < m && gj < n) {
-      E[(int64_t)gi * n + gj] = xs[rr][cb + u];
+      const float e = xs[rr][cb + u];
+      E[(int64_t)gi * n + gj] = e;
+      eacc += (double)e * (double)e;
       codes[(int64_t)gi * ldc + gj] = cs[rr][cb + u];
       M[(int64_t)gi * n + gj] = mo[0][rr][cb + u] + up[rr][cb + u];
     }
