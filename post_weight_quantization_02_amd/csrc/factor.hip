@@ -231,7 +231,9 @@ __device__ __forceinline__ void static_for(F&& f) {
 // alone, one row per lane in registers (pivot-row values by readlane:
 // a_jc = a_cj sits in lane c), and stores
 //   W  = pivot-time column values a_ij (i >= j) in the lower part of S0,
-//   M^T in the upper part of S0 (row j, columns i > j), d_j in dv, 1/d_j in rdv.
+//   M^T in the upper part of S0 (row j, columns i > j); d_j is W's diagonal.
+// Wave 0 stores without branches: a lane's store that has no place in S0 goes
+// to its own slot of a sink array that nothing reads.
 // The rank-8 update of Dm right of the panel runs on fp64 MFMA in 16x16 tiles:
 // wave 0 takes the next 16 columns and goes on to the next panel at once.
 // The stacked rows T follow one panel behind, off wave 0's path: each of waves
@@ -294,12 +296,11 @@ __device__ __forceinline__ void rank8_tiles(double* S0, double* S1, int lane, De
 
 // wave 0: eliminate panel P (columns 8P .. 8P+7) of Dm, one row per lane
 template <int P>
-__device__ __forceinline__ void ldl_dm_panel(double* S0, double* dv, double* rdv, int lane) {
+__device__ __forceinline__ void ldl_dm_panel(double* S0, double* sink, int lane) {
   constexpr int J0 = 8 * P;
   double v[8], mu[8];
 #pragma unroll
   for (int c = 0; c < 8; ++c) v[c] = S0[lane * kP + J0 + c];
-  double dsel = 0.0, rsel = 0.0;
 #pragma unroll
   for (int jj = 0; jj < 8; ++jj) {
     const double dj = readlane_f64(v[jj], J0 + jj);
@@ -310,36 +311,31 @@ __device__ __forceinline__ void ldl_dm_panel(double* S0, double* dv, double* rdv
     mu[jj] = (lane > J0 + jj) ? v[jj] * rd : 0.0;
 #pragma unroll
     for (int j2 = jj + 1; j2 < 8; ++j2) v[j2] = fma(-mu[jj], s[j2], v[j2]);
-    dsel = (lane == jj) ? dj : dsel;
-    rsel = (lane == jj) ? rd : rsel;
   }
-  if (lane < 8) {
-    dv[J0 + lane] = dsel;
-    rdv[J0 + lane] = rsel;
-  }
+  // W (lower part, with d_j = W[j][j]), then M^T (upper part): disjoint places
 #pragma unroll
-  for (int c = 0; c < 8; ++c)
-    if (lane >= J0 + c) S0[lane * kP + J0 + c] = v[c];
+  for (int c = 0; c < 8; ++c) *((lane >= J0 + c) ? &S0[lane * kP + J0 + c] : &sink[lane]) = v[c];
 #pragma unroll
-  for (int c = 0; c < 8; ++c)
-    if (lane > J0 + c) S0[(J0 + c) * kP + lane] = mu[c];
+  for (int c = 0; c < 8; ++c) *((lane > J0 + c) ? &S0[(J0 + c) * kP + lane] : &sink[lane]) = mu[c];
 }
 
 // rows row0 .. row0 + nrows - 1 of T (one per lane): the same eliminations of
 // panel P, t_j <- t_j / d_j, then t_j2 -= t_j a_{j, j2} (a_{j, j2} = W[j2][j]),
-// leaving the multipliers m_T in the panel columns
+// leaving the multipliers m_T in the panel columns.  1/d_j is formed here from
+// W's diagonal, as wave 0 formed it from the same d_j.
 template <int P>
-__device__ __forceinline__ void t_panel(const double* S0, double* S1, const double* rdv, int lane, int row0,
-                                        int nrows) {
+__device__ __forceinline__ void t_panel(const double* S0, double* S1, int lane, int row0, int nrows) {
   constexpr int J0 = 8 * P;
   if (lane >= nrows) return;
   double* r = S1 + (row0 + lane) * kP + J0;
-  double tv[8];
+  double tv[8], rd[8];
 #pragma unroll
   for (int c = 0; c < 8; ++c) tv[c] = r[c];
 #pragma unroll
+  for (int jj = 0; jj < 8; ++jj) rd[jj] = rcp_f64(S0[(J0 + jj) * kP + J0 + jj]);
+#pragma unroll
   for (int jj = 0; jj < 8; ++jj) {
-    tv[jj] *= rdv[J0 + jj];
+    tv[jj] *= rd[jj];
 #pragma unroll
     for (int j2 = jj + 1; j2 < 8; ++j2) tv[j2] = fma(-tv[jj], S0[(J0 + j2) * kP + J0 + jj], tv[j2]);
   }
@@ -353,9 +349,9 @@ __device__ __forceinline__ void tri_ab(int i, int& a, int& b) {
   b = i - (a - 1) * a / 2 + 1;
 }
 
-__device__ __forceinline__ void ldl_stacked(double* S0, double* S1, double* dv, double* rdv, int t) {
+__device__ __forceinline__ void ldl_stacked(double* S0, double* S1, double* sink, int t) {
   const int lane = t & 63, w = t >> 6;
-  if (w == 0) ldl_dm_panel<0>(S0, dv, rdv, lane);
+  if (w == 0) ldl_dm_panel<0>(S0, sink, lane);
   __syncthreads();
   static_for<0, kNB / 8>([&](auto PP) {
     constexpr int P = decltype(PP)::value;
@@ -365,17 +361,17 @@ __device__ __forceinline__ void ldl_stacked(double* S0, double* S1, double* dv, 
     if (w == 0) {
       if constexpr (nT > 0) {
         rank8_tiles<J0, nT>(S0, S1, lane, [&](int u) { return TileDesc{kTileDm, T0 + 16 * u, T0}; });
-        ldl_dm_panel<P + 1>(S0, dv, rdv, lane);
+        ldl_dm_panel<P + 1>(S0, sink, lane);
       }
     } else if (w == 1) {
-      t_panel<P>(S0, S1, rdv, lane, 0, 32);
+      t_panel<P>(S0, S1, lane, 0, 32);
       if constexpr (nT > 0)
         rank8_tiles<J0, 2 * nT>(S0, S1, lane, [&](int u) {
           return TileDesc{kTileT, 16 * (u / nT), T0 + 16 * (u % nT)};
         });
     } else {
       const int q = w;  // T rows 16 q .. 16 q + 15 (q = 2, 3)
-      t_panel<P>(S0, S1, rdv, lane, 16 * q, 16);
+      t_panel<P>(S0, S1, lane, 16 * q, 16);
       if constexpr (nT > 0)
         rank8_tiles<J0, nT + (nDm + 1) / 2>(S0, S1, lane, [&](int u) {
           if (u < nT) return TileDesc{kTileT, 16 * q, T0 + 16 * u};
@@ -450,7 +446,7 @@ __device__ __forceinline__ void mma_nt_stream(const double* __restrict__ A, int6
 
 struct PanelSmem {
   double S0[kNB * kP], S1[kNB * kP];
-  double dv[kNB], rdv[kNB], sq[kNB], rsq[kNB];
+  double sink[kNB], sq[kNB], rsq[kNB];   // sink: the LDL's discarded stores
   int fail;
 };
 
@@ -507,9 +503,9 @@ __device__ __forceinline__ void task_panel(const StepArgs a, int b, PanelSmem& s
       }
   if (t == 0) sm.fail = kNB;
   __syncthreads();
-  ldl_stacked(sm.S0, sm.S1, sm.dv, sm.rdv, t);
+  ldl_stacked(sm.S0, sm.S1, sm.sink, t);
   if (t < kNB) {
-    const double dj = sm.dv[t];
+    const double dj = sm.S0[t * kP + t];
     if (!(dj > 0.0)) atomicMin(&sm.fail, t);
     sm.sq[t] = sqrt(dj);
     sm.rsq[t] = 1.0 / sm.sq[t];
