@@ -40,8 +40,8 @@ __device__ __forceinline__ void static_for(F&& f) {
 // lane (16 * (lane / 16) + K) of the caller's DPP row, broadcast to the row
 template <int K>
 __device__ __forceinline__ float row_bcast(float v) {
-  return __builtin_bit_cast(
-      float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x150 + K, 0xF, 0xF, false));
+  // every lane is written (full row and bank masks), so no old value is kept
+  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0x150 + K, 0xF, 0xF, true));
 }
 
 __device__ __forceinline__ void grid_from_minmax(float mn, float mx, int maxq, float& s, float& z) {
@@ -175,19 +175,18 @@ struct PanelLds {
   double red[kThreads / 64];
 };
 
-template <int CPL, int GIN, bool FULL, int EMODE>
+template <int CPL, int GIN, bool FULL, int EMODE, bool PRE = false>
 __device__ __forceinline__ void panel_body(
     float* __restrict__ W, int d_row, int d_col, int i1, int width,
     const float* __restrict__ U, int maxq, int gwide, int ngroups,
     uint8_t* __restrict__ codes, float* __restrict__ scales, int32_t* __restrict__ zeros,
     float* __restrict__ E, double* __restrict__ part_e, const float* __restrict__ Eprev,
-    float (&er)[CPL], PanelLds<CPL>& L) {
+    float (&er)[CPL], PanelLds<CPL>& L, double& se, float (&ush)[2][CPL == 8 ? 32 : 1]) {
   constexpr int B = 16 * CPL;
   static_assert(GIN == 0 || (GIN % 16 == 0 && B % GIN == 0), "group inside block");
   static_assert(EMODE == kEprevMem || (FULL && CPL == 8), "shares from registers: full blocks of 128");
   float* Us = L.Us;
   float* rd = L.rd;
-  double* red = L.red;
   const int t = threadIdx.x;
   const size_t ldu = (size_t)d_col;
   // stage U's diagonal block in LDS.  Full blocks of 64 or 128 columns: whole
@@ -203,6 +202,26 @@ __device__ __forceinline__ void panel_body(
   constexpr int kRows0 = 32;                            // rows of the first part
   constexpr int kLoads0 = kRows0 / kRowsPerLoad;
   static_assert(!kDma || (kLoads0 % 4 == 0 && kLoads % 4 == 0), "loads per wave");
+  // The previous block's share on full blocks of 128 runs on the matrix cores
+  // (v_mfma_f32_16x16x4f32: 16 rows of the work-group x 32 columns per wave,
+  // K = 128).  Its B operand, U[i1 - B + k][i1 + 32 wave + n], lane l holding
+  // rows k = 4 kk + l / 16 and column n = 16 tt + l % 16, is loaded early: by
+  // the previous block of the same launch right after its column loop (PRE),
+  // else here, ahead of the diagonal block's staging.
+  constexpr bool kShareMfma = FULL && CPL == 8;
+  const bool share = EMODE == kEprevRegs || Eprev != nullptr;
+  auto share_loads = [&](int ib) {
+    const int l = t & 63, wv = __builtin_amdgcn_readfirstlane(t >> 6);
+    const float* us = U + (size_t)(ib - B + (l >> 4)) * ldu + ib + 32 * wv + (l & 15);
+#pragma unroll
+    for (int kk = 0; kk < B / 4; ++kk)
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt) ush[tt][kk] = us[(size_t)(4 * kk) * ldu + 16 * tt];
+  };
+  static_assert(!PRE || kShareMfma, "operands of the next block's share: full blocks of 128");
+  if constexpr (kShareMfma && EMODE == kEprevMem) {
+    if (share) share_loads(i1);
+  }
   const float udg = (t < width) ? U[(size_t)(i1 + t) * ldu + i1 + t] : 1.f;
   if constexpr (kDma) {
     const int w4 = __builtin_amdgcn_readfirstlane(t >> 6), l = t & 63;
@@ -259,41 +278,28 @@ __device__ __forceinline__ void panel_body(
     w[r] = (FULL || col < width) ? W[rowc * d_col + i1 + col] : 0.f;
     cr[r] = 0.f;
   }
-  if (EMODE == kEprevRegs || Eprev) {
-    // E_prev is stored [k][row].  U rows are 16-byte aligned here (the caller
-    // pairs blocks only then).
-    if constexpr (FULL && CPL == 8) {
-      // Each wave computes its 4 rows x 128 columns with lane l owning columns
-      // 2l, 2l + 1 of all four, so a U row is read once per wave (coalesced).
-      // The wave's E_prev words (128 k x 4 rows) are first copied to its own LDS
-      // strip and read back four at a time, the same address in every lane; the
-      // sums then reach the column-loop layout through the same strip.  U comes
-      // 16 rows of k at a time, the next chunk's loads issued before this
-      // chunk's FMAs.  Words written by one lane and read by another are
-      // ordered by a work-group barrier with LDS-only fences (the diagonal
-      // block's direct-to-LDS loads may stay in flight across it).
-      const int wv = __builtin_amdgcn_readfirstlane(t >> 6);
-      float* el = L.dl + wv * 4 * B;
-      const int erl = std::min((int)blockIdx.x * 16 + wv * 4 + (lane & 3), d_row - 1);
-      const float* up = U + (size_t)(i1 - B) * ldu + i1 + 2 * lane;
-      constexpr int KC = 16;
-      static_assert(B % KC == 0, "chunks of k");
-      float2 ua[2][KC];
-      float acc[4][2];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) acc[i][0] = acc[i][1] = 0.f;
-      auto ld = [&](int buf, int k0) {
-#pragma unroll
-        for (int k = 0; k < KC; ++k) ua[buf][k] = *(const float2*)(up + (size_t)(k0 + k) * ldu);
-      };
-      ld(0, 0);  // in flight while E_prev is staged
+  if (share) {
+    // E_prev is stored [k][row].
+    if constexpr (kShareMfma) {
+      // W[rows, block] -= E_prev U[i1 - B:i1, block]: E_prev staged in LDS as
+      // [k][16 rows] (the A operand, from the registers of the work-group's own
+      // previous block or from memory), U from the registers loaded above; the
+      // 16 x 128 product returns to the column layout through the same LDS.
+      // Words written by one lane and read by another are ordered by a
+      // work-group barrier with LDS-only fences (the diagonal block's
+      // direct-to-LDS loads may stay in flight across it).
+      float* es = L.dl;  // 16 B floats: [k][16] for E_prev, then [16][B] for the product
+      const int rl = (t >> 6) * 4 + (lane >> 4);
       if constexpr (EMODE == kEprevRegs) {
-        // this lane's row is row lane / 16 of the wave; its errors are columns p CPL + r
 #pragma unroll
-        for (int r = 0; r < CPL; ++r) el[4 * (p * CPL + r) + (lane >> 4)] = er[r];
+        for (int r = 0; r < CPL; ++r) es[(p * CPL + r) * 16 + rl] = er[r];
       } else {
 #pragma unroll
-        for (int j = 0; j < B / 16; ++j) el[j * 64 + lane] = Eprev[(size_t)(j * 16 + (lane >> 2)) * d_row + erl];
+        for (int q = 0; q < 16 * B / kThreads; ++q) {
+          const int idx = q * kThreads + t;
+          const int erow = std::min((int)blockIdx.x * 16 + (idx & 15), d_row - 1);
+          es[idx] = Eprev[(size_t)(idx >> 4) * d_row + erow];
+        }
       }
       auto lds_sync = [] {
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
@@ -301,25 +307,33 @@ __device__ __forceinline__ void panel_body(
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
       };
       lds_sync();
-      static_for<0, B / KC>([&](auto cc) {
-        constexpr int c = decltype(cc)::value;
-        if constexpr ((c + 1) * KC < B) ld((c + 1) & 1, (c + 1) * KC);
+      // two independent chains per column tile (the even and odd k steps)
+      f32x4 acc[2][2];
 #pragma unroll
-        for (int k = 0; k < KC; ++k) {
-          const f32x4 e = *(const f32x4*)&el[4 * (c * KC + k)];
+      for (int h = 0; h < 2; ++h) acc[h][0] = acc[h][1] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            acc[i][0] = fmaf(e[i], ua[c & 1][k].x, acc[i][0]);
-            acc[i][1] = fmaf(e[i], ua[c & 1][k].y, acc[i][1]);
-          }
-        }
-      });
-      lds_sync();  // every lane's E words read
+      for (int kk = 0; kk < B / 4; ++kk) {
+        const float a = es[(4 * kk + (lane >> 4)) * 16 + (lane & 15)];
+        acc[kk & 1][0] = __builtin_amdgcn_mfma_f32_16x16x4f32(a, ush[0][kk], acc[kk & 1][0], 0, 0, 0);
+        acc[kk & 1][1] = __builtin_amdgcn_mfma_f32_16x16x4f32(a, ush[1][kk], acc[kk & 1][1], 0, 0, 0);
+      }
 #pragma unroll
-      for (int i = 0; i < 4; ++i) *(float2*)&el[i * B + 2 * lane] = make_float2(acc[i][0], acc[i][1]);
+      for (int tt = 0; tt < 2; ++tt) acc[0][tt] += acc[1][tt];
+      lds_sync();  // every E word read
+      // lane l holds rows 4 (l / 16) + i, column 32 wave + 16 tt + l % 16
+      const int wv = t >> 6;
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) es[(4 * (lane >> 4) + i) * B + 32 * wv + 16 * tt + (lane & 15)] = acc[0][tt][i];
       lds_sync();
+      const f32x4 s0 = *(const f32x4*)&es[rl * B + p * CPL];
+      const f32x4 s1 = *(const f32x4*)&es[rl * B + p * CPL + 4];
 #pragma unroll
-      for (int r = 0; r < CPL; ++r) w[r] -= el[(lane >> 4) * B + p * CPL + r];
+      for (int r = 0; r < 4; ++r) {
+        w[r] -= s0[r];
+        w[4 + r] -= s1[r];
+      }
     } else {
       const float* ep = Eprev + rowc;
       const float* up = U + (size_t)(i1 - B) * ldu + i1 + p * CPL;
@@ -363,64 +377,93 @@ __device__ __forceinline__ void panel_body(
 #pragma unroll
   for (int j = 0; j < kPF; ++j) uload(j, ub[j]);
 
+  // the grid of the group starting at column j, from the current weights
+  auto group_start = [&](auto jc) {
+    constexpr int j = decltype(jc)::value;
+    // group [j, j + GIN): lanes j/CPL .. (j+GIN)/CPL - 1 of the row hold it
+    constexpr int l0 = j / CPL, l1 = (j + GIN) / CPL;
+    float mn = INFINITY, mx = -INFINITY;
+    const bool mine = (p >= l0 && p < l1);
+#pragma unroll
+    for (int r = 0; r < CPL; ++r) {
+      const bool in = mine && (FULL || p * CPL + r < width);
+      mn = in ? fminf(mn, w[r]) : mn;
+      mx = in ? fmaxf(mx, w[r]) : mx;
+    }
+#pragma unroll
+    for (int o = 8; o > 0; o >>= 1) {
+      mn = fminf(mn, __shfl_xor(mn, o, 16));
+      mx = fmaxf(mx, __shfl_xor(mx, o, 16));
+    }
+    grid_from_minmax(mn, mx, maxq, s, z);
+    rs = 1.f / s;
+    nz = -z;
+    mz = fmaxq - z;
+    if (p == 0 && valid) {
+      const int gi = (i1 + j) / GIN;
+      scales[rowc * ngroups + gi] = s;
+      zeros[rowc * ngroups + gi] = (int32_t)z;
+    }
+  };
+  // code and scaled error of the column in register jj (every lane computes
+  // it on its own register; the owner lane's values are the column's)
+  auto quant = [&](auto jc, float& e, float& c) {
+    constexpr int jj = decltype(jc)::value;
+    const float x = w[jj];
+    const float cz = __builtin_amdgcn_fmed3f(rintf(x * rs), nz, mz);
+    e = fmaf(-s, cz, x) * rdl[jj];
+    c = cz + z;
+  };
+
+  // Column j's e and c are ready when step j starts: step j broadcasts e,
+  // updates column j + 1 first and computes its e and c in the same scheduling
+  // region as the rest of step j's updates, which fill that chain's latency.
+  // A group start ends the region first (its grid needs every update).
+  float ecur = 0.f, ccur = 0.f;
+  if constexpr (GIN != 0) group_start(std::integral_constant<int, 0>{});
+  quant(std::integral_constant<int, 0>{}, ecur, ccur);
   static_for<0, 16>([&](auto kc) {
     constexpr int kk = decltype(kc)::value;
     static_for<0, CPL>([&](auto jc) {
       constexpr int jj = decltype(jc)::value;
       constexpr int j = kk * CPL + jj;
       if (FULL || j < width) {
-        if constexpr (GIN != 0 && j % GIN == 0) {
-          // group [j, j + GIN): lanes j/CPL .. (j+GIN)/CPL - 1 of the row hold it
-          constexpr int l0 = j / CPL, l1 = (j + GIN) / CPL;
-          float mn = INFINITY, mx = -INFINITY;
-          const bool mine = (p >= l0 && p < l1);
-#pragma unroll
-          for (int r = 0; r < CPL; ++r) {
-            const bool in = mine && (FULL || p * CPL + r < width);
-            mn = in ? fminf(mn, w[r]) : mn;
-            mx = in ? fmaxf(mx, w[r]) : mx;
-          }
-#pragma unroll
-          for (int o = 8; o > 0; o >>= 1) {
-            mn = fminf(mn, __shfl_xor(mn, o, 16));
-            mx = fmaxf(mx, __shfl_xor(mx, o, 16));
-          }
-          grid_from_minmax(mn, mx, maxq, s, z);
-          rs = 1.f / s;
-          nz = -z;
-          mz = fmaxq - z;
-          if (p == 0 && valid) {
-            const int gi = (i1 + j) / GIN;
-            scales[rowc * ngroups + gi] = s;
-            zeros[rowc * ngroups + gi] = (int32_t)z;
-          }
-        }
         if constexpr (kDma && kRows0 < B && j == kRows0 - kPF)
           asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
-        const float x = w[jj];
-        const float cz = __builtin_amdgcn_fmed3f(rintf(x * rs), nz, mz);
-        const float e = fmaf(-s, cz, x) * rdl[jj];
-        const float c = cz + z;
-        const bool own = (p == kk);
-        cr[jj] = own ? c : cr[jj];
-        er[jj] = own ? e : er[jj];
-        const float eb = row_bcast<kk>(e);
+        const float eb = row_bcast<kk>(ecur);
         const f32x4* u = ub[j % kPF];
-        if constexpr (CPL >= 4) {
+        constexpr int jn = (jj + 1) % CPL;
+        constexpr bool kNext = j + 1 < B;
+        constexpr bool kNextGroup = kNext && GIN != 0 && (j + 1) % GIN == 0;
+        w[jn] = fmaf(-eb, u[jn / 4][jn % 4], w[jn]);
+        float enx = 0.f, cnx = 0.f;
+        if constexpr (kNext && !kNextGroup) quant(std::integral_constant<int, jn>{}, enx, cnx);
 #pragma unroll
-          for (int q = 0; q < kQ; ++q)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) w[4 * q + r] = fmaf(-eb, u[q][r], w[4 * q + r]);
-        } else {
-#pragma unroll
-          for (int r = 0; r < CPL; ++r) w[r] = fmaf(-eb, u[0][r], w[r]);
-        }
+        for (int r = 0; r < CPL; ++r)
+          if (r != jn) w[r] = fmaf(-eb, u[r / 4][r % 4], w[r]);
+        const bool own = (p == kk);
+        cr[jj] = own ? ccur : cr[jj];
+        er[jj] = own ? ecur : er[jj];
+        asm volatile("" : "+v"(cr[jj]), "+v"(er[jj]));
         if constexpr (j + kPF < B) uload(j + kPF, ub[j % kPF]);
+        // The owner's e and c are selected inside their own step (the empty asm
+        // above) and nothing crosses a step (this barrier): left free, the
+        // compiler keeps every step's e and c live to the end of the block and
+        // then sinks each U-row prefetch to one step ahead of its use
+        __builtin_amdgcn_sched_barrier(0);
+        if constexpr (kNextGroup) {
+          if (FULL || j + 1 < width) {
+            group_start(std::integral_constant<int, j + 1>{});
+            quant(std::integral_constant<int, jn>{}, enx, cnx);
+          }
+        }
+        ecur = enx;
+        ccur = cnx;
       }
     });
   });
 
-  double se = 0.0;
+  if constexpr (PRE) share_loads(i1 + B);
 #pragma unroll
   for (int r = 0; r < CPL; ++r) {
     const int col = p * CPL + r;
@@ -430,8 +473,18 @@ __device__ __forceinline__ void panel_body(
       se += (double)er[r] * (double)er[r];
     }
   }
+  // the next block's diagonal staging (pair launches) overwrites the LDS this
+  // block's waves read
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+// the work-group's sum of its lanes' squared errors, added to its partial
+__device__ __forceinline__ void panel_error_sum(double se, double* __restrict__ part_e, double* red) {
+  const int t = threadIdx.x;
   for (int o = 32; o > 0; o >>= 1) se += __shfl_xor(se, o, 64);
-  if (lane == 0) red[t >> 6] = se;
+  if ((t & 63) == 0) red[t >> 6] = se;
   __syncthreads();
   if (t == 0) part_e[blockIdx.x] += (red[0] + red[1]) + (red[2] + red[3]);
 }
@@ -444,8 +497,11 @@ __global__ __launch_bounds__(kThreads) void panel_kernel(
     float* __restrict__ E, double* __restrict__ part_e, const float* __restrict__ Eprev) {
   __shared__ __attribute__((aligned(16))) PanelLds<CPL> L;
   float er[CPL];
+  double se = 0.0;
+  float ush[2][CPL == 8 ? 32 : 1];
   panel_body<CPL, GIN, FULL, kEprevMem>(W, d_row, d_col, i1, width, U, maxq, gwide, ngroups, codes, scales,
-                                         zeros, E, part_e, Eprev, er, L);
+                                         zeros, E, part_e, Eprev, er, L, se, ush);
+  panel_error_sum(se, part_e, L.red);
 }
 
 // Two full blocks of 128 columns, [i1, i1 + 128) and [i1 + 128, i1 + 256), for
@@ -460,10 +516,13 @@ __global__ __launch_bounds__(kThreads) void panel_pair_kernel(
     float* __restrict__ E, double* __restrict__ part_e) {
   __shared__ __attribute__((aligned(16))) PanelLds<8> L;
   float er[8];
-  panel_body<8, GIN, true, kEprevMem>(W, d_row, d_col, i1, 128, U, maxq, gwide, ngroups, codes, scales, zeros, E,
-                                      part_e, nullptr, er, L);
+  double se = 0.0;  // both blocks' squared errors, one sum per lane
+  float ush[2][32];  // the odd block's share operands, loaded after the even block's loop
+  panel_body<8, GIN, true, kEprevMem, true>(W, d_row, d_col, i1, 128, U, maxq, gwide, ngroups, codes, scales,
+                                            zeros, E, part_e, nullptr, er, L, se, ush);
   panel_body<8, GIN, true, kEprevRegs>(W, d_row, d_col, i1 + 128, 128, U, maxq, gwide, ngroups, codes, scales,
-                                       zeros, E + (size_t)128 * d_row, part_e, nullptr, er, L);
+                                       zeros, E + (size_t)128 * d_row, part_e, nullptr, er, L, se, ush);
+  panel_error_sum(se, part_e, L.red);
 }
 
 hipError_t launch_panel_pair(int gin, dim3 grid, hipStream_t s, float* W, int d_row, int d_col, int i1,
