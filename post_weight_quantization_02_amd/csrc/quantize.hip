@@ -416,9 +416,9 @@ __device__ __forceinline__ void panel_body(
   };
 
   // Column j's e and c are ready when step j starts: step j broadcasts e,
-  // updates column j + 1 first and computes its e and c in the same scheduling
-  // region as the rest of step j's updates, which fill that chain's latency.
-  // A group start ends the region first (its grid needs every update).
+  // updates column j + 1 first and computes its e and c at once, so that chain
+  // runs under the rest of step j's updates.  At a group start the next
+  // column's chain waits for the group's grid, which needs every update.
   float ecur = 0.f, ccur = 0.f;
   if constexpr (GIN != 0) group_start(std::integral_constant<int, 0>{});
   quant(std::integral_constant<int, 0>{}, ecur, ccur);
@@ -434,7 +434,7 @@ __device__ __forceinline__ void panel_body(
         const f32x4* u = ub[j % kPF];
         constexpr int jn = (jj + 1) % CPL;
         constexpr bool kNext = j + 1 < B;
-        constexpr bool kNextGroup = kNext && GIN != 0 && (j + 1) % GIN == 0;
+        constexpr bool kNextGroup = kNext && GIN != 0 && (j + 1) % (GIN ? GIN : 1) == 0;
         w[jn] = fmaf(-eb, u[jn / 4][jn % 4], w[jn]);
         float enx = 0.f, cnx = 0.f;
         if constexpr (kNext && !kNextGroup) quant(std::integral_constant<int, jn>{}, enx, cnx);
@@ -444,13 +444,13 @@ __device__ __forceinline__ void panel_body(
         const bool own = (p == kk);
         cr[jj] = own ? ccur : cr[jj];
         er[jj] = own ? ecur : er[jj];
+        // The owner's e and c are selected inside their own step: left free,
+        // the compiler keeps every step's e and c live to the end of the block,
+        // and the register pressure that causes sinks each U-row prefetch to one
+        // step ahead of its use.  (A scheduling barrier per step as well cost 7%:
+        // the next step's chain then cannot fill this step's gaps.)
         asm volatile("" : "+v"(cr[jj]), "+v"(er[jj]));
         if constexpr (j + kPF < B) uload(j + kPF, ub[j % kPF]);
-        // The owner's e and c are selected inside their own step (the empty asm
-        // above) and nothing crosses a step (this barrier): left free, the
-        // compiler keeps every step's e and c live to the end of the block and
-        // then sinks each U-row prefetch to one step ahead of its use
-        __builtin_amdgcn_sched_barrier(0);
         if constexpr (kNextGroup) {
           if (FULL || j + 1 < width) {
             group_start(std::integral_constant<int, j + 1>{});
