@@ -39,38 +39,37 @@ constexpr int kP = kNB + 1;  // LDS pitch (elements) of 64x64 tiles
 // D[l / 16 + 4 r][l % 16] (checked on gfx950 against a host product).
 __device__ __forceinline__ int f64_row(int lane, int r) { return (lane >> 4) + 4 * r; }
 
-__global__ __launch_bounds__(kThreads) void damp_kernel(const float* __restrict__ H, int64_t d,
-                                                        float percdamp, double* lam64,
-                                                        float* lambda_out, int32_t* info) {
-  __shared__ double red[kThreads];
-  const int t = threadIdx.x;
-  double s = 0.0;
-  for (int64_t i = t; i < d; i += kThreads) s += (double)H[i * (d + 1)];
-  red[t] = s;
-  __syncthreads();
-  for (int o = kThreads / 2; o > 0; o >>= 1) {
-    if (t < o) red[t] += red[t + o];
-    __syncthreads();
-  }
-  if (t == 0) {
-    const double lam = (double)percdamp * (red[0] / (double)d);
-    *lam64 = lam;
-    *lambda_out = (float)lam;
-    *info = 0;
-  }
-}
-
 // A[i][j] = Hp[d-1-i][d-1-j] (+ lambda on the diagonal), lower 64x64 tiles only;
 // Hp = H, or H with rows and columns taken in the order perm (Hp[a][b] =
-// H[perm[a]][perm[b]]; indices clamped into range)
+// H[perm[a]][perm[b]]; indices clamped into range).  lambda = percdamp times
+// the mean of diag(H) (the same under any perm), summed in fp64 by every
+// diagonal-tile work-group in one fixed order, so all of them add the same
+// value; work-group (0, 0) also writes lambda out and clears info.
 __global__ __launch_bounds__(kThreads) void rev_copy_kernel(const float* __restrict__ H, int64_t d,
-                                                            const double* lam64,
+                                                            float percdamp,
                                                             const int32_t* __restrict__ perm,
-                                                            double* __restrict__ A) {
+                                                            double* __restrict__ A, float* lambda_out,
+                                                            int32_t* info) {
   const int bj = blockIdx.x, bi = blockIdx.y;
   if (bj > bi) return;
-  const double lam = *lam64;
   const int t = threadIdx.x;
+  double lam = 0.0;
+  if (bi == bj) {
+    __shared__ double red[kThreads];
+    double s = 0.0;
+    for (int64_t i = t; i < d; i += kThreads) s += (double)H[i * (d + 1)];
+    red[t] = s;
+    __syncthreads();
+    for (int o = kThreads / 2; o > 0; o >>= 1) {
+      if (t < o) red[t] += red[t + o];
+      __syncthreads();
+    }
+    lam = (double)percdamp * (red[0] / (double)d);
+    if (bi == 0 && t == 0) {
+      *lambda_out = (float)lam;
+      *info = 0;
+    }
+  }
   const int64_t j = (int64_t)bj * 64 + (t & 63);
   for (int k = 0; k < 16; ++k) {
     const int64_t i = (int64_t)bi * 64 + (t >> 6) + 4 * k;
@@ -965,8 +964,6 @@ FactorPlan factor_plan(int64_t d) {
   off = align_up(off + tw * sizeof(float), 256);
   p.off_tmp = off;  // L^-1 (d*d fp32)
   off = align_up(off + (size_t)d * d * sizeof(float), 256);
-  p.off_lam = off;
-  off = align_up(off + 64, 256);
   p.ws_bytes = off;
   return p;
 }
@@ -979,11 +976,10 @@ hipError_t factor_launch(const FactorPlan& p, const float* H, const int32_t* per
   double* part = (double*)(base + p.off_part);
   float* Tw = (float*)(base + p.off_tw);
   float* Linv = (float*)(base + p.off_tmp);
-  double* lam = (double*)(base + p.off_lam);
   hipError_t e;
-  hipLaunchKernelGGL(damp_kernel, dim3(1), dim3(kThreads), 0, s, H, d, percdamp, lam, lambda_out, info);
   const unsigned nt = (unsigned)p.nblk;
-  hipLaunchKernelGGL(rev_copy_kernel, dim3(nt, nt), dim3(kThreads), 0, s, H, d, lam, perm, A);
+  hipLaunchKernelGGL(rev_copy_kernel, dim3(nt, nt), dim3(kThreads), 0, s, H, d, percdamp, perm, A, lambda_out,
+                     info);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   const int nblk = (int)p.nblk;
   if (deferred_updates(nblk)) {

@@ -48,7 +48,7 @@ struct FactorPlan {
   int nb;                 // Cholesky block
   int64_t nblk;
   size_t part_slot;       // doubles per half of the deferred-product double buffer
-  size_t off_a64, off_part, off_tw, off_tmp, off_lam, ws_bytes;
+  size_t off_a64, off_part, off_tw, off_tmp, ws_bytes;
 };
 FactorPlan factor_plan(int64_t d);
 // perm: NULL, or the order in which the columns are factored (H[perm][:, perm])
