@@ -3,7 +3,11 @@
 
 One step = one whole layer through the three C-ABI calls with the inputs
 already resident in HBM: H := 0; H += 2 X^T X over all calibration rows;
-damping + U; the lazy-batch loop with the output error.  Workload: a
+damping + U; the lazy-batch loop with the output error.  The timed steps
+replay that step captured once in a HIP graph (about 110 dependent launches
+per step); every replay's outputs are first checked bitwise against an eager
+step's, and the per-stage times come from an eager pass with HIP events
+between the stages (--eager times the eager steps instead).  Workload: a
 4096 x 4096 fp16 attention projection, X = 262144 x 4096 fp16 (rank-64
 covariance, 1% outlier channels at 20x), 4-bit asymmetric grid, group 128,
 block 128, 1% damping.  With --act-order the same layer is quantized with the
@@ -42,6 +46,9 @@ def parse():
     ap.add_argument("--steps", type=int, default=5)
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--eager", action="store_true",
+                    help="time the layer steps as launched one by one instead of replaying the "
+                         "step captured once in a HIP graph")
     ap.add_argument("--act-order", action="store_true",
                     help="quantize the columns in act-order (descending Hessian diagonal)")
     ap.add_argument("--traffic", default=os.path.join(ROOT, "profiles", "syrk_f16_attn4096_traffic.json"),
@@ -772,6 +779,8 @@ def main():
     stream = torch.cuda.current_stream()
 
     def step(ev=None):
+        # the caller's current stream: the default one, or the capture stream
+        stream = torch.cuda.current_stream()
         H.zero_()
         if ev:
             ev[0].record(stream)
@@ -809,6 +818,30 @@ def main():
     st = np.array([[e[0].elapsed_time(e[1]), e[1].elapsed_time(e[2]), e[2].elapsed_time(e[3])]
                    for e in evs]) / 1e3   # seconds: hessian, factor, quantize
     per_step = wall / args.steps
+    timing = "eager launches"
+    if not args.eager:
+        # the same step captured once and replayed; each replay's outputs must
+        # equal the eager step's bitwise before the replays are timed
+        ref = [t.clone() for t in (H, U, lam, codes, scales, zeros, err)]
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            step()
+        torch.cuda.synchronize()
+        for r in range(2):
+            graph.replay()
+            torch.cuda.synchronize()
+            got = (H, U, lam, codes, scales, zeros, err)
+            if not all(torch.equal(a, b) for a, b in zip(ref, got)):
+                raise SystemExit(f"graph replay {r} differs from the eager step")
+        t0 = time.perf_counter()
+        for k in range(args.steps):
+            graph.replay()
+        torch.cuda.synchronize()
+        graph_step = (time.perf_counter() - t0) / args.steps
+        log(f"bench: eager {per_step * 1e3:.3f} ms per step, graph replay {graph_step * 1e3:.3f} ms")
+        per_step = graph_step
+        timing = "HIP graph replay of the whole step (captured once, replays checked bitwise against an eager step)"
+        del graph
     t_h, t_f, t_q = (float(np.mean(st[:, i])) for i in range(3))
     flops_h = n * d * (d + 1)                       # upper triangle of X^T X, 2 flop per MAC
     flops_f = 2.0 * d ** 3 / 3.0                    # Cholesky d^3/3 + triangular inverse d^3/3
@@ -868,6 +901,7 @@ def main():
         "roofline": roof,
         "roofline_panel": roof_panel,
         "roofline_gemm": roof_gemm,
+        "timing": timing + "; stage times from eager steps with HIP events between the stages",
     }
     if not args.no_cpu_baseline:
         log("bench: timing the fp64 oracle on the whole layer (CPU)")
