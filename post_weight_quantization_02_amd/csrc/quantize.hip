@@ -667,6 +667,52 @@ __global__ __launch_bounds__(kThreads) void err_final_kernel(const double* __res
   if (t == 0) *out = 0.5 * re[0] - (lambda ? 0.5 * (double)*lambda * rdd[0] : 0.0);
 }
 
+// The same sum in the quantization order of a permutation, with the row of W0
+// and the row's codes staged in LDS (dynamic: d_col floats, then d_col bytes):
+// W0 is read and the codes are written back to their original columns with
+// coalesced accesses, the gather and the scatter go through LDS.  Each element
+// is taken by the same thread, in the same order, as in err_delta_kernel.
+template <typename T>
+__global__ __launch_bounds__(kThreads) void err_delta_perm_kernel(
+    const T* __restrict__ W0, int64_t ldw, int64_t d_row, int64_t d_col,
+    const uint8_t* __restrict__ cpos, const float* __restrict__ scales,
+    const int32_t* __restrict__ zeros, int g, int64_t ngroups, const int32_t* __restrict__ perm,
+    uint8_t* __restrict__ codes, double* __restrict__ part_d) {
+  extern __shared__ __attribute__((aligned(16))) unsigned char err_lds[];
+  float* wrow = (float*)err_lds;
+  uint8_t* crow = err_lds + d_col * sizeof(float);
+  __shared__ double red[kThreads];
+  const int t = threadIdx.x;
+  double acc = 0.0;
+  for (int64_t row = blockIdx.x; row < d_row; row += gridDim.x) {
+    for (int64_t c = t; c < d_col; c += kThreads) wrow[c] = (float)W0[row * ldw + c];
+    __syncthreads();
+    for (int64_t c = t; c < d_col; c += kThreads) {
+      const int gi = (int)c / g;
+      const int64_t oc = perm_col(perm, c, d_col);
+      const float s = scales[row * ngroups + gi];
+      const float z = (float)zeros[row * ngroups + gi];
+      const uint8_t cv = cpos[row * d_col + c];
+      crow[oc] = cv;
+      const float wh = s * ((float)cv - z);
+      const double dlt = (double)wrow[oc] - (double)wh;
+      acc += dlt * dlt;
+    }
+    __syncthreads();
+    for (int64_t c = t; c < d_col; c += kThreads) codes[row * d_col + c] = crow[c];
+    __syncthreads();  // this row's LDS fully read before the next row's
+  }
+  red[t] = acc;
+  __syncthreads();
+  for (int o = kThreads / 2; o > 0; o >>= 1) {
+    if (t < o) red[t] += red[t + o];
+    __syncthreads();
+  }
+  if (t == 0) part_d[blockIdx.x] = red[0];
+}
+// widths whose row fits the LDS of err_delta_perm_kernel
+constexpr int64_t kErrPermMaxCols = 12288;  // d_col * 5 bytes + 2 KB within 64 KB of LDS
+
 // group of each original column: g_idx[perm[c]] = c / g
 __global__ __launch_bounds__(kThreads) void g_idx_kernel(const int32_t* __restrict__ perm, int64_t d_col,
                                                          int64_t g, int32_t* __restrict__ g_idx) {
@@ -868,12 +914,22 @@ hipError_t quant_launch(const QuantPlan& p, const void* W0, int w_dtype, int64_t
   const int64_t gsz = group ? group : d_col;
   const int vec8 = !perm && gsz % 8 == 0 && d_col % 8 == 0 && ldw % 8 == 0 && ((uintptr_t)cpos & 7) == 0 &&
                    ((uintptr_t)W0 & (w_dtype == 1 ? 15 : 31)) == 0;
-  if (w_dtype == 1)
+  if (perm && d_col <= kErrPermMaxCols) {
+    const size_t lds = (size_t)d_col * (sizeof(float) + 1);
+    if (w_dtype == 1)
+      hipLaunchKernelGGL(err_delta_perm_kernel<_Float16>, dim3(nerr), dim3(kThreads), lds, s,
+                         (const _Float16*)W0, ldw, d_row, d_col, cpos, scales, zeros, gsz, ngroups, perm, codes,
+                         part_d);
+    else
+      hipLaunchKernelGGL(err_delta_perm_kernel<float>, dim3(nerr), dim3(kThreads), lds, s, (const float*)W0, ldw,
+                         d_row, d_col, cpos, scales, zeros, gsz, ngroups, perm, codes, part_d);
+  } else if (w_dtype == 1) {
     hipLaunchKernelGGL(err_delta_kernel<_Float16>, dim3(nerr), dim3(kThreads), 0, s,
                        (const _Float16*)W0, ldw, d_row, d_col, cpos, scales, zeros, gsz, ngroups, perm, codes, part_d, vec8);
-  else
+  } else {
     hipLaunchKernelGGL(err_delta_kernel<float>, dim3(nerr), dim3(kThreads), 0, s, (const float*)W0, ldw,
                        d_row, d_col, cpos, scales, zeros, gsz, ngroups, perm, codes, part_d, vec8);
+  }
   hipLaunchKernelGGL(err_final_kernel, dim3(1), dim3(kThreads), 0, s, part_e, p.panel_wgs, part_d,
                      (int64_t)nerr, lambda, out_err);
   if (g_idx)
